@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Paged decode benchmark on one MI355X.
+
+One step = one decode token for every sequence of the batch, through the whole
+hot path: host slot allocation (allocate-on-fill, copy-on-write), block copies,
+block-table / length / slot upload, cache_append, paged decode attention
+(partition + merge kernels) and the pool's fragmentation accounting.  Inputs
+are synthetic and seeded (see synth/), resident in HBM before timing starts.
+
+Prints one JSON line.  `value` is the step's algorithmic bytes (K/V read by
+attention, q, out, table entries, lengths, plus cache_append's reads and
+writes) per second of wall-clock step time; `roofline` is the decode
+operation alone, timed with HIP events on the stream it runs on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="long", help="tiny|small_mha|gqa|long|prefix")
+    ap.add_argument("--block-size", type=int, default=None)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget for the CPU oracle baseline (0 = skip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--check", action="store_true",
+                    help="after timing, compare sampled outputs with the oracle")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes(lengths, hq, hkv, d, p, s):
+    kv = int(np.sum(lengths)) * hkv * d * 2 * s
+    qo = 2 * len(lengths) * hq * d * s
+    table = 4 * int(np.sum(-(-np.asarray(lengths) // p)))
+    return kv + qo + table + 4 * len(lengths)
+
+
+def append_bytes(b, hkv, d, s):
+    return 2 * 2 * b * hkv * d * s + 4 * b
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
+                          "multi-GPU runs are not supported (use --gpus 1)"}))
+        sys.exit(2)
+    import torch
+    from synth import CONFIGS, make_workload
+    from paged_kv_cache_399_amd.session import PagedKVCache
+
+    cfg = CONFIGS[args.config]
+    if args.block_size:
+        cfg = cfg.with_block_size(args.block_size)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    nsteps = args.warmup + args.steps
+    t_setup = time.perf_counter()
+    w = make_workload(cfg, args.seed, dev, extra_steps=nsteps)
+    b, hq, hkv, d, p = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
+    s = 2 if cfg.dtype == "bf16" else 4
+    kv = PagedKVCache(w.num_blocks, p, hkv, d, w.torch_dtype, dev, w.free_order, fill=0.0)
+    if cfg.prefix_len:
+        root = kv.new_sequences(1)[0]
+        kv.write([root], [cfg.prefix_len], w.prefix_k, w.prefix_v)
+        seqs = [root] + [kv.fork(root) for _ in range(b - 1)]
+    else:
+        seqs = kv.new_sequences(b)
+    priv = (w.lengths - cfg.prefix_len).astype(np.int64)
+    # prefill every generated token; the timed steps then append one token each
+    slots, cow = kv.pool.append_slots(seqs, priv)
+    assert len(cow) == 0
+    kv.write_slots(torch.from_numpy(slots).to(dev), w.ctx_k, w.ctx_v)
+    max_len = int(w.lengths.max()) + nsteps
+    total = int(w.lengths.sum()) + b * nsteps
+    meta = kv.prepare(seqs, -(-max_len // p), hq, max_len, total)
+    out = torch.empty_like(w.q)
+    torch.cuda.synchronize()
+    log(f"[bench] setup {time.perf_counter() - t_setup:.1f}s: {cfg.name} B={b} Hq={hq} Hkv={hkv} "
+        f"D={d} P={p} tokens={int(w.lengths.sum())} blocks={w.num_blocks}")
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    frag = []
+
+    def step(i, events=None):
+        kv.append_decode_tokens(meta, w.step_k[i], w.step_v[i], stream)
+        if events:
+            events[0].record(stream)
+        kv.attend(meta, w.q, out, stream=stream)
+        if events:
+            events[1].record(stream)
+        frag.append(kv.pool.stats()["fragmentation"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    dec_ms = float(np.mean([a.elapsed_time(e) for a, e in ev]))
+    log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step, decode {dec_ms:.3f} ms")
+
+    # algorithmic bytes, averaged over the timed steps (contexts grow by one per step)
+    base = w.lengths.astype(np.int64)
+    dbytes = np.mean([decode_bytes(base + args.warmup + i + 1, hq, hkv, d, p, s)
+                      for i in range(args.steps)])
+    abytes = append_bytes(b, hkv, d, s)
+    step_gbs = (dbytes + abytes) / (ms_step * 1e-3) / 1e9
+    dec_gbs = dbytes / (dec_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": "paged decode attention: achieved HBM GB/s (% of peak) + decode tokens/s",
+        "value": round(step_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}_decode", "batch": b, "num_q_heads": hq, "num_kv_heads": hkv,
+            "head_dim": d, "block_size": p, "context_tokens": int(base.sum()),
+            "max_context": int(base.max()), "seed": args.seed,
+            "lengths": cfg.length_rule + (f" [{cfg.length_lo},{cfg.length_hi}]" if cfg.length_hi else ""),
+            "prefix_len": cfg.prefix_len, "parallelism": "single GPU",
+        },
+        "decode_tokens_per_s": round(b / (ms_step * 1e-3), 1),
+        "pct_of_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
+        "decode_ms": round(dec_ms, 4),
+        "decode_bytes_per_step": int(dbytes),
+        "fragmentation": round(float(np.mean(frag)), 6),
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "paged_attention_decode (plan + partition + merge)"},
+    }
+    if args.check:
+        result["check_max_err"] = check_sample(w, kv, meta, out, cfg)
+    if not args.no_cpu_baseline and args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(w, cfg, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def check_sample(w, kv, meta, out, cfg):
+    """Oracle check of a few sequences after the timed steps (not timed)."""
+    from oracle import attention as oatt
+    from synth import bf16_bits
+    import torch
+    torch.cuda.synchronize()
+    # rebuild each sampled sequence's keys/values in logical order from the inputs
+    nsteps = w.step_k.shape[0]
+    rng = np.random.default_rng(7)
+    pick = sorted(set([int(np.argmax(w.lengths)), int(np.argmin(w.lengths))] +
+                      rng.choice(cfg.batch, size=min(4, cfg.batch), replace=False).tolist()))
+    worst = 0.0
+    for bi in pick:
+        k, v = w.seq_kv(bi)
+        k = torch.cat([k, w.step_k[:, bi]], 0)
+        v = torch.cat([v, w.step_v[:, bi]], 0)
+        hb = (lambda t: bf16_bits(t)) if cfg.dtype == "bf16" else (lambda t: t.cpu().numpy())
+        ref = oatt.decode(hb(w.q[bi]), hb(k), hb(v))
+        got = out[bi].to(torch.float64).cpu().numpy()
+        worst = max(worst, float(np.abs(got - ref).max()))
+    return worst
+
+
+def cpu_baseline(w, cfg, budget_s):
+    """The float64 oracle on host cores, over as many whole sequences as fit the budget."""
+    import torch
+    from oracle import attention as oatt
+    from synth import bf16_bits
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    hb = (lambda t: bf16_bits(t)) if cfg.dtype == "bf16" else (lambda t: t.cpu().numpy())
+    order = np.random.default_rng(11).permutation(cfg.batch)
+    s = 2 if cfg.dtype == "bf16" else 4
+    spent, nbytes, done, toks = 0.0, 0, 0, 0
+    for bi in order:
+        k, v = w.seq_kv(int(bi))
+        hk, hv, hq_ = hb(k), hb(v), hb(w.q[int(bi)])
+        t0 = time.perf_counter()
+        oatt.decode(hq_, hk, hv)
+        spent += time.perf_counter() - t0
+        L = hk.shape[0]
+        nbytes += L * cfg.num_kv_heads * cfg.head_dim * 2 * s + 2 * cfg.num_q_heads * cfg.head_dim * s
+        toks += L
+        done += 1
+        if spent >= budget_s:
+            break
+    return {"value": round(nbytes / spent / 1e9, 3), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {cfg.batch} sequences ({toks} context tokens), float64 numpy "
+                      f"attention per sequence and KV head, {spent:.1f}s",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

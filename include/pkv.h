@@ -1,0 +1,252 @@
+/*
+ * pkv.h -- C ABI of libpkv.so: paged KV cache and paged decode attention on
+ *          AMD Instinct MI355X (gfx950).
+ *
+ * What the library does, and where each part is described:
+ *
+ *   - A host block pool: the KV cache is cut into fixed-size blocks, each
+ *     sequence owns a block table from logical block to physical block, a new
+ *     block is taken only when the current one is full, finished sequences
+ *     release their blocks ("PagedAttention Internals", sections "Fixed-Size
+ *     KV Blocks", "The Block Table Map" and "Sharing And Dynamic Growth").
+ *   - Prefix sharing: several sequences point at the same physical blocks and
+ *     copy a block only when a sharer writes into it ("pagedattention" topic
+ *     page, fourth paragraph and the comparison table's sharing row).
+ *   - Device kernels: write new tokens' keys/values at the slots the pool
+ *     handed out, copy blocks for copy-on-write, and decode attention that
+ *     follows each sequence's block table to its keys and values ("The Block
+ *     Table Map"; topic page, third paragraph).
+ *
+ * Conventions for every entry point
+ *   - Return value: PKV_OK (0) or a negative PKV_ERR_* code.  On error,
+ *     pkv_last_error() returns a message for the calling thread and the
+ *     call has changed no pool state and launched no device work.
+ *   - "host" pointers are ordinary CPU memory owned by the caller; "device"
+ *     pointers are HIP device allocations owned by the caller (the library
+ *     never allocates or frees device memory for caller data).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     All device work is enqueued asynchronously on it, in call order.
+ *   - A pool is not thread-safe: callers serialise calls on one pool.
+ *   - No C++ exception crosses this boundary.
+ *
+ * Cache layout (the pages fix none; this library's choice):
+ *   k_cache: [num_blocks, num_kv_heads, block_size, head_dim]   row-major
+ *   v_cache: [num_blocks, num_kv_heads, head_dim, block_size]   row-major
+ *   i.e. each block stores its keys token-major and its values transposed
+ *   (token-minor), so that the value product of decode attention reads
+ *   contiguous runs of tokens.  Slot s = block (s / block_size), offset
+ *   (s % block_size).
+ *   q, out:          [n_seqs, num_q_heads, head_dim]
+ *   k_new, v_new:    [n_tokens, num_kv_heads, head_dim]
+ *   block table:     int32 [n_seqs, max_blocks_per_seq], unused entries -1
+ *   query head h reads KV head h / (num_q_heads / num_kv_heads).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define PKV_OK                 0
+#define PKV_ERR_INVALID_ARG   -1   /* malformed argument, NULL pointer, bad shape   */
+#define PKV_ERR_NO_BLOCKS     -2   /* the free list cannot cover the request        */
+#define PKV_ERR_BAD_SEQ       -3   /* unknown or already released sequence id       */
+#define PKV_ERR_UNSUPPORTED   -4   /* shape / dtype combination not implemented     */
+#define PKV_ERR_WORKSPACE     -5   /* workspace missing or too small                */
+#define PKV_ERR_HIP           -6   /* a HIP runtime call or launch failed           */
+#define PKV_ERR_CAPACITY      -7   /* an output buffer is too small                 */
+#define PKV_ERR_DEVICE        -8   /* a kernel reported bad indices (see below)     */
+
+/* device error bits reported by pkv_check_device_errors */
+#define PKV_DEVERR_TABLE_ENTRY   1 /* block-table entry outside [0, num_blocks)     */
+#define PKV_DEVERR_SLOT          2 /* cache_append slot >= num_blocks * block_size  */
+#define PKV_DEVERR_COPY_PAIR     4 /* copy_blocks pair outside [0, num_blocks)      */
+#define PKV_DEVERR_CONTEXT_LEN   8 /* context length < 0 or > table capacity       */
+#define PKV_DEVERR_WORK_OVERFLOW 16/* more partitions than the workspace was sized */
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+typedef struct pkv_pool pkv_pool;
+
+typedef struct {
+  int64_t num_blocks;
+  int64_t free_blocks;
+  int64_t used_blocks;      /* blocks with refcount > 0, each counted once      */
+  int64_t allocated_slots;  /* used_blocks * block_size                         */
+  int64_t live_tokens;      /* slots holding a token, each slot counted once    */
+  int64_t wasted_slots;     /* allocated_slots - live_tokens                    */
+  int64_t num_seqs;         /* live sequences                                   */
+  double  fragmentation;    /* wasted_slots / allocated_slots (0 if none)       */
+} pkv_stats;
+
+/* ---- host block pool --------------------------------------------------- */
+
+/* Create a pool of `num_blocks` blocks of `block_size` token slots.
+ * `free_order` (host, num_blocks entries, may be NULL = 0..num_blocks-1) is
+ * the initial free list, a permutation of the block ids; allocation takes its
+ * head, release appends to its tail.  *out receives the handle.
+ * Errors: INVALID_ARG (sizes <= 0, not a permutation, out NULL). */
+int pkv_pool_create(int32_t num_blocks, int32_t block_size,
+                    const int32_t* free_order, pkv_pool** out);
+
+/* Destroy a pool (waits for its pending table uploads).  NULL is a no-op. */
+int pkv_pool_destroy(pkv_pool* pool);
+
+/* New empty sequence (no blocks, length 0).  Ids count up from 0 and are
+ * never reused within a pool. */
+int pkv_seq_create(pkv_pool* pool, int64_t* seq_out);
+
+/* Append tokens: n_new[i] tokens to seqs[i], for i in call order
+ * ("Fixed-Size KV Blocks": a block is taken when a token finds the current
+ * one full; topic page fourth paragraph: copy-on-write on divergence).
+ * For each token: if length % block_size == 0 take the free-list head as a
+ * new block; else if the last block is shared (refcount > 1) take the head as
+ * a private copy, report (old, new) in cow_pairs_out and drop one reference to
+ * the old block; then slot = table[length / P] * P + length % P, length += 1.
+ *   seqs        host int64[n_seqs], distinct live ids
+ *   n_new       host int32[n_seqs], >= 0
+ *   slot_mapping_out  host int32[slot_cap]: slots in call order
+ *   cow_pairs_out     host int32[2 * cow_cap]: (src, dst) pairs, may be NULL
+ *                     if cow_cap == 0
+ *   n_cow_out   number of pairs written
+ * The call is all-or-nothing.  Errors: BAD_SEQ, INVALID_ARG (duplicate id,
+ * negative count), NO_BLOCKS, CAPACITY (sum(n_new) > slot_cap or more
+ * copies than cow_cap). */
+int pkv_seq_append_slots(pkv_pool* pool, const int64_t* seqs, const int32_t* n_new,
+                         int32_t n_seqs, int32_t* slot_mapping_out, int64_t slot_cap,
+                         int32_t* cow_pairs_out, int32_t cow_cap, int32_t* n_cow_out);
+
+/* Fork: a new sequence sharing every block of `parent` (refcount + 1 each),
+ * with the parent's length (topic page, fourth paragraph). */
+int pkv_seq_fork(pkv_pool* pool, int64_t parent, int64_t* child_out);
+
+/* Release a sequence: drop one reference to each block in logical order;
+ * blocks reaching zero go to the free-list tail in that order. */
+int pkv_seq_free(pkv_pool* pool, int64_t seq);
+
+/* Place an empty sequence on explicit free blocks `phys` (host int32[n_blocks],
+ * logical order) holding `length` tokens, ceil(length / P) == n_blocks
+ * ("The Block Table Map": logical blocks 0,1,2 at physical 8,3,11).  The
+ * blocks leave the free list; the rest keep their order.
+ * Errors: BAD_SEQ, INVALID_ARG (sequence not empty, block not free / out of
+ * range / repeated, length mismatch). */
+int pkv_seq_set_table(pkv_pool* pool, int64_t seq, const int32_t* phys,
+                      int32_t n_blocks, int64_t length);
+
+/* Copy a sequence's table (host int32[cap]) and length.  *n_out is the number
+ * of blocks; CAPACITY if it exceeds cap (nothing written then). */
+int pkv_seq_get_table(pkv_pool* pool, int64_t seq, int32_t* phys_out, int32_t cap,
+                      int32_t* n_out, int64_t* len_out);
+
+/* Occupancy and fragmentation ("inference-acceleration-pagedattention-vllm"
+ * chapter: wasted = allocated but not holding a token, over allocated).
+ * A shared block and its tokens count once. */
+int pkv_pool_stats(pkv_pool* pool, pkv_stats* out);
+
+/* State export for bit-exact checks: free list in order (host int32[num_blocks],
+ * first *n_free_out entries valid) and every block's refcount (host
+ * int32[num_blocks]).  Either output may be NULL. */
+int pkv_pool_export(pkv_pool* pool, int32_t* free_order_out, int32_t* refcount_out,
+                    int32_t* n_free_out);
+
+/* Build the padded block table of `seqs` (row i = seqs[i], entries beyond the
+ * sequence's blocks = -1) and its context lengths in pool-owned pinned
+ * staging memory, then enqueue the host-to-device copies on `stream`:
+ *   d_block_table   device int32[n_seqs * max_blocks_per_seq]
+ *   d_context_lens  device int32[n_seqs]
+ *   slot_mapping / d_slot_mapping / n_slots: optional (host int32[n_slots] ->
+ *                   device int32[n_slots]) copy of a slot mapping in the same
+ *                   staging round; pass NULL/NULL/0 to skip.
+ *   max_context_len_out, total_tokens_out: host outputs, may be NULL.
+ * Staging buffers are double-buffered and reused only after the copy that
+ * last read them has completed, so the host may return before the copy runs.
+ * Errors: BAD_SEQ, CAPACITY (a sequence has more than max_blocks_per_seq
+ * blocks), INVALID_ARG, HIP. */
+int pkv_block_table_upload(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs,
+                           int32_t max_blocks_per_seq, int32_t* d_block_table,
+                           int32_t* d_context_lens, const int32_t* slot_mapping,
+                           int32_t* d_slot_mapping, int32_t n_slots,
+                           int32_t* max_context_len_out, int64_t* total_tokens_out,
+                           void* stream);
+
+/* ---- device kernels ---------------------------------------------------- */
+
+/* Copy-on-write block copies: for each pair, every slot of block src (K and V,
+ * all heads) is copied to block dst.  `pairs` is HOST memory, int32[2*n_pairs]
+ * as returned by pkv_seq_append_slots; the pairs travel in kernel arguments,
+ * so no host-to-device copy is needed.  Enqueue before the cache_append that
+ * writes into the new blocks.  Pairs outside [0, num_blocks) are skipped and
+ * flagged (PKV_DEVERR_COPY_PAIR). */
+int pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n_pairs,
+                    int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, pkv_dtype dtype, void* stream);
+
+/* Write token i's keys/values (device k_new/v_new [n_tokens, Hkv, D]) into the
+ * cache at slot d_slot_mapping[i] (device int32[n_tokens]) -- each generated
+ * token goes into the current block ("Fixed-Size KV Blocks").  A negative
+ * slot skips the token; a slot >= num_blocks * block_size is skipped and
+ * flagged (PKV_DEVERR_SLOT).  Live slots must be distinct within one call.
+ * Bit copy: no arithmetic on the values. */
+int pkv_cache_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                     const int32_t* d_slot_mapping, int32_t n_tokens, int32_t num_blocks,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     pkv_dtype dtype, void* stream);
+
+/* Workspace bytes that pkv_paged_attention_decode needs for these arguments
+ * (same meaning as there).  total_context_tokens may be -1 if unknown (a
+ * looser bound is used). */
+int pkv_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size,
+                               int32_t max_context_len, int64_t total_context_tokens,
+                               pkv_dtype dtype, size_t* bytes_out);
+
+/* Paged decode attention ("The Block Table Map": attention follows each
+ * sequence's table to its keys and values).  For sequence b, query head h,
+ * G = Hq / Hkv, KV head g = h / G, L = d_context_lens[b]:
+ *   out[b,h] = sum_{t<L} softmax_t(scale * q[b,h] . K_b[t,g]) V_b[t,g]
+ * where K_b[t,g] = k_cache[table[b][t/P], g, t%P, :] and
+ *       V_b[t,g] = v_cache[table[b][t/P], g, :, t%P].  L = 0 gives zeros.
+ *   out, q           device [n_seqs, Hq, D], dtype
+ *   k_cache, v_cache device, layout above, dtype
+ *   d_block_table    device int32[n_seqs * max_blocks_per_seq]
+ *   d_context_lens   device int32[n_seqs], 0 <= L <= max_blocks_per_seq * P
+ *   max_context_len  >= every L (host knowledge, used for sizing)
+ *   total_context_tokens  sum of L, or -1 if unknown (sizing only)
+ *   workspace        device, >= pkv_decode_workspace_bytes(...) bytes
+ * Long contexts are cut into fixed partitions whose partial results are merged
+ * by a second kernel; the summation order depends only on logical positions,
+ * so results do not depend on where the blocks sit.  Arithmetic is fp32
+ * (bf16 inputs: score and value products on matrix cores with fp32
+ * accumulation).  Supported: head_dim <= 256, Hq % Hkv == 0, Hq / Hkv <= 16,
+ * any block_size >= 1; fastest path: bf16, head_dim 64/128, block_size a
+ * multiple of 8.  Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.  Bad
+ * table entries or lengths are clamped in-bounds and flagged. */
+int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* d_block_table,
+                               const int32_t* d_context_lens, int32_t n_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t num_blocks,
+                               int32_t max_blocks_per_seq, int32_t max_context_len,
+                               int64_t total_context_tokens, float scale, pkv_dtype dtype,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Synchronise `stream`, then read and clear the current device's error bits
+ * (PKV_DEVERR_*) into *flags_out.  Returns PKV_ERR_DEVICE if any bit was set. */
+int pkv_check_device_errors(void* stream, int32_t* flags_out);
+
+/* Message for the last non-zero status returned on this thread ("" if none).
+ * The pointer stays valid until the thread's next failing call. */
+const char* pkv_last_error(void);
+
+/* Library version string. */
+const char* pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKV_H */

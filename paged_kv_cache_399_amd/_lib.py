@@ -1,0 +1,83 @@
+"""ctypes declarations of libpkv.so (the C ABI in include/pkv.h)."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpkv.so")
+
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_NO_BLOCKS = -2
+ERR_BAD_SEQ = -3
+ERR_UNSUPPORTED = -4
+ERR_WORKSPACE = -5
+ERR_HIP = -6
+ERR_CAPACITY = -7
+ERR_DEVICE = -8
+
+DEVERR_TABLE_ENTRY = 1
+DEVERR_SLOT = 2
+DEVERR_COPY_PAIR = 4
+DEVERR_CONTEXT_LEN = 8
+DEVERR_WORK_OVERFLOW = 16
+
+F32 = 0
+BF16 = 1
+
+
+class Stats(C.Structure):
+    _fields_ = [("num_blocks", C.c_int64), ("free_blocks", C.c_int64),
+                ("used_blocks", C.c_int64), ("allocated_slots", C.c_int64),
+                ("live_tokens", C.c_int64), ("wasted_slots", C.c_int64),
+                ("num_seqs", C.c_int64), ("fragmentation", C.c_double)]
+
+
+_i32, _i64, _vp = C.c_int32, C.c_int64, C.c_void_p
+_pi32, _pi64 = C.POINTER(C.c_int32), C.POINTER(C.c_int64)
+
+SIGNATURES = {
+    "pkv_pool_create": (C.c_int, [_i32, _i32, _pi32, C.POINTER(_vp)]),
+    "pkv_pool_destroy": (C.c_int, [_vp]),
+    "pkv_seq_create": (C.c_int, [_vp, _pi64]),
+    "pkv_seq_append_slots": (C.c_int, [_vp, _pi64, _pi32, _i32, _pi32, _i64, _pi32, _i32, _pi32]),
+    "pkv_seq_fork": (C.c_int, [_vp, _i64, _pi64]),
+    "pkv_seq_free": (C.c_int, [_vp, _i64]),
+    "pkv_seq_set_table": (C.c_int, [_vp, _i64, _pi32, _i32, _i64]),
+    "pkv_seq_get_table": (C.c_int, [_vp, _i64, _pi32, _i32, _pi32, _pi64]),
+    "pkv_pool_stats": (C.c_int, [_vp, C.POINTER(Stats)]),
+    "pkv_pool_export": (C.c_int, [_vp, _pi32, _pi32, _pi32]),
+    "pkv_block_table_upload": (C.c_int, [_vp, _pi64, _i32, _i32, _vp, _vp, _pi32, _vp, _i32,
+                                         _pi32, _pi64, _vp]),
+    "pkv_copy_blocks": (C.c_int, [_vp, _vp, _pi32, _i32, _i32, _i32, _i32, _i32, C.c_int, _vp]),
+    "pkv_cache_append": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                   C.c_int, _vp]),
+    "pkv_decode_workspace_bytes": (C.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i64, C.c_int,
+                                             C.POINTER(C.c_size_t)]),
+    "pkv_paged_attention_decode": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                             _i32, _i32, _i32, _i32, _i64, C.c_float, C.c_int, _vp,
+                                             C.c_size_t, _vp]),
+    "pkv_check_device_errors": (C.c_int, [_vp, _pi32]),
+    "pkv_last_error": (C.c_char_p, []),
+    "pkv_version": (C.c_char_p, []),
+}
+
+_lib = None
+
+
+def load():
+    """Load libpkv.so from the package directory; fail loudly if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m paged_kv_cache_399_amd.build` (hipcc, gfx950)")
+    lib = C.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib

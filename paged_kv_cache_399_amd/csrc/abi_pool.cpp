@@ -1,0 +1,256 @@
+// C ABI of the host block pool and of the block-table upload.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <climits>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "block_pool.hpp"
+#include "internal.hpp"
+
+namespace pkv {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+}  // namespace pkv
+
+// Pool handle: the host pool plus two pinned staging buffers for uploads.
+struct pkv_pool {
+  struct Stage {
+    void* host = nullptr;
+    size_t bytes = 0;
+    hipEvent_t done = nullptr;  // recorded after the copies that read `host`
+    bool pending = false;
+  };
+  pkv::BlockPool pool;
+  Stage stage[2];
+  int next = 0;
+
+  pkv_pool(int32_t nb, int32_t p, const int32_t* order) : pool(nb, p, order) {}
+  ~pkv_pool() {
+    for (Stage& s : stage) {
+      if (s.pending) (void)hipEventSynchronize(s.done);
+      if (s.done) (void)hipEventDestroy(s.done);
+      if (s.host) (void)hipHostFree(s.host);
+    }
+  }
+};
+
+using pkv::fail;
+
+extern "C" {
+
+const char* pkv_last_error(void) { return pkv::g_last_error.c_str(); }
+
+const char* pkv_version(void) { return "pkv 0.1 gfx950"; }
+
+int pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                    pkv_pool** out) {
+  PKV_TRY_BEGIN
+  if (!out) return fail(PKV_ERR_INVALID_ARG, "out is NULL");
+  if (num_blocks <= 0 || block_size <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_blocks and block_size must be positive");
+  if ((int64_t)num_blocks * block_size > INT32_MAX)
+    return fail(PKV_ERR_INVALID_ARG, "num_blocks * block_size exceeds int32 slot range");
+  if (free_order) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      const int32_t b = free_order[i];
+      if (b < 0 || b >= num_blocks || seen[b])
+        return fail(PKV_ERR_INVALID_ARG, "free_order is not a permutation of 0..num_blocks-1");
+      seen[b] = 1;
+    }
+  }
+  *out = new pkv_pool(num_blocks, block_size, free_order);
+  return PKV_OK;
+  PKV_TRY_END
+}
+
+int pkv_pool_destroy(pkv_pool* pool) {
+  PKV_TRY_BEGIN
+  delete pool;
+  return PKV_OK;
+  PKV_TRY_END
+}
+
+int pkv_seq_create(pkv_pool* pool, int64_t* seq_out) {
+  PKV_TRY_BEGIN
+  if (!pool || !seq_out) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+  *seq_out = pool->pool.create();
+  return PKV_OK;
+  PKV_TRY_END
+}
+
+int pkv_seq_append_slots(pkv_pool* pool, const int64_t* seqs, const int32_t* n_new,
+                         int32_t n_seqs, int32_t* slot_mapping_out, int64_t slot_cap,
+                         int32_t* cow_pairs_out, int32_t cow_cap, int32_t* n_cow_out) {
+  PKV_TRY_BEGIN
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "NULL pool");
+  if (cow_cap < 0) return fail(PKV_ERR_INVALID_ARG, "cow_cap < 0");
+  return pool->pool.append(seqs, n_new, n_seqs, slot_mapping_out, slot_cap, cow_pairs_out,
+                           cow_cap, n_cow_out);
+  PKV_TRY_END
+}
+
+int pkv_seq_fork(pkv_pool* pool, int64_t parent, int64_t* child_out) {
+  PKV_TRY_BEGIN
+  if (!pool || !child_out) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+  return pool->pool.fork(parent, child_out);
+  PKV_TRY_END
+}
+
+int pkv_seq_free(pkv_pool* pool, int64_t seq) {
+  PKV_TRY_BEGIN
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "NULL pool");
+  return pool->pool.release(seq);
+  PKV_TRY_END
+}
+
+int pkv_seq_set_table(pkv_pool* pool, int64_t seq, const int32_t* phys, int32_t n_blocks,
+                      int64_t length) {
+  PKV_TRY_BEGIN
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "NULL pool");
+  return pool->pool.set_table(seq, phys, n_blocks, length);
+  PKV_TRY_END
+}
+
+int pkv_seq_get_table(pkv_pool* pool, int64_t seq, int32_t* phys_out, int32_t cap,
+                      int32_t* n_out, int64_t* len_out) {
+  PKV_TRY_BEGIN
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "NULL pool");
+  if (!pool->pool.live(seq)) return fail(PKV_ERR_BAD_SEQ, "sequence %lld is not live", (long long)seq);
+  const std::vector<int32_t>& t = pool->pool.table(seq);
+  if ((int64_t)t.size() > cap)
+    return fail(PKV_ERR_CAPACITY, "table of %zu blocks does not fit cap %d", t.size(), cap);
+  if (!t.empty() && !phys_out) return fail(PKV_ERR_INVALID_ARG, "NULL phys_out");
+  std::copy(t.begin(), t.end(), phys_out);
+  if (n_out) *n_out = (int32_t)t.size();
+  if (len_out) *len_out = pool->pool.length(seq);
+  return PKV_OK;
+  PKV_TRY_END
+}
+
+int pkv_pool_stats(pkv_pool* pool, pkv_stats* out) {
+  PKV_TRY_BEGIN
+  if (!pool || !out) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+  const pkv::BlockPool& p = pool->pool;
+  out->num_blocks = p.num_blocks();
+  out->free_blocks = p.free_count();
+  out->used_blocks = p.num_blocks() - p.free_count();
+  out->allocated_slots = out->used_blocks * p.block_size();
+  out->live_tokens = p.live_tokens();
+  out->wasted_slots = out->allocated_slots - out->live_tokens;
+  out->num_seqs = p.live_seqs();
+  out->fragmentation =
+      out->allocated_slots ? (double)out->wasted_slots / (double)out->allocated_slots : 0.0;
+  return PKV_OK;
+  PKV_TRY_END
+}
+
+int pkv_pool_export(pkv_pool* pool, int32_t* free_order_out, int32_t* refcount_out,
+                    int32_t* n_free_out) {
+  PKV_TRY_BEGIN
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "NULL pool");
+  pool->pool.export_state(free_order_out, refcount_out);
+  if (n_free_out) *n_free_out = (int32_t)pool->pool.free_count();
+  return PKV_OK;
+  PKV_TRY_END
+}
+
+int pkv_block_table_upload(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs,
+                           int32_t max_blocks_per_seq, int32_t* d_block_table,
+                           int32_t* d_context_lens, const int32_t* slot_mapping,
+                           int32_t* d_slot_mapping, int32_t n_slots,
+                           int32_t* max_context_len_out, int64_t* total_tokens_out,
+                           void* stream) {
+  PKV_TRY_BEGIN
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "NULL pool");
+  if (n_seqs < 0 || max_blocks_per_seq < 0 || n_slots < 0)
+    return fail(PKV_ERR_INVALID_ARG, "negative size");
+  if (n_seqs > 0 && (!seqs || !d_context_lens || (max_blocks_per_seq > 0 && !d_block_table)))
+    return fail(PKV_ERR_INVALID_ARG, "NULL table / length pointer");
+  if (n_slots > 0 && (!slot_mapping || !d_slot_mapping))
+    return fail(PKV_ERR_INVALID_ARG, "NULL slot mapping pointer");
+  const pkv::BlockPool& bp = pool->pool;
+  int64_t total = 0;
+  int32_t longest = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    if (!bp.live(seqs[i])) return fail(PKV_ERR_BAD_SEQ, "sequence %lld is not live", (long long)seqs[i]);
+    if ((int64_t)bp.table(seqs[i]).size() > max_blocks_per_seq)
+      return fail(PKV_ERR_CAPACITY, "sequence %lld holds %zu blocks > max_blocks_per_seq %d",
+                  (long long)seqs[i], bp.table(seqs[i]).size(), max_blocks_per_seq);
+    const int64_t L = bp.length(seqs[i]);
+    if (L > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "context length exceeds int32");
+    total += L;
+    longest = std::max<int32_t>(longest, (int32_t)L);
+  }
+  const size_t table_bytes = (size_t)n_seqs * max_blocks_per_seq * sizeof(int32_t);
+  const size_t lens_bytes = (size_t)n_seqs * sizeof(int32_t);
+  const size_t slot_bytes = (size_t)n_slots * sizeof(int32_t);
+  const size_t need = table_bytes + lens_bytes + slot_bytes;
+  hipStream_t st = (hipStream_t)stream;
+
+  if (need > 0) {
+    pkv_pool::Stage& sg = pool->stage[pool->next];
+    if (sg.pending) {
+      if (hipEventSynchronize(sg.done) != hipSuccess)
+        return fail(PKV_ERR_HIP, "waiting for a previous upload failed");
+      sg.pending = false;
+    }
+    if (sg.bytes < need) {
+      if (sg.host) (void)hipHostFree(sg.host);
+      sg.host = nullptr;
+      sg.bytes = 0;
+      size_t cap = std::max<size_t>(need, 4096);
+      if (hipHostMalloc(&sg.host, cap, hipHostMallocDefault) != hipSuccess)
+        return fail(PKV_ERR_HIP, "pinned staging allocation of %zu bytes failed", cap);
+      sg.bytes = cap;
+    }
+    if (!sg.done && hipEventCreateWithFlags(&sg.done, hipEventDisableTiming) != hipSuccess)
+      return fail(PKV_ERR_HIP, "event creation failed");
+    char* base = (char*)sg.host;
+    int32_t* tab = (int32_t*)base;
+    int32_t* lens = (int32_t*)(base + table_bytes);
+    int32_t* slots = (int32_t*)(base + table_bytes + lens_bytes);
+    for (int32_t i = 0; i < n_seqs; ++i) {
+      const std::vector<int32_t>& t = bp.table(seqs[i]);
+      int32_t* row = tab + (size_t)i * max_blocks_per_seq;
+      std::copy(t.begin(), t.end(), row);
+      std::fill(row + t.size(), row + max_blocks_per_seq, -1);
+      lens[i] = (int32_t)bp.length(seqs[i]);
+    }
+    if (n_slots) std::memcpy(slots, slot_mapping, slot_bytes);
+    hipError_t e = hipSuccess;
+    if (table_bytes) e = hipMemcpyAsync(d_block_table, tab, table_bytes, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess && lens_bytes)
+      e = hipMemcpyAsync(d_context_lens, lens, lens_bytes, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess && slot_bytes)
+      e = hipMemcpyAsync(d_slot_mapping, slots, slot_bytes, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipEventRecord(sg.done, st);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "upload failed: %s", hipGetErrorString(e));
+    sg.pending = true;
+    pool->next ^= 1;
+  }
+  if (max_context_len_out) *max_context_len_out = longest;
+  if (total_tokens_out) *total_tokens_out = total;
+  return PKV_OK;
+  PKV_TRY_END
+}
+
+}  // extern "C"

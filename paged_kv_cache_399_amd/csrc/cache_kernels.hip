@@ -1,0 +1,167 @@
+// cache_append and copy_blocks: bit copies into the paged K/V caches.
+//
+// "PagedAttention Internals", section "Fixed-Size KV Blocks": each generated
+// token is stored in its sequence's current block; the slot comes from the
+// host pool.  "pagedattention" topic page, fourth paragraph: shared blocks are
+// copied only when a sharer diverges (copy_blocks performs that copy).
+//
+// Layout: k_cache [NB, Hkv, P, D] (token rows), v_cache [NB, Hkv, D, P]
+// (value columns per token).  Elements are moved as raw 16- or 32-bit words.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace pkv {
+namespace {
+
+// One workgroup per token (grid-stride).  Keys: each token row of every head
+// is contiguous in the cache, so threads move 16-byte chunks.  Values: the
+// token's column is strided by P elements; threads move single elements.
+template <typename E>
+__global__ __launch_bounds__(256) void cache_append_kernel(
+    E* __restrict__ kc, E* __restrict__ vc, const E* __restrict__ kn, const E* __restrict__ vn,
+    const int32_t* __restrict__ slots, int32_t n_tokens, int64_t num_slots, int32_t hkv,
+    int32_t d, int32_t p, int32_t vec_ok, int32_t* __restrict__ err) {
+  const int32_t hd = hkv * d;
+  for (int32_t tok = blockIdx.x; tok < n_tokens; tok += gridDim.x) {
+    const int32_t s = slots[tok];
+    if (s < 0) continue;
+    if ((int64_t)s >= num_slots) {
+      if (threadIdx.x == 0) atomicOr(err, PKV_DEVERR_SLOT);
+      continue;
+    }
+    const int64_t blk = s / p, off = s % p;
+    const E* ksrc = kn + (int64_t)tok * hd;
+    const E* vsrc = vn + (int64_t)tok * hd;
+    if (vec_ok) {
+      constexpr int V = 16 / sizeof(E);  // elements per 16-byte chunk
+      const int32_t nvec = hd / V;
+      for (int32_t i = threadIdx.x; i < nvec; i += blockDim.x) {
+        const int32_t e = i * V, h = e / d, dd = e % d;
+        const uint4 x = *reinterpret_cast<const uint4*>(ksrc + e);
+        *reinterpret_cast<uint4*>(kc + ((blk * hkv + h) * p + off) * d + dd) = x;
+      }
+    } else {
+      for (int32_t e = threadIdx.x; e < hd; e += blockDim.x) {
+        const int32_t h = e / d, dd = e % d;
+        kc[((blk * hkv + h) * p + off) * d + dd] = ksrc[e];
+      }
+    }
+    for (int32_t e = threadIdx.x; e < hd; e += blockDim.x) {
+      const int32_t h = e / d, dd = e % d;
+      vc[((blk * hkv + h) * d + dd) * p + off] = vsrc[e];
+    }
+  }
+}
+
+constexpr int kMaxPairsPerLaunch = 128;
+
+struct CopyPairs {
+  int32_t src[kMaxPairsPerLaunch];
+  int32_t dst[kMaxPairsPerLaunch];
+};
+
+// grid (chunks, pairs): every block is one contiguous run of `words` words in
+// each cache, whatever the layout inside it.
+template <typename W>
+__global__ __launch_bounds__(256) void copy_blocks_kernel(W* __restrict__ kc, W* __restrict__ vc,
+                                                          CopyPairs pairs, int64_t words,
+                                                          int32_t num_blocks,
+                                                          int32_t* __restrict__ err) {
+  const int32_t src = pairs.src[blockIdx.y], dst = pairs.dst[blockIdx.y];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(err, PKV_DEVERR_COPY_PAIR);
+    return;
+  }
+  const W* ks = kc + (int64_t)src * words;
+  const W* vs = vc + (int64_t)src * words;
+  W* kd = kc + (int64_t)dst * words;
+  W* vd = vc + (int64_t)dst * words;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    kd[i] = ks[i];
+    vd[i] = vs[i];
+  }
+}
+
+}  // namespace
+}  // namespace pkv
+
+using pkv::fail;
+
+extern "C" int pkv_cache_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                                const int32_t* d_slot_mapping, int32_t n_tokens, int32_t num_blocks,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                pkv_dtype dtype, void* stream) {
+  PKV_TRY_BEGIN
+  if (n_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "bad sizes");
+  if (!pkv::dtype_valid(dtype)) return fail(PKV_ERR_INVALID_ARG, "bad dtype");
+  if (n_tokens == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !k_new || !v_new || !d_slot_mapping)
+    return fail(PKV_ERR_INVALID_ARG, "NULL pointer");
+  int32_t* err = nullptr;
+  int rc = pkv::device_error_word(&err);
+  if (rc) return rc;
+  const int64_t num_slots = (int64_t)num_blocks * block_size;
+  const size_t es = pkv::dtype_size(dtype);
+  const int32_t vec_ok = ((size_t)head_dim * es % 16 == 0) &&
+                         ((uintptr_t)k_cache % 16 == 0) && ((uintptr_t)k_new % 16 == 0);
+  const int grid = (int)std::min<int32_t>(n_tokens, 1 << 16);
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == PKV_BF16)
+    hipLaunchKernelGGL(pkv::cache_append_kernel<uint16_t>, dim3(grid), dim3(256), 0, st,
+                       (uint16_t*)k_cache, (uint16_t*)v_cache, (const uint16_t*)k_new,
+                       (const uint16_t*)v_new, d_slot_mapping, n_tokens, num_slots, num_kv_heads,
+                       head_dim, block_size, vec_ok, err);
+  else
+    hipLaunchKernelGGL(pkv::cache_append_kernel<uint32_t>, dim3(grid), dim3(256), 0, st,
+                       (uint32_t*)k_cache, (uint32_t*)v_cache, (const uint32_t*)k_new,
+                       (const uint32_t*)v_new, d_slot_mapping, n_tokens, num_slots, num_kv_heads,
+                       head_dim, block_size, vec_ok, err);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "cache_append launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+  PKV_TRY_END
+}
+
+extern "C" int pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n_pairs,
+                               int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, pkv_dtype dtype, void* stream) {
+  PKV_TRY_BEGIN
+  if (n_pairs < 0 || num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "bad sizes");
+  if (!pkv::dtype_valid(dtype)) return fail(PKV_ERR_INVALID_ARG, "bad dtype");
+  if (n_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !pairs) return fail(PKV_ERR_INVALID_ARG, "NULL pointer");
+  int32_t* err = nullptr;
+  int rc = pkv::device_error_word(&err);
+  if (rc) return rc;
+  const int64_t bytes = (int64_t)num_kv_heads * block_size * head_dim * pkv::dtype_size(dtype);
+  const bool vec = bytes % 16 == 0 && (uintptr_t)k_cache % 16 == 0 && (uintptr_t)v_cache % 16 == 0;
+  const int64_t words = vec ? bytes / 16 : bytes / 2;
+  const int chunks = (int)std::max<int64_t>(1, std::min<int64_t>(64, (words + 255) / 256));
+  hipStream_t st = (hipStream_t)stream;
+  for (int32_t base = 0; base < n_pairs; base += pkv::kMaxPairsPerLaunch) {
+    const int32_t n = std::min(pkv::kMaxPairsPerLaunch, n_pairs - base);
+    pkv::CopyPairs cp;
+    for (int32_t i = 0; i < n; ++i) {
+      cp.src[i] = pairs[2 * (base + i)];
+      cp.dst[i] = pairs[2 * (base + i) + 1];
+    }
+    if (vec)
+      hipLaunchKernelGGL(pkv::copy_blocks_kernel<uint4>, dim3(chunks, n), dim3(256), 0, st,
+                         (uint4*)k_cache, (uint4*)v_cache, cp, words, num_blocks, err);
+    else
+      hipLaunchKernelGGL(pkv::copy_blocks_kernel<uint16_t>, dim3(chunks, n), dim3(256), 0, st,
+                         (uint16_t*)k_cache, (uint16_t*)v_cache, cp, words, num_blocks, err);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "copy_blocks launch: %s", hipGetErrorString(e));
+  }
+  return PKV_OK;
+  PKV_TRY_END
+}

@@ -1,0 +1,831 @@
+// Paged decode attention for gfx950 (MI355X).
+//
+// What is computed ("PagedAttention Internals", "The Block Table Map";
+// "pagedattention" topic page, third paragraph: attention follows each
+// sequence's block table to its keys and values): for sequence b, query head
+// h, KV head g = h / G, context length L,
+//     out[b,h] = sum_{t<L} softmax_t(scale * q[b,h] . K[t,g]) V[t,g]
+// with K[t,g] = k_cache[table[b][t/P], g, t%P, :] and
+//      V[t,g] = v_cache[table[b][t/P], g, :, t%P].
+//
+// Work decomposition.  A sequence's tokens are cut into partitions of T
+// tokens (T a power of two, chosen on the host from the batch's size).  One
+// wavefront handles one (partition, KV head) unit and all G query heads that
+// share that KV head, so each key/value byte is read from HBM exactly once.
+// A small plan kernel lays the units out: full partitions first, the shorter
+// last partitions of every sequence at the end of the grid, so the tail of
+// the launch is made of short units.  A sequence with one partition writes its
+// output directly; otherwise each partition writes (max, sum, normalised
+// output) in fp32 and the merge kernel combines them.  Summation order depends
+// only on logical token positions and T, never on where the blocks sit.
+//
+// Two partition kernels:
+//  * decode_mfma_kernel (bf16, head_dim 64/128, block size 8/16/32, G <= 16):
+//    scores and the value product run on v_mfma_f32_16x16x32_bf16 with the
+//    head group as the 16-wide N dimension (padded with zero queries).  Each
+//    lane loads exactly the 16-byte operand fragments it feeds to the matrix
+//    core straight from HBM (keys token-major, values token-minor), with the
+//    next 32-token chunk's loads in flight while the current one is computed.
+//    The score fragment a lane receives is already the probability fragment
+//    it must feed to the value product, so no data moves between lanes except
+//    for the two-step max / sum reductions across the four 16-lane rows.
+//  * decode_valu_kernel (any dtype / shape within limits): one token per lane
+//    for scores, one head_dim element per lane for the value product, wave
+//    reductions for max and sum.  Used for fp32, for single-head groups and
+//    for shapes the matrix-core kernel does not cover.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct Plan {
+  int32_t* counts;     // [0] full units F, [1] ragged units R
+  int32_t* seq_info;   // [3 * n_seqs]: first full row, number of full rows, ragged row or -1
+  int2* work;          // [max_units]: (sequence, partition index)
+  float* part_ml;      // [max_units * Hq * 2]: running max (log2 units), sum
+  float* part_o;       // [max_units * Hq * D]: normalised partial output
+};
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const int32_t* table;
+  const int32_t* ctx;
+  int32_t n_seqs, hq, hkv, d, p, num_blocks, max_blocks, part_tokens, max_units;
+  int64_t len_cap;   // min(max_blocks * p, max_context_len): longer contexts are clamped
+  float scale_log2;  // scale * log2(e): scores are kept in log2 units
+  Plan plan;
+  int32_t* err;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) {
+  return __uint_as_float((uint32_t)x << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ float load_f32(const T* p);
+template <>
+__device__ __forceinline__ float load_f32<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float load_f32<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+
+template <typename T>
+__device__ __forceinline__ void store_f32(T* p, float v);
+template <>
+__device__ __forceinline__ void store_f32<float>(float* p, float v) { *p = v; }
+template <>
+__device__ __forceinline__ void store_f32<uint16_t>(uint16_t* p, float v) {
+  const __bf16 b = (__bf16)v;  // round to nearest even
+  *p = __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Unit bookkeeping common to both partition kernels.
+struct Unit {
+  int32_t b, part, t0, t1, nparts, valid;
+};
+
+__device__ __forceinline__ Unit decode_unit(const DecodeArgs& a, int32_t unit) {
+  Unit u;
+  const int32_t F = a.plan.counts[0], R = a.plan.counts[1];
+  u.valid = unit < F || (unit >= a.max_units - R && unit < a.max_units);
+  if (!u.valid) return u;
+  const int2 w = a.plan.work[unit];
+  u.b = w.x;
+  u.part = w.y;
+  int64_t L = a.ctx[u.b];
+  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
+  u.t0 = u.part * a.part_tokens;
+  u.t1 = (int32_t)(L < (int64_t)u.t0 + a.part_tokens ? L : (int64_t)u.t0 + a.part_tokens);
+  const int32_t* si = a.plan.seq_info + 3 * u.b;
+  u.nparts = si[1] + (si[2] >= 0 ? 1 : 0);
+  return u;
+}
+
+// ---------------------------------------------------------------------------
+// Plan: per sequence, floor(L/T) full partitions and (L % T != 0 or L == 0)
+// one ragged partition.  Full units fill rows [0, F) in sequence order,
+// ragged units fill rows [max_units - R, max_units).  One workgroup.
+// ---------------------------------------------------------------------------
+__device__ int32_t block_exclusive_scan(int32_t v, int32_t* smem, int32_t* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int nw = blockDim.x >> 6;
+  int32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) smem[wid] = x;
+  __syncthreads();
+  int32_t before = 0, tot = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int32_t t = smem[w];
+    before += w < wid ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(1024) void plan_kernel(DecodeArgs a) {
+  __shared__ int32_t smem[16];
+  const int32_t T = a.part_tokens;
+  const int64_t cap = a.len_cap;
+  int32_t full_base = 0, ragged_base = 0;
+  for (int32_t base = 0; base < a.n_seqs; base += blockDim.x) {
+    const int32_t b = base + threadIdx.x;
+    int32_t nfull = 0, rag = 0;
+    if (b < a.n_seqs) {
+      int64_t L = a.ctx[b];
+      if (L < 0 || L > cap) {
+        atomicOr(a.err, PKV_DEVERR_CONTEXT_LEN);
+        L = L < 0 ? 0 : cap;
+      }
+      nfull = (int32_t)(L / T);
+      rag = (L % T != 0 || L == 0) ? 1 : 0;
+    }
+    int32_t ftot, rtot;
+    const int32_t fo = full_base + block_exclusive_scan(nfull, smem, &ftot);
+    const int32_t ro = ragged_base + block_exclusive_scan(rag, smem, &rtot);
+    if (b < a.n_seqs) {
+      const int32_t rrow = rag ? a.max_units - 1 - ro : -1;
+      a.plan.seq_info[3 * b + 0] = fo;
+      a.plan.seq_info[3 * b + 1] = nfull;
+      a.plan.seq_info[3 * b + 2] = rrow;
+      // rows must stay inside [0, F) and [max_units - R, max_units) without overlap
+      for (int32_t j = 0; j < nfull; ++j)
+        if (fo + j < a.max_units) a.plan.work[fo + j] = make_int2(b, j);
+      if (rag && rrow >= 0) a.plan.work[rrow] = make_int2(b, nfull);
+    }
+    full_base += ftot;
+    ragged_base += rtot;
+  }
+  if (threadIdx.x == 0) {
+    int32_t F = full_base, R = ragged_base;
+    if ((int64_t)F + R > a.max_units) {
+      atomicOr(a.err, PKV_DEVERR_WORK_OVERFLOW);
+      F = 0;  // run nothing rather than overlapping rows
+      R = 0;
+    }
+    a.plan.counts[0] = F;
+    a.plan.counts[1] = R;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core partition kernel.
+//
+// Lane l of a wave: n = l % 16 (query head within the group, the MFMA N
+// index) and r = l / 16 (row group).  A 32-token chunk starting at c0:
+//   scores  S^T[tok, n] = K[tok, :] . Q[n, :] as two 16x16x32 MFMA chains
+//           over head_dim: chain X holds tokens c0 + 8r' + i (i < 4) in
+//           output row 4r' + i, chain Y holds c0 + 8r' + 4 + i.  So lane l
+//           receives the scores of head n for tokens c0 + 8r + s, s = 0..7.
+//   values  O^T[dim, n] += V^T[dim, tok] P^T[tok, n] with the MFMA reduction
+//           index k = 8r + s mapped to token c0 + 8r + s: the B operand of
+//           lane l is exactly its own eight probabilities, and its A operand
+//           is the 16-byte run v_cache[blk, g, dim, off .. off+7].
+// Key fragments: lane l reads 16 bytes of token row (chain X/Y row l % 16) at
+// head_dim offset 32 i + 8 r for MFMA step i.
+// ---------------------------------------------------------------------------
+template <int D, int P>
+struct MfmaChunk {
+  static constexpr int KI = D / 32;  // MFMA steps over head_dim (scores)
+  static constexpr int NJ = D / 16;  // 16-row output tiles over head_dim (values)
+  uint4 kx[KI], ky[KI], v[NJ];
+};
+
+template <int D, int P, int WPB>
+__global__ __launch_bounds__(64 * WPB) void decode_mfma_kernel(DecodeArgs a) {
+  using Chunk = MfmaChunk<D, P>;
+  constexpr int KI = Chunk::KI, NJ = Chunk::NJ;
+  constexpr int CH = 32;  // tokens per chunk
+  static_assert(P % 8 == 0 && (P <= CH ? CH % P == 0 : P % CH == 0), "block size");
+  const int lane = threadIdx.x & 63;
+  const int32_t wave = blockIdx.x * WPB + uniform(threadIdx.x >> 6);
+  const int32_t unit = uniform(wave / a.hkv);
+  const int32_t g = wave - unit * a.hkv;
+  if (unit >= a.max_units) return;
+  const Unit u = decode_unit(a, unit);
+  if (!u.valid) return;
+  const int32_t G = a.hq / a.hkv;
+  const int n = lane & 15, r = lane >> 4;
+  const int32_t head = g * G + n;
+  const bool head_ok = n < G;
+
+  const uint16_t* kc = (const uint16_t*)a.kc;
+  const uint16_t* vc = (const uint16_t*)a.vc;
+  const int64_t blk_stride = (int64_t)a.hkv * P * D;  // elements per physical block
+  const int64_t head_off = (int64_t)g * P * D;
+
+  f32x4 acc[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c = a.scale_log2;
+
+  if (u.t1 > u.t0) {
+    // query fragments (B operand of the score MFMA): head n, dims 32 i + 8 r
+    bf16x8 qf[KI];
+    {
+      const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)u.b * a.hq + head) * D + 8 * r;
+#pragma unroll
+      for (int i = 0; i < KI; ++i) {
+        uint4 x = head_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * i) : uint4{0, 0, 0, 0};
+        qf[i] = __builtin_bit_cast(bf16x8, x);
+      }
+    }
+    const int32_t* trow = a.table + (int64_t)u.b * a.max_blocks;
+    // block-table window: lane i holds the entry of logical block wb + i
+    int32_t wb = u.t0 / P;
+    const int32_t last_blk = (u.t1 - 1) / P;
+    auto load_window = [&](int32_t base) -> int32_t {
+      int32_t e = 0;
+      if (base + lane <= last_blk) {
+        e = trow[base + lane];
+        if ((uint32_t)e >= (uint32_t)a.num_blocks) {
+          atomicOr(a.err, PKV_DEVERR_TABLE_ENTRY);
+          e = 0;
+        }
+      }
+      return e;
+    };
+    int32_t tabv = load_window(wb);
+
+    // per-lane pieces of the chunk addresses
+    const int32_t krow_x = 8 * (n >> 2) + (n & 3);  // token of chain-X row n within the chunk
+    const int32_t tlast = u.t1 - 1;
+
+    auto issue = [&](Chunk& f, int32_t c0) {
+      const int32_t cb = c0 / P;
+      if (cb - wb >= 64) {  // uniform; only without splitting
+        wb = cb;
+        tabv = load_window(wb);
+      }
+      // keys: rows of chain X / Y, clamped to the last valid token
+      const int32_t tx = min(c0 + krow_x, tlast);
+      const int32_t ty = min(c0 + krow_x + 4, tlast);
+      const int32_t pk = __shfl(tabv, tx / P - wb, 64);
+      const uint16_t* kb = kc + (int64_t)pk * blk_stride + head_off + 8 * r;
+      const uint16_t* kxp = kb + (tx % P) * D;
+      const uint16_t* kyp = kb + (ty % P) * D;
+#pragma unroll
+      for (int i = 0; i < KI; ++i) {
+        f.kx[i] = *reinterpret_cast<const uint4*>(kxp + 32 * i);
+        f.ky[i] = *reinterpret_cast<const uint4*>(kyp + 32 * i);
+      }
+      // values: tokens c0 + 8 r .. +7 of head_dim rows 16 j + n
+      const int32_t tv = min(c0 + 8 * r, tlast);
+      const int32_t pv = __shfl(tabv, tv / P - wb, 64);
+      const uint16_t* vb = vc + (int64_t)pv * blk_stride + head_off + (int64_t)n * P + ((tv % P) & ~7);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) f.v[j] = *reinterpret_cast<const uint4*>(vb + 16 * j * P);
+    };
+
+    auto compute = [&](Chunk& f, int32_t c0) {
+      f32x4 sx = {0.f, 0.f, 0.f, 0.f}, sy = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < KI; ++i) {
+        sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.kx[i]), qf[i], sx, 0, 0, 0);
+        sy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.ky[i]), qf[i], sy, 0, 0, 0);
+      }
+      float s[8] = {sx[0], sx[1], sx[2], sx[3], sy[0], sy[1], sy[2], sy[3]};
+      if (c0 + 32 > u.t1) {  // ragged chunk (uniform): mask tokens >= t1
+        const int32_t nv = min(max(u.t1 - (c0 + 8 * r), 0), 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] = e < nv ? s[e] : -INFINITY;
+        // zero the value columns of masked tokens so stale data cannot leak
+        const uint32_t m0 = nv >= 2 ? 0xffffffffu : (nv == 1 ? 0x0000ffffu : 0u);
+        const uint32_t m1 = nv >= 4 ? 0xffffffffu : (nv == 3 ? 0x0000ffffu : 0u);
+        const uint32_t m2 = nv >= 6 ? 0xffffffffu : (nv == 5 ? 0x0000ffffu : 0u);
+        const uint32_t m3 = nv >= 8 ? 0xffffffffu : (nv == 7 ? 0x0000ffffu : 0u);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          f.v[j].x &= m0;
+          f.v[j].y &= m1;
+          f.v[j].z &= m2;
+          f.v[j].w &= m3;
+        }
+      }
+      float cm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                       fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+      cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+      cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+      const float m_new = fmaxf(m_run, cm);
+      const float alpha = fast_exp2((m_run - m_new) * c);
+      const float mc = m_new * c;
+      bf16x8 pb;
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const __bf16 x = (__bf16)fast_exp2(fmaf(s[e], c, -mc));
+        pb[e] = x;
+        psum += (float)x;
+      }
+      l_run = fmaf(l_run, alpha, psum);
+      m_run = m_new;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        acc[j] *= alpha;
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.v[j]), pb, acc[j], 0, 0, 0);
+      }
+    };
+
+    Chunk f0, f1;
+    int32_t c0 = u.t0;
+    issue(f0, c0);
+    while (true) {
+      int32_t c1 = c0 + CH;
+      if (c1 < u.t1) issue(f1, c1);
+      compute(f0, c0);
+      if (c1 >= u.t1) break;
+      c0 = c1;
+      c1 = c0 + CH;
+      if (c1 < u.t1) issue(f0, c1);
+      compute(f1, c0);
+      if (c1 >= u.t1) break;
+      c0 = c1;
+    }
+  }
+
+  // totals per head: the four row groups hold disjoint token subsets
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (!head_ok) return;
+  if (u.nparts == 1) {
+    uint16_t* orow = (uint16_t*)a.out + ((int64_t)u.b * a.hq + head) * D + 4 * r;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const __bf16 o0 = (__bf16)(acc[j][0] * inv), o1 = (__bf16)(acc[j][1] * inv);
+      const __bf16 o2 = (__bf16)(acc[j][2] * inv), o3 = (__bf16)(acc[j][3] * inv);
+      uint2 w;
+      w.x = (uint32_t)__builtin_bit_cast(uint16_t, o0) | ((uint32_t)__builtin_bit_cast(uint16_t, o1) << 16);
+      w.y = (uint32_t)__builtin_bit_cast(uint16_t, o2) | ((uint32_t)__builtin_bit_cast(uint16_t, o3) << 16);
+      *reinterpret_cast<uint2*>(orow + 16 * j) = w;
+    }
+  } else {
+    float* prow = a.plan.part_o + ((int64_t)unit * a.hq + head) * D + 4 * r;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      *reinterpret_cast<float4*>(prow + 16 * j) =
+          make_float4(acc[j][0] * inv, acc[j][1] * inv, acc[j][2] * inv, acc[j][3] * inv);
+    if (r == 0) {
+      float* ml = a.plan.part_ml + ((int64_t)unit * a.hq + head) * 2;
+      ml[0] = m_run * c;
+      ml[1] = l_tot;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// VALU partition kernel: one wave per unit, any block size, head_dim <= 256.
+// ---------------------------------------------------------------------------
+template <typename T, int GMAX, int DK>
+__global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
+  __shared__ float qs[GMAX][DK * 64];
+  __shared__ float ps[GMAX][64];
+  const int lane = threadIdx.x;
+  const int32_t unit = blockIdx.x / a.hkv;
+  const int32_t g = blockIdx.x - unit * a.hkv;
+  if (unit >= a.max_units) return;
+  const Unit u = decode_unit(a, unit);
+  if (!u.valid) return;
+  const int32_t G = a.hq / a.hkv, D = a.d, P = a.p;
+  const T* q = (const T*)a.q;
+  const T* kc = (const T*)a.kc;
+  const T* vc = (const T*)a.vc;
+  const int32_t* trow = a.table + (int64_t)u.b * a.max_blocks;
+
+  for (int32_t i = lane; i < G * D; i += 64)
+    qs[i / D][i % D] = load_f32(q + ((int64_t)u.b * a.hq + (int64_t)g * G) * D + i);
+  __syncthreads();
+
+  float m[GMAX], l[GMAX], acc[GMAX][DK];
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int k = 0; k < DK; ++k) acc[h][k] = 0.f;
+  }
+  const float c = a.scale_log2;
+  auto phys_of = [&](int32_t t) -> int64_t {
+    int32_t e = trow[t / P];
+    if ((uint32_t)e >= (uint32_t)a.num_blocks) {
+      atomicOr(a.err, PKV_DEVERR_TABLE_ENTRY);
+      e = 0;
+    }
+    return e;
+  };
+
+  for (int32_t c0 = u.t0; c0 < u.t1; c0 += 64) {
+    const int32_t t = c0 + lane;
+    const bool valid = t < u.t1;
+    float s[GMAX];
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) s[h] = 0.f;
+    if (valid) {
+      const T* kr = kc + ((phys_of(t) * a.hkv + g) * P + t % P) * D;
+      for (int32_t dd = 0; dd < D; ++dd) {
+        const float kv = load_f32(kr + dd);
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h)
+          if (h < G) s[h] = fmaf(qs[h][dd], kv, s[h]);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) {
+      if (h >= G) continue;
+      const float sh = valid ? s[h] * c : -INFINITY;
+      const float mn = fmaxf(m[h], wave_max(sh));
+      const float al = fast_exp2(m[h] - mn);
+      const float pv = fast_exp2(sh - mn);
+      l[h] = fmaf(l[h], al, wave_sum(pv));
+      ps[h][lane] = pv;
+#pragma unroll
+      for (int k = 0; k < DK; ++k) acc[h][k] *= al;
+      m[h] = mn;
+    }
+    __syncthreads();
+    const int32_t nt = min(64, u.t1 - c0);
+    for (int32_t i = 0; i < nt; ++i) {
+      const int32_t tt = c0 + i;
+      const T* vcol = vc + (phys_of(tt) * a.hkv + g) * D * P + tt % P;
+#pragma unroll
+      for (int k = 0; k < DK; ++k) {
+        const int32_t dd = lane + 64 * k;
+        if (dd < D) {
+          const float vv = load_f32(vcol + (int64_t)dd * P);
+#pragma unroll
+          for (int h = 0; h < GMAX; ++h)
+            if (h < G) acc[h][k] = fmaf(ps[h][i], vv, acc[h][k]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) {
+    if (h >= G) continue;
+    const int32_t head = g * G + h;
+    const float inv = l[h] > 0.f ? 1.f / l[h] : 0.f;
+    if (u.nparts == 1) {
+      T* orow = (T*)a.out + ((int64_t)u.b * a.hq + head) * D;
+#pragma unroll
+      for (int k = 0; k < DK; ++k) {
+        const int32_t dd = lane + 64 * k;
+        if (dd < D) store_f32(orow + dd, acc[h][k] * inv);
+      }
+    } else {
+      float* prow = a.plan.part_o + ((int64_t)unit * a.hq + head) * D;
+#pragma unroll
+      for (int k = 0; k < DK; ++k) {
+        const int32_t dd = lane + 64 * k;
+        if (dd < D) prow[dd] = acc[h][k] * inv;
+      }
+      if (lane == 0) {
+        float* ml = a.plan.part_ml + ((int64_t)unit * a.hq + head) * 2;
+        ml[0] = m[h];
+        ml[1] = l[h];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge: out = sum_p w_p o_p / sum_p w_p, w_p = l_p * 2^(m_p - max_p m_p).
+// grid (n_seqs, ceil(Hq / 4)), one wave per query head.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
+  const int32_t b = blockIdx.x;
+  const int32_t* si = a.plan.seq_info + 3 * b;
+  const int32_t f0 = si[0], nf = si[1], rr = si[2];
+  const int32_t n = nf + (rr >= 0 ? 1 : 0);
+  if (n <= 1) return;
+  if (a.plan.counts[0] + a.plan.counts[1] == 0) return;  // plan overflowed
+  const int32_t head = blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (head >= a.hq) return;
+  const int lane = threadIdx.x & 63;
+  auto row = [&](int32_t i) -> int64_t { return i < nf ? f0 + i : rr; };
+  float mx = -INFINITY;
+  for (int32_t i = 0; i < n; ++i) mx = fmaxf(mx, a.plan.part_ml[(row(i) * a.hq + head) * 2]);
+  float wsum = 0.f;
+  for (int32_t i = 0; i < n; ++i) {
+    const float* ml = a.plan.part_ml + (row(i) * a.hq + head) * 2;
+    wsum += ml[1] * fast_exp2(ml[0] - mx);
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  for (int32_t dd = lane; dd < a.d; dd += 64) {
+    float o = 0.f;
+    for (int32_t i = 0; i < n; ++i) {
+      const int64_t rw = row(i);
+      const float* ml = a.plan.part_ml + (rw * a.hq + head) * 2;
+      const float w = ml[1] * fast_exp2(ml[0] - mx);
+      o = fmaf(w, a.plan.part_o[(rw * a.hq + head) * a.d + dd], o);
+    }
+    store_f32((T*)a.out + ((int64_t)b * a.hq + head) * a.d + dd, o * inv);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side: partition size, workspace layout, dispatch.
+// ---------------------------------------------------------------------------
+int device_cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+int32_t env_int(const char* name, int32_t dflt) {
+  const char* s = std::getenv(name);
+  if (!s || !*s) return dflt;
+  return (int32_t)std::strtol(s, nullptr, 10);
+}
+
+bool env_is(const char* name, const char* val) {
+  const char* s = std::getenv(name);
+  return s && std::strcmp(s, val) == 0;
+}
+
+int32_t pow2_floor(int64_t x) {
+  int32_t p = 1;
+  while ((int64_t)p * 2 <= x && p < (1 << 30)) p *= 2;
+  return p;
+}
+
+struct Choice {
+  bool mfma;
+  int32_t part_tokens;
+  int64_t max_units;
+  bool need_partials;
+};
+
+enum { kMathAuto, kMathValu, kMathMfma };
+
+int math_mode() {
+  if (env_is("PKV_DECODE_MATH", "valu")) return kMathValu;
+  if (env_is("PKV_DECODE_MATH", "mfma")) return kMathMfma;
+  return kMathAuto;
+}
+
+bool mfma_shape_ok(int32_t hq, int32_t hkv, int32_t d, int32_t p, pkv_dtype dt) {
+  const int32_t G = hq / hkv;
+  return dt == PKV_BF16 && (d == 64 || d == 128) && (p == 8 || p == 16 || p == 32) && G >= 1 && G <= 16;
+}
+
+bool valu_shape_ok(int32_t hq, int32_t hkv, int32_t d) { return d <= 256 && hq / hkv <= 16; }
+
+int choose(int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t p, int32_t max_len,
+           int64_t total, pkv_dtype dt, Choice* out) {
+  const int mode = math_mode();
+  const bool mshape = mfma_shape_ok(hq, hkv, d, p, dt);
+  bool mfma;
+  if (mode == kMathMfma) {
+    if (!mshape) return fail(PKV_ERR_UNSUPPORTED, "matrix-core decode needs bf16, head_dim 64/128, block 8/16/32, G <= 16");
+    mfma = true;
+  } else if (mode == kMathValu) {
+    mfma = false;
+  } else {
+    mfma = mshape && hq / hkv >= 2;  // matrix cores only when a head group shares K/V
+  }
+  if (!mfma && !valu_shape_ok(hq, hkv, d))
+    return fail(PKV_ERR_UNSUPPORTED, "decode supports head_dim <= 256 and Hq/Hkv <= 16");
+  const int64_t L = std::max<int32_t>(max_len, 1);
+  if (total < 0) total = (int64_t)n_seqs * L;
+  int32_t T;
+  const int32_t forced = env_int("PKV_PARTITION_TOKENS", 0);
+  const int32_t tmax = mfma ? std::min(512, 64 * p) : 512;
+  if (env_is("PKV_DECODE_SPLIT", "off")) {
+    T = 64;
+    while (T < L) T *= 2;
+  } else if (forced > 0) {
+    T = std::max(64, pow2_floor(forced));
+  } else {
+    const int64_t want = total * hkv / ((int64_t)device_cu_count() * 16);
+    T = std::min<int64_t>(tmax, std::max<int64_t>(64, pow2_floor(std::max<int64_t>(want, 1))));
+  }
+  const int64_t by_len = (int64_t)n_seqs * ((L + T - 1) / T);
+  const int64_t by_total = total / T + n_seqs;
+  out->mfma = mfma;
+  out->part_tokens = T;
+  out->max_units = std::max<int64_t>(1, std::min(by_len, by_total));
+  out->need_partials = T < L;
+  return PKV_OK;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Layout {
+  size_t counts, seq_info, work, part_ml, part_o, total;
+};
+
+Layout layout_of(int32_t n_seqs, int32_t hq, int32_t d, const Choice& c) {
+  Layout l;
+  size_t off = 0;
+  l.counts = off;
+  off = align256(off + 2 * sizeof(int32_t));
+  l.seq_info = off;
+  off = align256(off + (size_t)3 * n_seqs * sizeof(int32_t));
+  l.work = off;
+  off = align256(off + (size_t)c.max_units * sizeof(int2));
+  l.part_ml = off;
+  if (c.need_partials) off = align256(off + (size_t)c.max_units * hq * 2 * sizeof(float));
+  l.part_o = off;
+  if (c.need_partials) off = align256(off + (size_t)c.max_units * hq * d * sizeof(float));
+  l.total = off;
+  return l;
+}
+
+template <int D, int P>
+void launch_mfma(const DecodeArgs& a, int64_t waves, hipStream_t st) {
+  constexpr int WPB = 4;
+  const int64_t blocks = (waves + WPB - 1) / WPB;
+  hipLaunchKernelGGL((decode_mfma_kernel<D, P, WPB>), dim3((unsigned)blocks), dim3(64 * WPB), 0, st, a);
+}
+
+template <typename T, int GMAX>
+void launch_valu_g(const DecodeArgs& a, int64_t waves, hipStream_t st) {
+  const int dk = (a.d + 63) / 64;
+  switch (dk) {
+    case 1: hipLaunchKernelGGL((decode_valu_kernel<T, GMAX, 1>), dim3((unsigned)waves), dim3(64), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((decode_valu_kernel<T, GMAX, 2>), dim3((unsigned)waves), dim3(64), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((decode_valu_kernel<T, GMAX, 3>), dim3((unsigned)waves), dim3(64), 0, st, a); break;
+    default: hipLaunchKernelGGL((decode_valu_kernel<T, GMAX, 4>), dim3((unsigned)waves), dim3(64), 0, st, a); break;
+  }
+}
+
+template <typename T>
+void launch_valu(const DecodeArgs& a, int64_t waves, hipStream_t st) {
+  const int32_t G = a.hq / a.hkv;
+  if (G <= 1) launch_valu_g<T, 1>(a, waves, st);
+  else if (G <= 2) launch_valu_g<T, 2>(a, waves, st);
+  else if (G <= 4) launch_valu_g<T, 4>(a, waves, st);
+  else if (G <= 8) launch_valu_g<T, 8>(a, waves, st);
+  else launch_valu_g<T, 16>(a, waves, st);
+}
+
+}  // namespace
+}  // namespace pkv
+
+using pkv::fail;
+
+extern "C" int pkv_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t block_size,
+                                          int32_t max_context_len, int64_t total_context_tokens,
+                                          pkv_dtype dtype, size_t* bytes_out) {
+  PKV_TRY_BEGIN
+  if (!bytes_out) return fail(PKV_ERR_INVALID_ARG, "bytes_out is NULL");
+  if (n_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_context_len < 0 || num_q_heads % num_kv_heads)
+    return fail(PKV_ERR_INVALID_ARG, "bad sizes");
+  if (!pkv::dtype_valid(dtype)) return fail(PKV_ERR_INVALID_ARG, "bad dtype");
+  pkv::Choice c;
+  int rc = pkv::choose(n_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                       total_context_tokens, dtype, &c);
+  if (rc) return rc;
+  *bytes_out = pkv::layout_of(n_seqs, num_q_heads, head_dim, c).total;
+  return PKV_OK;
+  PKV_TRY_END
+}
+
+extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
+                                          const void* v_cache, const int32_t* d_block_table,
+                                          const int32_t* d_context_lens, int32_t n_seqs,
+                                          int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                          int32_t max_blocks_per_seq, int32_t max_context_len,
+                                          int64_t total_context_tokens, float scale,
+                                          pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  PKV_TRY_BEGIN
+  if (n_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0 || max_blocks_per_seq < 0 || max_context_len < 0)
+    return fail(PKV_ERR_INVALID_ARG, "bad sizes");
+  if (num_q_heads % num_kv_heads) return fail(PKV_ERR_INVALID_ARG, "num_q_heads % num_kv_heads != 0");
+  if (!pkv::dtype_valid(dtype)) return fail(PKV_ERR_INVALID_ARG, "bad dtype");
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(PKV_ERR_INVALID_ARG, "scale must be finite and positive");
+  if (n_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !d_context_lens || (max_blocks_per_seq > 0 && !d_block_table))
+    return fail(PKV_ERR_INVALID_ARG, "NULL pointer");
+  if ((int64_t)max_blocks_per_seq * block_size < max_context_len)
+    return fail(PKV_ERR_INVALID_ARG, "max_context_len exceeds the block-table capacity");
+  pkv::Choice c;
+  int rc = pkv::choose(n_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                       total_context_tokens, dtype, &c);
+  if (rc) return rc;
+  if (c.mfma) {
+    const uintptr_t mis = (uintptr_t)out | (uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache;
+    if (mis % 16) {
+      if (pkv::math_mode() == pkv::kMathMfma)
+        return fail(PKV_ERR_UNSUPPORTED, "matrix-core decode needs 16-byte aligned buffers");
+      c.mfma = false;
+    }
+  }
+  if ((int64_t)c.max_units * num_kv_heads > (int64_t)INT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, "too many partitions");
+  const pkv::Layout lay = pkv::layout_of(n_seqs, num_q_heads, head_dim, c);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, lay.total);
+  int32_t* err = nullptr;
+  rc = pkv::device_error_word(&err);
+  if (rc) return rc;
+
+  char* ws = (char*)workspace;
+  pkv::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.table = d_block_table;
+  a.ctx = d_context_lens;
+  a.n_seqs = n_seqs;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.d = head_dim;
+  a.p = block_size;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.part_tokens = c.part_tokens;
+  a.max_units = (int32_t)c.max_units;
+  a.len_cap = std::min<int64_t>((int64_t)max_blocks_per_seq * block_size, max_context_len);
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.plan.counts = (int32_t*)(ws + lay.counts);
+  a.plan.seq_info = (int32_t*)(ws + lay.seq_info);
+  a.plan.work = (int2*)(ws + lay.work);
+  a.plan.part_ml = c.need_partials ? (float*)(ws + lay.part_ml) : nullptr;
+  a.plan.part_o = c.need_partials ? (float*)(ws + lay.part_o) : nullptr;
+  a.err = err;
+
+  hipStream_t st = (hipStream_t)stream;
+  hipLaunchKernelGGL(pkv::plan_kernel, dim3(1), dim3(1024), 0, st, a);
+  const int64_t waves = c.max_units * num_kv_heads;
+  if (c.mfma) {
+    if (head_dim == 128) {
+      if (block_size == 8) pkv::launch_mfma<128, 8>(a, waves, st);
+      else if (block_size == 16) pkv::launch_mfma<128, 16>(a, waves, st);
+      else pkv::launch_mfma<128, 32>(a, waves, st);
+    } else {
+      if (block_size == 8) pkv::launch_mfma<64, 8>(a, waves, st);
+      else if (block_size == 16) pkv::launch_mfma<64, 16>(a, waves, st);
+      else pkv::launch_mfma<64, 32>(a, waves, st);
+    }
+  } else if (dtype == PKV_BF16) {
+    pkv::launch_valu<uint16_t>(a, waves, st);
+  } else {
+    pkv::launch_valu<float>(a, waves, st);
+  }
+  if (c.need_partials) {
+    const dim3 grid((unsigned)n_seqs, (unsigned)((num_q_heads + 3) / 4));
+    if (dtype == PKV_BF16)
+      hipLaunchKernelGGL(pkv::merge_kernel<uint16_t>, grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(pkv::merge_kernel<float>, grid, dim3(256), 0, st, a);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+  PKV_TRY_END
+}

@@ -1,0 +1,273 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer and byte work (slots, cache contents, copy-on-write) must match bit for
+bit; attention must be within 2e-2 absolute of float64 for bf16 inputs and
+within 1e-5 * max(1, max|ref|) for fp32 inputs.
+"""
+import dataclasses
+import os
+
+import numpy as np
+import pytest
+
+from tests.paged_case import (BF16_TOL, build_case, check_attention, expected_caches, host_bits,
+                              oracle_out, oracle_slots, say)
+from synth import CONFIGS, DecodeConfig
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu_guard(request):
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    say(f"\n[gpu] {request.node.name}")
+    yield
+    torch.cuda.synchronize()
+    import paged_kv_cache_399_amd as pkv
+    assert pkv.check_device_errors() == 0
+
+
+def _bits_equal(a, b):
+    a = np.ascontiguousarray(a)
+    b = np.ascontiguousarray(b)
+    view = np.uint32 if a.dtype == np.float32 else a.dtype
+    return np.array_equal(a.view(view), b.view(view))
+
+
+def _fill_bits(case, value):
+    import torch
+    t = torch.full((1,), value, dtype=case.w.torch_dtype)
+    return host_bits(t)[0]
+
+
+@pytest.mark.parametrize("name", ["tiny", "small_mha"])
+def test_small_configs_bit_exact_cache_and_attention(name):
+    cfg = CONFIGS[name]
+    case = build_case(cfg, seed=0, fill=7.0)
+    kc, vc, (pfx, pre, dec) = expected_caches(case, _fill_bits(case, 7.0))
+    assert np.array_equal(case.prefill_slots, pre)
+    assert np.array_equal(case.decode_slots, dec)
+    assert _bits_equal(host_bits(case.kv.k_cache), kc)
+    assert _bits_equal(host_bits(case.kv.v_cache), vc)
+    err = check_attention(case)
+    say(f"  max err {err:.3e}")
+
+
+def test_tiny_single_token_sequence_returns_its_value():
+    case = build_case(CONFIGS["tiny"], seed=0)
+    # sequence 0 has length 1: its output is its only value vector, exactly
+    k, v = case.w.seq_kv(0)
+    assert case.w.lengths[0] == 1
+    import torch
+    assert torch.equal(case.out[0], v[0].repeat(case.cfg.num_q_heads // case.cfg.num_kv_heads, 1))
+
+
+def test_tiny_fragmentation_matches_worked_example():
+    case = build_case(CONFIGS["tiny"], seed=0, run_decode=True)
+    st = case.kv.pool.stats()
+    assert (st["allocated_slots"], st["wasted_slots"]) == (8, 1)
+    assert st["fragmentation"] == 0.125
+
+
+def test_printed_block_table_placement():
+    """A sequence placed on physical blocks 8, 3, 11 attends like its logical order."""
+    import torch
+    import paged_kv_cache_399_amd as pkv
+    from paged_kv_cache_399_amd.session import PagedKVCache
+    from oracle import attention as oatt
+    kv = PagedKVCache(16, 2, 1, 8, torch.float32, "cuda", fill=float("nan"))
+    sid = kv.new_sequences(1)[0]
+    kv.pool.set_table(sid, [8, 3, 11], 6)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    k = torch.rand((6, 1, 8), generator=g, device="cuda") * 2 - 1
+    v = torch.rand((6, 1, 8), generator=g, device="cuda") * 2 - 1
+    q = torch.rand((1, 1, 8), generator=g, device="cuda") * 2 - 1
+    slots = torch.tensor([8 * 2, 8 * 2 + 1, 3 * 2, 3 * 2 + 1, 11 * 2, 11 * 2 + 1],
+                         dtype=torch.int32, device="cuda")
+    kv.write_slots(slots, k, v)
+    m = kv.prepare([sid], 3, 1, 6, 6)
+    kv.upload(m)
+    out = torch.empty_like(q)
+    kv.attend(m, q, out)
+    ref = oatt.decode(q[0].cpu().numpy(), k.cpu().numpy(), v.cpu().numpy())
+    assert np.abs(out[0].double().cpu().numpy() - ref).max() <= 1e-5
+    assert torch.equal(kv.k_cache[8, 0, 1], k[1, 0]) and torch.equal(kv.v_cache[11, 0, :, 0], v[4, 0])
+
+
+def test_gqa_config_parity_and_cache():
+    cfg = CONFIGS["gqa"]
+    case = build_case(cfg, seed=0, fill=7.0)
+    kc, vc, (pfx, pre, dec) = expected_caches(case, _fill_bits(case, 7.0))
+    assert np.array_equal(case.prefill_slots, pre) and np.array_equal(case.decode_slots, dec)
+    assert _bits_equal(host_bits(case.kv.k_cache), kc)
+    assert _bits_equal(host_bits(case.kv.v_cache), vc)
+    err = check_attention(case)
+    say(f"  max err {err:.3e}")
+
+
+SMALL_GQA = dataclasses.replace(CONFIGS["gqa"], name="gqa_small", batch=12, length_lo=1,
+                                length_hi=1500)
+
+
+@pytest.mark.parametrize("env", [
+    {"PKV_DECODE_MATH": "valu"},
+    {"PKV_DECODE_MATH": "mfma"},
+    {"PKV_DECODE_SPLIT": "off"},
+    {"PKV_PARTITION_TOKENS": "64"},
+    {"PKV_DECODE_MATH": "valu", "PKV_PARTITION_TOKENS": "64"},
+])
+def test_every_path_matches_oracle(monkeypatch, env):
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    for cfg in (SMALL_GQA, CONFIGS["small_mha"]):
+        case = build_case(cfg, seed=1)
+        err = check_attention(case)
+        say(f"  {cfg.name} {env}: max err {err:.3e}")
+
+
+def test_split_and_single_pass_agree(monkeypatch):
+    import torch
+    a = build_case(SMALL_GQA, seed=2).out.clone()
+    monkeypatch.setenv("PKV_DECODE_SPLIT", "off")
+    b = build_case(SMALL_GQA, seed=2).out.clone()
+    assert (a.double() - b.double()).abs().max().item() <= BF16_TOL
+
+
+@pytest.mark.parametrize("cfg", [SMALL_GQA, CONFIGS["small_mha"], CONFIGS["tiny"]],
+                         ids=lambda c: c.name)
+def test_block_permutation_gives_identical_output(cfg):
+    import torch
+    a = build_case(cfg, seed=3)
+    rng = np.random.default_rng(99)
+    other = rng.permutation(a.w.num_blocks).astype(np.int32)
+    b = build_case(cfg, seed=3, free_order=other)
+    assert not np.array_equal(a.prefill_slots, b.prefill_slots)
+    assert torch.equal(a.out, b.out)
+
+
+@pytest.mark.parametrize("cfg", [SMALL_GQA, CONFIGS["small_mha"]], ids=lambda c: c.name)
+def test_poisoned_free_slots_do_not_leak(cfg):
+    import torch
+    a = build_case(cfg, seed=4, fill=float("nan"))
+    b = build_case(cfg, seed=4, fill=0.0)
+    assert torch.isfinite(a.out.float()).all()
+    assert torch.equal(a.out, b.out)
+
+
+@pytest.mark.parametrize("page", [8, 16, 32])
+def test_prefix_sharing_block_sizes(page):
+    cfg = dataclasses.replace(CONFIGS["prefix"], name=f"prefix_small_p{page}", batch=16,
+                              prefix_len=256, length_hi=200, block_size=page)
+    case = build_case(cfg, seed=0, fill=7.0)
+    kc, vc, (pfx, pre, dec) = expected_caches(case, _fill_bits(case, 7.0))
+    assert _bits_equal(host_bits(case.kv.k_cache), kc)
+    assert _bits_equal(host_bits(case.kv.v_cache), vc)
+    st = case.kv.pool.stats()
+    assert st["used_blocks"] < cfg.batch * (256 // page)          # prefix held once
+    err = check_attention(case)
+    say(f"  P={page}: max err {err:.3e}, frag {st['fragmentation']:.4f}")
+
+
+EDGE_LENGTHS = [1, 2, 7, 8, 9, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 1000]
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d,p", [
+    ("bf16", 8, 1, 128, 16), ("bf16", 32, 8, 128, 8), ("bf16", 16, 4, 64, 32),
+    ("bf16", 4, 4, 64, 16), ("f32", 8, 2, 64, 16), ("f32", 2, 1, 8, 3),
+    ("bf16", 16, 1, 128, 16),
+])
+@pytest.mark.parametrize("part", ["64", "auto"])
+def test_edge_lengths(monkeypatch, dtype, hq, hkv, d, p, part):
+    if part != "auto":
+        monkeypatch.setenv("PKV_PARTITION_TOKENS", part)
+    cfg = DecodeConfig(f"edge_{dtype}_{hq}_{hkv}_{d}_{p}", len(EDGE_LENGTHS), hq, hkv, d, p, dtype,
+                       "fixed", fixed_lengths=tuple(EDGE_LENGTHS))
+    case = build_case(cfg, seed=5)
+    err = check_attention(case)
+    say(f"  {cfg.name} part={part}: max err {err:.3e}")
+
+
+def test_empty_context_gives_zeros_and_empty_batch_is_a_no_op():
+    import torch
+    import paged_kv_cache_399_amd as pkv
+    from paged_kv_cache_399_amd.session import PagedKVCache
+    kv = PagedKVCache(8, 16, 2, 64, torch.bfloat16, "cuda")
+    seqs = kv.new_sequences(3)
+    g = torch.Generator(device="cuda").manual_seed(1)
+    k = torch.randn((5, 2, 64), generator=g, device="cuda").to(torch.bfloat16)
+    kv.write([seqs[1]], [5], k, k)
+    m = kv.prepare(seqs, 1, 8, 16, 16)
+    kv.upload(m)
+    q = torch.randn((3, 8, 64), generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.full_like(q, float("nan"))
+    kv.attend(m, q, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out[0], torch.zeros_like(out[0]))
+    assert torch.equal(out[2], torch.zeros_like(out[2]))
+    assert torch.isfinite(out[1].float()).all()
+    empty_q = q[:0]
+    pkv.paged_attention_decode(empty_q.clone(), empty_q, kv.k_cache, kv.v_cache,
+                               m.table[:0], m.lens[:0], 16)
+
+
+def test_copy_on_write_copies_match_oracle():
+    """Prefix of 3 tokens at page 2 shared by 3 sequences: two block copies."""
+    import torch
+    from paged_kv_cache_399_amd.session import PagedKVCache
+    from oracle import layout as olayout
+    from oracle.pool_model import PoolModel
+    nb, p, hkv, d = 10, 2, 2, 64
+    kv = PagedKVCache(nb, p, hkv, d, torch.bfloat16, "cuda", fill=7.0)
+    model = PoolModel(nb, p)
+    g = torch.Generator(device="cuda").manual_seed(3)
+    pk = torch.randn((3, hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    pv = torch.randn((3, hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    a = kv.new_sequences(1)[0]
+    ma = model.seq_create()
+    s0 = kv.write([a], [3], pk, pv)
+    m0, _ = model.append_slots([ma], [3])
+    b, c = kv.fork(a), kv.fork(a)
+    mb, mc = model.fork(ma), model.fork(ma)
+    nk = torch.randn((3, hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    nv = torch.randn((3, hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    s1 = kv.write([a, b, c], [1, 1, 1], nk, nv)
+    m1, mcow = model.append_slots([ma, mb, mc], [1, 1, 1])
+    assert s0.tolist() == m0 and s1.tolist() == m1 and len(mcow) == 2
+    fill = host_bits(torch.full((1,), 7.0, dtype=torch.bfloat16))[0]
+    kc = np.full((nb, hkv, p, d), fill, np.uint16)
+    vc = np.full((nb, hkv, d, p), fill, np.uint16)
+    olayout.write_tokens(kc, vc, m0, host_bits(pk), host_bits(pv))
+    for src, dst in mcow:
+        olayout.copy_block(kc, vc, src, dst)
+    olayout.write_tokens(kc, vc, m1, host_bits(nk), host_bits(nv))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(kv.k_cache), kc)
+    assert np.array_equal(host_bits(kv.v_cache), vc)
+
+
+def test_bad_indices_are_clamped_and_flagged():
+    import torch
+    import paged_kv_cache_399_amd as pkv
+    from paged_kv_cache_399_amd.session import PagedKVCache
+    kv = PagedKVCache(4, 16, 1, 64, torch.bfloat16, "cuda", fill=0.0)
+    k = torch.ones((2, 1, 64), dtype=torch.bfloat16, device="cuda")
+    slots = torch.tensor([3, 4 * 16 + 5], dtype=torch.int32, device="cuda")
+    pkv.cache_append(kv.k_cache, kv.v_cache, k, k, slots)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.check_device_errors()
+    assert "0x2" in str(e.value)
+    pkv.copy_blocks(kv.k_cache, kv.v_cache, np.array([[0, 9]]))
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.check_device_errors()
+    assert "0x4" in str(e.value)
+    table = torch.tensor([[0, 77]], dtype=torch.int32, device="cuda")
+    lens = torch.tensor([20], dtype=torch.int32, device="cuda")
+    q = torch.ones((1, 4, 64), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(q)
+    pkv.paged_attention_decode(out, q, kv.k_cache, kv.v_cache, table, lens, 20)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.check_device_errors()
+    assert "0x1" in str(e.value)
+    assert pkv.check_device_errors() == 0
