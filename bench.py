@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--check", action="store_true",
                     help="after timing, compare sampled outputs with the oracle")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="before the steps, run one device copy of this many MiB (a known-size "
+                         "reference for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -97,6 +100,14 @@ def main():
     log(f"[bench] setup {time.perf_counter() - t_setup:.1f}s: {cfg.name} B={b} Hq={hq} Hkv={hkv} "
         f"D={d} P={p} tokens={int(w.lengths.sum())} blocks={w.num_blocks}")
 
+    if args.calibrate_copy_mib:
+        src = torch.empty(args.calibrate_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
