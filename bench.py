@@ -60,6 +60,24 @@ def append_bytes(b, hkv, d, s):
     return 2 * 2 * b * hkv * d * s + 4 * b
 
 
+def measured_traffic(cfg_name, root):
+    """HBM bytes per decode from the committed counter summary, if it was taken
+    on the current decode kernel source (else None)."""
+    import hashlib
+    path = os.path.join(root, "profiles", f"paged_decode_{cfg_name}_traffic.json")
+    src = os.path.join(root, "paged_kv_cache_399_amd", "csrc", "decode_kernels.hip")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        with open(src, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != digest:
+        return None
+    return int(rec["traffic_bytes_per_decode"])
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -169,8 +187,9 @@ def main():
         "decode_bytes_per_step": int(dbytes),
         "fragmentation": round(float(np.mean(frag)), 6),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "paged_attention_decode (plan + partition + merge)"},
+                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(cfg.name, os.path.dirname(os.path.abspath(__file__))),
+                     "kernel": "paged_attention_decode (plan + partition + merge launches)"},
     }
     if args.check:
         result["check_max_err"] = check_sample(w, kv, meta, out, cfg)

@@ -73,7 +73,7 @@ def load():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m paged_kv_cache_399_amd.build` (hipcc, gfx950)")
+                          "`python paged_kv_cache_399_amd/build.py` (hipcc, gfx950)")
     lib = C.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

@@ -1,6 +1,6 @@
 """Build libpkv.so in-tree: host C++ with g++, HIP kernels with hipcc for gfx950.
 
-Usage: python -m paged_kv_cache_399_amd.build   (or __graft_entry__.build())
+Usage: python paged_kv_cache_399_amd/build.py   (or __graft_entry__.build())
 """
 from __future__ import annotations
 

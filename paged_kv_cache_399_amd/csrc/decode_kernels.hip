@@ -97,6 +97,15 @@ __device__ __forceinline__ void store_f32<uint16_t>(uint16_t* p, float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Keys and values are read once per decode step: streaming (nontemporal)
+// loads keep them from displacing reusable lines and raise read bandwidth.
+__device__ __forceinline__ uint4 load_stream16(const uint16_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return uint4{v.x, v.y, v.z, v.w};
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -227,19 +236,29 @@ struct MfmaChunk {
   uint4 kx[KI], ky[KI], v[NJ];
 };
 
-template <int D, int P, int WPB>
-__global__ __launch_bounds__(64 * WPB) void decode_mfma_kernel(DecodeArgs a) {
+// Workgroup of W waves per (partition, KV head) unit.  Wave w streams the
+// tokens [t0 + w TW, t0 + (w + 1) TW) of the partition (TW = T / W) with its
+// own running max, sum and accumulator; the W states are combined through
+// LDS at the end.  So a partial result goes to HBM once per workgroup, not
+// once per wave: partial-result writes interleaved with the key/value read
+// stream cost far more than their byte count.
+template <int D, int P, int W>
+__global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
   using Chunk = MfmaChunk<D, P>;
   constexpr int KI = Chunk::KI, NJ = Chunk::NJ;
-  constexpr int CH = 32;  // tokens per chunk
+  constexpr int CH = 32;     // tokens per chunk
+  constexpr int DP = D + 4;  // padded LDS row of one head's accumulator
   static_assert(P % 8 == 0 && (P <= CH ? CH % P == 0 : P % CH == 0), "block size");
+  __shared__ float red_o[W][16][DP];
+  __shared__ float red_m[W][16], red_l[W][16];
+
   const int lane = threadIdx.x & 63;
-  const int32_t wave = blockIdx.x * WPB + uniform(threadIdx.x >> 6);
-  const int32_t unit = uniform(wave / a.hkv);
-  const int32_t g = wave - unit * a.hkv;
-  if (unit >= a.max_units) return;
+  const int w = uniform(threadIdx.x >> 6);
+  const int32_t unit = blockIdx.x / a.hkv;
+  const int32_t g = blockIdx.x - unit * a.hkv;
+  if (unit >= a.max_units) return;  // uniform over the workgroup
   const Unit u = decode_unit(a, unit);
-  if (!u.valid) return;
+  if (!u.valid) return;             // uniform over the workgroup
   const int32_t G = a.hq / a.hkv;
   const int n = lane & 15, r = lane >> 4;
   const int32_t head = g * G + n;
@@ -256,7 +275,10 @@ __global__ __launch_bounds__(64 * WPB) void decode_mfma_kernel(DecodeArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c = a.scale_log2;
 
-  if (u.t1 > u.t0) {
+  const int32_t TW = a.part_tokens / W;  // a multiple of the chunk length
+  const int32_t s0 = u.t0 + w * TW;
+  const int32_t s1 = min(u.t1, s0 + TW);
+  if (s1 > s0) {
     // query fragments (B operand of the score MFMA): head n, dims 32 i + 8 r
     bf16x8 qf[KI];
     {
@@ -269,8 +291,7 @@ __global__ __launch_bounds__(64 * WPB) void decode_mfma_kernel(DecodeArgs a) {
     }
     const int32_t* trow = a.table + (int64_t)u.b * a.max_blocks;
     // block-table window: lane i holds the entry of logical block wb + i
-    int32_t wb = u.t0 / P;
-    const int32_t last_blk = (u.t1 - 1) / P;
+    const int32_t last_blk = (s1 - 1) / P;
     auto load_window = [&](int32_t base) -> int32_t {
       int32_t e = 0;
       if (base + lane <= last_blk) {
@@ -282,36 +303,28 @@ __global__ __launch_bounds__(64 * WPB) void decode_mfma_kernel(DecodeArgs a) {
       }
       return e;
     };
-    int32_t tabv = load_window(wb);
-
-    // per-lane pieces of the chunk addresses
+    int32_t wb = 0, tabv = 0, wlast = 0;
     const int32_t krow_x = 8 * (n >> 2) + (n & 3);  // token of chain-X row n within the chunk
-    const int32_t tlast = u.t1 - 1;
 
+    // Loads of one chunk; addresses are clamped to the window's last token.
     auto issue = [&](Chunk& f, int32_t c0) {
-      const int32_t cb = c0 / P;
-      if (cb - wb >= 64) {  // uniform; only without splitting
-        wb = cb;
-        tabv = load_window(wb);
-      }
-      // keys: rows of chain X / Y, clamped to the last valid token
-      const int32_t tx = min(c0 + krow_x, tlast);
-      const int32_t ty = min(c0 + krow_x + 4, tlast);
+      const int32_t tx = min(c0 + krow_x, wlast);
+      const int32_t ty = min(c0 + krow_x + 4, wlast);
       const int32_t pk = __shfl(tabv, tx / P - wb, 64);
       const uint16_t* kb = kc + (int64_t)pk * blk_stride + head_off + 8 * r;
       const uint16_t* kxp = kb + (tx % P) * D;
       const uint16_t* kyp = kb + (ty % P) * D;
 #pragma unroll
       for (int i = 0; i < KI; ++i) {
-        f.kx[i] = *reinterpret_cast<const uint4*>(kxp + 32 * i);
-        f.ky[i] = *reinterpret_cast<const uint4*>(kyp + 32 * i);
+        f.kx[i] = load_stream16(kxp + 32 * i);
+        f.ky[i] = load_stream16(kyp + 32 * i);
       }
       // values: tokens c0 + 8 r .. +7 of head_dim rows 16 j + n
-      const int32_t tv = min(c0 + 8 * r, tlast);
+      const int32_t tv = min(c0 + 8 * r, wlast);
       const int32_t pv = __shfl(tabv, tv / P - wb, 64);
       const uint16_t* vb = vc + (int64_t)pv * blk_stride + head_off + (int64_t)n * P + ((tv % P) & ~7);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) f.v[j] = *reinterpret_cast<const uint4*>(vb + 16 * j * P);
+      for (int j = 0; j < NJ; ++j) f.v[j] = load_stream16(vb + 16 * j * P);
     };
 
     auto compute = [&](Chunk& f, int32_t c0) {
@@ -322,8 +335,8 @@ __global__ __launch_bounds__(64 * WPB) void decode_mfma_kernel(DecodeArgs a) {
         sy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.ky[i]), qf[i], sy, 0, 0, 0);
       }
       float s[8] = {sx[0], sx[1], sx[2], sx[3], sy[0], sy[1], sy[2], sy[3]};
-      if (c0 + 32 > u.t1) {  // ragged chunk (uniform): mask tokens >= t1
-        const int32_t nv = min(max(u.t1 - (c0 + 8 * r), 0), 8);
+      if (c0 + CH > s1) {  // ragged chunk (uniform): mask tokens >= s1
+        const int32_t nv = min(max(s1 - (c0 + 8 * r), 0), 8);
 #pragma unroll
         for (int e = 0; e < 8; ++e) s[e] = e < nv ? s[e] : -INFINITY;
         // zero the value columns of masked tokens so stale data cannot leak
@@ -363,49 +376,73 @@ __global__ __launch_bounds__(64 * WPB) void decode_mfma_kernel(DecodeArgs a) {
       }
     };
 
-    Chunk f0, f1;
-    int32_t c0 = u.t0;
-    issue(f0, c0);
-    while (true) {
-      int32_t c1 = c0 + CH;
-      if (c1 < u.t1) issue(f1, c1);
-      compute(f0, c0);
-      if (c1 >= u.t1) break;
-      c0 = c1;
-      c1 = c0 + CH;
-      if (c1 < u.t1) issue(f0, c1);
-      compute(f1, c0);
-      if (c1 >= u.t1) break;
-      c0 = c1;
+    // Windows of 64 blocks (one table entry per lane).  Window starts are
+    // multiples of 64 P tokens past s0 (itself a multiple of the chunk
+    // length), so chunks never straddle two windows.  Within a window the
+    // next chunk's loads are in flight while the current one is computed;
+    // the prefetch past the window end reads clamped, in-bounds addresses.
+    for (int32_t ws = s0; ws < s1;) {
+      wb = uniform(ws / P);
+      const int32_t we = min(s1, (wb + 64) * P);
+      wlast = we - 1;
+      tabv = load_window(wb);
+      Chunk f0, f1;
+      int32_t c0 = ws;
+      issue(f0, c0);
+      while (true) {
+        issue(f1, c0 + CH);
+        compute(f0, c0);
+        c0 += CH;
+        if (c0 >= we) break;
+        issue(f0, c0 + CH);
+        compute(f1, c0);
+        c0 += CH;
+        if (c0 >= we) break;
+      }
+      ws = we;
     }
   }
 
-  // totals per head: the four row groups hold disjoint token subsets
+  // this wave's state -> LDS; the four row groups hold disjoint token subsets
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (!head_ok) return;
-  if (u.nparts == 1) {
-    uint16_t* orow = (uint16_t*)a.out + ((int64_t)u.b * a.hq + head) * D + 4 * r;
+  if (r == 0) {
+    red_m[w][n] = m_run;
+    red_l[w][n] = l_tot;
+  }
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const __bf16 o0 = (__bf16)(acc[j][0] * inv), o1 = (__bf16)(acc[j][1] * inv);
-      const __bf16 o2 = (__bf16)(acc[j][2] * inv), o3 = (__bf16)(acc[j][3] * inv);
-      uint2 w;
-      w.x = (uint32_t)__builtin_bit_cast(uint16_t, o0) | ((uint32_t)__builtin_bit_cast(uint16_t, o1) << 16);
-      w.y = (uint32_t)__builtin_bit_cast(uint16_t, o2) | ((uint32_t)__builtin_bit_cast(uint16_t, o3) << 16);
-      *reinterpret_cast<uint2*>(orow + 16 * j) = w;
+  for (int j = 0; j < NJ; ++j)
+    *reinterpret_cast<f32x4*>(&red_o[w][n][16 * j + 4 * r]) = acc[j];
+  __syncthreads();
+
+  // combine the W waves: out = sum_v 2^((m_v - M) c) o_v / sum_v 2^((m_v - M) c) l_v
+  for (int32_t e = threadIdx.x; e < G * D; e += 64 * W) {
+    const int32_t h = e / D, dd = e - h * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < W; ++v)
+      if (red_l[v][h] > 0.f) M = fmaxf(M, red_m[v][h]);
+    float sum = 0.f, o = 0.f;
+#pragma unroll
+    for (int v = 0; v < W; ++v) {
+      const float lv = red_l[v][h];
+      if (lv > 0.f) {
+        const float wt = fast_exp2((red_m[v][h] - M) * c);
+        sum = fmaf(lv, wt, sum);
+        o = fmaf(wt, red_o[v][h][dd], o);
+      }
     }
-  } else {
-    float* prow = a.plan.part_o + ((int64_t)unit * a.hq + head) * D + 4 * r;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      *reinterpret_cast<float4*>(prow + 16 * j) =
-          make_float4(acc[j][0] * inv, acc[j][1] * inv, acc[j][2] * inv, acc[j][3] * inv);
-    if (r == 0) {
-      float* ml = a.plan.part_ml + ((int64_t)unit * a.hq + head) * 2;
-      ml[0] = m_run * c;
-      ml[1] = l_tot;
+    const float inv = sum > 0.f ? 1.f / sum : 0.f;
+    const int32_t qh = g * G + h;
+    if (u.nparts == 1) {
+      store_f32((uint16_t*)a.out + ((int64_t)u.b * a.hq + qh) * D + dd, o * inv);
+    } else {
+      __builtin_nontemporal_store(o * inv, a.plan.part_o + ((int64_t)unit * a.hq + qh) * D + dd);
+      if (dd == 0) {
+        float* ml = a.plan.part_ml + ((int64_t)unit * a.hq + qh) * 2;
+        ml[0] = M * c;
+        ml[1] = sum;
+      }
     }
   }
 }
@@ -527,38 +564,81 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge: out = sum_p w_p o_p / sum_p w_p, w_p = l_p * 2^(m_p - max_p m_p).
-// grid (n_seqs, ceil(Hq / 4)), one wave per query head.
+// Merge: out = sum_p w_p o_p / sum_p w_p with w_p = l_p * 2^(m_p - M), M the
+// largest m_p.  One workgroup of four waves per (sequence, query head); wave w
+// folds partitions w, w + 4, ... with a running maximum (four partitions'
+// loads in flight per step), then the four waves are combined through LDS.
+// The fold order depends only on the partition indices.  grid (n_seqs, Hq).
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int DK>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
-  const int32_t b = blockIdx.x;
+  constexpr int W = 4, U = 4;
+  __shared__ float red_m[W], red_s[W];
+  __shared__ float red_o[W][DK * 64];
+  const int32_t b = blockIdx.x, head = blockIdx.y;
   const int32_t* si = a.plan.seq_info + 3 * b;
   const int32_t f0 = si[0], nf = si[1], rr = si[2];
   const int32_t n = nf + (rr >= 0 ? 1 : 0);
   if (n <= 1) return;
   if (a.plan.counts[0] + a.plan.counts[1] == 0) return;  // plan overflowed
-  const int32_t head = blockIdx.y * 4 + (threadIdx.x >> 6);
-  if (head >= a.hq) return;
-  const int lane = threadIdx.x & 63;
-  auto row = [&](int32_t i) -> int64_t { return i < nf ? f0 + i : rr; };
-  float mx = -INFINITY;
-  for (int32_t i = 0; i < n; ++i) mx = fmaxf(mx, a.plan.part_ml[(row(i) * a.hq + head) * 2]);
-  float wsum = 0.f;
-  for (int32_t i = 0; i < n; ++i) {
-    const float* ml = a.plan.part_ml + (row(i) * a.hq + head) * 2;
-    wsum += ml[1] * fast_exp2(ml[0] - mx);
-  }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  for (int32_t dd = lane; dd < a.d; dd += 64) {
-    float o = 0.f;
-    for (int32_t i = 0; i < n; ++i) {
-      const int64_t rw = row(i);
-      const float* ml = a.plan.part_ml + (rw * a.hq + head) * 2;
-      const float w = ml[1] * fast_exp2(ml[0] - mx);
-      o = fmaf(w, a.plan.part_o[(rw * a.hq + head) * a.d + dd], o);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int32_t D = a.d;
+  float m_run = -INFINITY, s_run = 0.f, acc[DK];
+#pragma unroll
+  for (int k = 0; k < DK; ++k) acc[k] = 0.f;
+  for (int32_t i0 = w; i0 < n; i0 += W * U) {
+    float mp[U], lp[U], op[U][DK];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int32_t i = i0 + W * u;
+      mp[u] = -INFINITY;
+      lp[u] = 0.f;
+#pragma unroll
+      for (int k = 0; k < DK; ++k) op[u][k] = 0.f;
+      if (i < n) {
+        const int64_t row = (i < nf ? f0 + i : rr) * (int64_t)a.hq + head;
+        mp[u] = a.plan.part_ml[row * 2];
+        lp[u] = a.plan.part_ml[row * 2 + 1];
+#pragma unroll
+        for (int k = 0; k < DK; ++k) {
+          const int32_t dd = lane + 64 * k;
+          if (dd < D) op[u][k] = a.plan.part_o[row * D + dd];
+        }
+      }
     }
-    store_f32((T*)a.out + ((int64_t)b * a.hq + head) * a.d + dd, o * inv);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!(lp[u] > 0.f)) continue;  // empty partition or padding
+      const float m_new = fmaxf(m_run, mp[u]);
+      const float al = fast_exp2(m_run - m_new), wt = lp[u] * fast_exp2(mp[u] - m_new);
+      s_run = fmaf(s_run, al, wt);
+#pragma unroll
+      for (int k = 0; k < DK; ++k) acc[k] = fmaf(acc[k], al, wt * op[u][k]);
+      m_run = m_new;
+    }
+  }
+  if (lane == 0) {
+    red_m[w] = m_run;
+    red_s[w] = s_run;
+  }
+#pragma unroll
+  for (int k = 0; k < DK; ++k) red_o[w][lane + 64 * k] = acc[k];
+  __syncthreads();
+  float mx = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < W; ++v) mx = fmaxf(mx, red_m[v]);
+  float sc[W], tot = 0.f;
+#pragma unroll
+  for (int v = 0; v < W; ++v) {
+    sc[v] = red_s[v] > 0.f ? fast_exp2(red_m[v] - mx) : 0.f;
+    tot = fmaf(red_s[v], sc[v], tot);
+  }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  for (int32_t dd = threadIdx.x; dd < D; dd += blockDim.x) {
+    float o = 0.f;
+#pragma unroll
+    for (int v = 0; v < W; ++v) o = fmaf(sc[v], red_o[v][dd], o);
+    store_f32((T*)a.out + ((int64_t)b * a.hq + head) * D + dd, o * inv);
   }
 }
 
@@ -597,6 +677,7 @@ int32_t pow2_floor(int64_t x) {
 
 struct Choice {
   bool mfma;
+  int32_t waves_per_group;  // matrix-core path: waves sharing one unit
   int32_t part_tokens;
   int64_t max_units;
   bool need_partials;
@@ -634,21 +715,28 @@ int choose(int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t p, int32_
     return fail(PKV_ERR_UNSUPPORTED, "decode supports head_dim <= 256 and Hq/Hkv <= 16");
   const int64_t L = std::max<int32_t>(max_len, 1);
   if (total < 0) total = (int64_t)n_seqs * L;
+  // matrix-core path: W waves share a partition of T tokens, T / W >= 32
+  int32_t W = 1;
+  if (mfma) W = env_int("PKV_DECODE_WAVES", 4) == 8 ? 8 : 4;
+  const int32_t tmin = mfma ? 32 * W : 64;
+  const int32_t tmax = mfma ? 512 * W : 512;
   int32_t T;
   const int32_t forced = env_int("PKV_PARTITION_TOKENS", 0);
-  const int32_t tmax = mfma ? std::min(512, 64 * p) : 512;
   if (env_is("PKV_DECODE_SPLIT", "off")) {
-    T = 64;
+    T = tmin;
     while (T < L) T *= 2;
   } else if (forced > 0) {
-    T = std::max(64, pow2_floor(forced));
+    T = std::max(tmin, pow2_floor(forced));
   } else {
-    const int64_t want = total * hkv / ((int64_t)device_cu_count() * 16);
-    T = std::min<int64_t>(tmax, std::max<int64_t>(64, pow2_floor(std::max<int64_t>(want, 1))));
+    // enough (partition, KV head) units for every compute unit to hold a few
+    const int64_t div = std::max(1, env_int("PKV_SPLIT_DIV", 8));
+    const int64_t want = total * hkv / ((int64_t)device_cu_count() * div);
+    T = (int32_t)std::min<int64_t>(tmax, std::max<int64_t>(tmin, pow2_floor(std::max<int64_t>(want, 1))));
   }
   const int64_t by_len = (int64_t)n_seqs * ((L + T - 1) / T);
   const int64_t by_total = total / T + n_seqs;
   out->mfma = mfma;
+  out->waves_per_group = W;
   out->part_tokens = T;
   out->max_units = std::max<int64_t>(1, std::min(by_len, by_total));
   out->need_partials = T < L;
@@ -679,10 +767,11 @@ Layout layout_of(int32_t n_seqs, int32_t hq, int32_t d, const Choice& c) {
 }
 
 template <int D, int P>
-void launch_mfma(const DecodeArgs& a, int64_t waves, hipStream_t st) {
-  constexpr int WPB = 4;
-  const int64_t blocks = (waves + WPB - 1) / WPB;
-  hipLaunchKernelGGL((decode_mfma_kernel<D, P, WPB>), dim3((unsigned)blocks), dim3(64 * WPB), 0, st, a);
+void launch_mfma(const DecodeArgs& a, int32_t waves_per_group, int64_t groups, hipStream_t st) {
+  if (waves_per_group == 8)
+    hipLaunchKernelGGL((decode_mfma_kernel<D, P, 8>), dim3((unsigned)groups), dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<D, P, 4>), dim3((unsigned)groups), dim3(256), 0, st, a);
 }
 
 template <typename T, int GMAX>
@@ -704,6 +793,16 @@ void launch_valu(const DecodeArgs& a, int64_t waves, hipStream_t st) {
   else if (G <= 4) launch_valu_g<T, 4>(a, waves, st);
   else if (G <= 8) launch_valu_g<T, 8>(a, waves, st);
   else launch_valu_g<T, 16>(a, waves, st);
+}
+
+template <typename T>
+void launch_merge(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+  switch ((a.d + 63) / 64) {
+    case 1: hipLaunchKernelGGL((merge_kernel<T, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((merge_kernel<T, 2>), grid, dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((merge_kernel<T, 3>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((merge_kernel<T, 4>), grid, dim3(256), 0, st, a); break;
+  }
 }
 
 }  // namespace
@@ -744,6 +843,7 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
       num_blocks <= 0 || max_blocks_per_seq < 0 || max_context_len < 0)
     return fail(PKV_ERR_INVALID_ARG, "bad sizes");
   if (num_q_heads % num_kv_heads) return fail(PKV_ERR_INVALID_ARG, "num_q_heads % num_kv_heads != 0");
+  if (num_q_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "more than 65535 query heads");
   if (!pkv::dtype_valid(dtype)) return fail(PKV_ERR_INVALID_ARG, "bad dtype");
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(PKV_ERR_INVALID_ARG, "scale must be finite and positive");
@@ -803,14 +903,15 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   hipLaunchKernelGGL(pkv::plan_kernel, dim3(1), dim3(1024), 0, st, a);
   const int64_t waves = c.max_units * num_kv_heads;
   if (c.mfma) {
+    const int32_t W = c.waves_per_group;
     if (head_dim == 128) {
-      if (block_size == 8) pkv::launch_mfma<128, 8>(a, waves, st);
-      else if (block_size == 16) pkv::launch_mfma<128, 16>(a, waves, st);
-      else pkv::launch_mfma<128, 32>(a, waves, st);
+      if (block_size == 8) pkv::launch_mfma<128, 8>(a, W, waves, st);
+      else if (block_size == 16) pkv::launch_mfma<128, 16>(a, W, waves, st);
+      else pkv::launch_mfma<128, 32>(a, W, waves, st);
     } else {
-      if (block_size == 8) pkv::launch_mfma<64, 8>(a, waves, st);
-      else if (block_size == 16) pkv::launch_mfma<64, 16>(a, waves, st);
-      else pkv::launch_mfma<64, 32>(a, waves, st);
+      if (block_size == 8) pkv::launch_mfma<64, 8>(a, W, waves, st);
+      else if (block_size == 16) pkv::launch_mfma<64, 16>(a, W, waves, st);
+      else pkv::launch_mfma<64, 32>(a, W, waves, st);
     }
   } else if (dtype == PKV_BF16) {
     pkv::launch_valu<uint16_t>(a, waves, st);
@@ -818,11 +919,9 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
     pkv::launch_valu<float>(a, waves, st);
   }
   if (c.need_partials) {
-    const dim3 grid((unsigned)n_seqs, (unsigned)((num_q_heads + 3) / 4));
-    if (dtype == PKV_BF16)
-      hipLaunchKernelGGL(pkv::merge_kernel<uint16_t>, grid, dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL(pkv::merge_kernel<float>, grid, dim3(256), 0, st, a);
+    const dim3 grid((unsigned)n_seqs, (unsigned)num_q_heads);
+    if (dtype == PKV_BF16) pkv::launch_merge<uint16_t>(a, grid, st);
+    else pkv::launch_merge<float>(a, grid, st);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
