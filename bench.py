@@ -109,7 +109,15 @@ def main():
     # prefill every generated token; the timed steps then append one token each
     slots, cow = kv.pool.append_slots(seqs, priv)
     assert len(cow) == 0
-    kv.write_slots(torch.from_numpy(slots).to(dev), w.ctx_k, w.ctx_v)
+    d_slots = torch.from_numpy(slots).to(dev)
+    torch.cuda.synchronize()
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record()
+    kv.write_slots(d_slots, w.ctx_k, w.ctx_v)
+    p1.record()
+    torch.cuda.synchronize()
+    prefill_ms = p0.elapsed_time(p1)
+    prefill_bytes = 2 * 2 * int(priv.sum()) * hkv * d * s + 4 * int(priv.sum())
     max_len = int(w.lengths.max()) + nsteps
     total = int(w.lengths.sum()) + b * nsteps
     meta = kv.prepare(seqs, -(-max_len // p), hq, max_len, total)
@@ -127,38 +135,51 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
     frag = []
 
-    def step(i, events=None):
+    def step(i):
         kv.append_decode_tokens(meta, w.step_k[i], w.step_v[i], stream)
-        if events:
-            events[0].record(stream)
         kv.attend(meta, w.q, out, stream=stream)
-        if events:
-            events[1].record(stream)
         frag.append(kv.pool.stats()["fragmentation"])
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
+    # timed region 1: whole steps (host allocation + uploads + kernels), no
+    # events inside the loop so nothing is added between the step's launches
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
+    s0.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, ev[i])
+        step(args.warmup + i)
+    s1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    dec_ms = float(np.mean([a.elapsed_time(e) for a, e in ev]))
-    log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step, decode {dec_ms:.3f} ms")
+    gpu_ms_step = s0.elapsed_time(s1) / args.steps
+    # timed region 2: the decode operation alone, `steps` back-to-back calls on
+    # the final state, HIP events on the stream its kernels run on
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    d0.record(stream)
+    for _ in range(args.steps):
+        kv.attend(meta, w.q, out, stream=stream)
+    d1.record(stream)
+    torch.cuda.synchronize()
+    dec_ms = d0.elapsed_time(d1) / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step wall, {gpu_ms_step:.3f} ms/step "
+        f"on the stream, decode alone {dec_ms:.3f} ms")
 
-    # algorithmic bytes, averaged over the timed steps (contexts grow by one per step)
+    # algorithmic bytes: steps averaged over their growing contexts; the
+    # decode-alone loop runs at the final lengths
     base = w.lengths.astype(np.int64)
-    dbytes = np.mean([decode_bytes(base + args.warmup + i + 1, hq, hkv, d, p, s)
+    sbytes = np.mean([decode_bytes(base + args.warmup + i + 1, hq, hkv, d, p, s)
                       for i in range(args.steps)])
+    dbytes = decode_bytes(base + args.warmup + args.steps, hq, hkv, d, p, s)
     abytes = append_bytes(b, hkv, d, s)
-    step_gbs = (dbytes + abytes) / (ms_step * 1e-3) / 1e9
+    step_gbs = (sbytes + abytes) / (ms_step * 1e-3) / 1e9
     dec_gbs = dbytes / (dec_ms * 1e-3) / 1e9
 
     result = {
@@ -184,8 +205,11 @@ def main():
         "decode_tokens_per_s": round(b / (ms_step * 1e-3), 1),
         "pct_of_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
         "decode_ms": round(dec_ms, 4),
+        "gpu_ms_per_step": round(gpu_ms_step, 4),
         "decode_bytes_per_step": int(dbytes),
         "fragmentation": round(float(np.mean(frag)), 6),
+        "cache_append_prefill": {"tokens": int(priv.sum()), "ms": round(prefill_ms, 3),
+                                 "GB_per_s": round(prefill_bytes / (prefill_ms * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(cfg.name, os.path.dirname(os.path.abspath(__file__))),

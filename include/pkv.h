@@ -154,25 +154,38 @@ int pkv_pool_stats(pkv_pool* pool, pkv_stats* out);
 int pkv_pool_export(pkv_pool* pool, int32_t* free_order_out, int32_t* refcount_out,
                     int32_t* n_free_out);
 
-/* Build the padded block table of `seqs` (row i = seqs[i], entries beyond the
- * sequence's blocks = -1) and its context lengths in pool-owned pinned
- * staging memory, then enqueue the host-to-device copies on `stream`:
- *   d_block_table   device int32[n_seqs * max_blocks_per_seq]
+/* Bring a device block table, its context lengths and (optionally) a slot
+ * mapping up to date with the pool ("The Block Table Map": the table records
+ * each new block as the sequence grows):
+ *   d_block_table   device int32[n_seqs * max_blocks_per_seq]; row i belongs
+ *                   to seqs[i], entries beyond the sequence's blocks are -1
  *   d_context_lens  device int32[n_seqs]
  *   slot_mapping / d_slot_mapping / n_slots: optional (host int32[n_slots] ->
  *                   device int32[n_slots]) copy of a slot mapping in the same
- *                   staging round; pass NULL/NULL/0 to skip.
+ *                   round; pass NULL/NULL/0 to skip.
  *   max_context_len_out, total_tokens_out: host outputs, may be NULL.
- * Staging buffers are double-buffered and reused only after the copy that
- * last read them has completed, so the host may return before the copy runs.
+ *   flags  0: full upload.  The padded table is assembled on the host and
+ *             copied through pool-owned pinned staging (double-buffered,
+ *             reused only after the copy that last read it has completed).
+ *          PKV_UPLOAD_INCREMENTAL: the caller asserts that d_block_table
+ *             still holds what this pool last uploaded to that address (with
+ *             the same max_blocks_per_seq).  Rows that hold the same sequence
+ *             as then, with no copy-on-write since, receive only their new
+ *             entries; other rows are rewritten.  Lengths, slots and entries
+ *             travel in the arguments of small patch kernels: no staging and
+ *             no host-to-device copy.  Falls back to a full upload when the
+ *             patch would be large (or nothing was uploaded there before).
+ * The pool records, per device table address and row, what it wrote.  All
+ * device work is enqueued on `stream`; the host may return before it runs.
  * Errors: BAD_SEQ, CAPACITY (a sequence has more than max_blocks_per_seq
- * blocks), INVALID_ARG, HIP. */
+ * blocks), INVALID_ARG (including unknown flags), HIP. */
+#define PKV_UPLOAD_INCREMENTAL 1
 int pkv_block_table_upload(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs,
                            int32_t max_blocks_per_seq, int32_t* d_block_table,
                            int32_t* d_context_lens, const int32_t* slot_mapping,
                            int32_t* d_slot_mapping, int32_t n_slots,
                            int32_t* max_context_len_out, int64_t* total_tokens_out,
-                           void* stream);
+                           int32_t flags, void* stream);
 
 /* ---- device kernels ---------------------------------------------------- */
 

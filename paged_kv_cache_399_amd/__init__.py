@@ -171,8 +171,12 @@ class BlockPool:
 
     def block_table_upload(self, seqs: Sequence[int], max_blocks: int, d_block_table,
                            d_context_lens, slot_mapping=None, d_slot_mapping=None,
-                           stream=None) -> Tuple[int, int]:
-        """Upload the padded block table and lengths; returns (max length, total tokens)."""
+                           stream=None, incremental: bool = False) -> Tuple[int, int]:
+        """Upload the padded block table and lengths; returns (max length, total tokens).
+
+        ``incremental=True`` sends only what changed since this pool's last upload
+        to the same device table (see PKV_UPLOAD_INCREMENTAL in pkv.h).
+        """
         import torch
         s = _i64_array(seqs)
         if d_block_table.dtype != torch.int32 or d_context_lens.dtype != torch.int32:
@@ -193,7 +197,8 @@ class BlockPool:
             self._h, _p64(s), len(s), int(max_blocks), _dev(d_block_table, "block table"),
             _dev(d_context_lens, "context lengths"), None if hs is None else _p32(hs),
             None if hs is None else _dev(d_slot_mapping, "slot mapping"), n_slots,
-            C.byref(mx), C.byref(tot), _stream_ptr(stream)))
+            C.byref(mx), C.byref(tot), _lib.UPLOAD_INCREMENTAL if incremental else 0,
+            _stream_ptr(stream)))
         return mx.value, tot.value
 
 

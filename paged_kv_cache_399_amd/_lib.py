@@ -26,6 +26,8 @@ DEVERR_WORK_OVERFLOW = 16
 F32 = 0
 BF16 = 1
 
+UPLOAD_INCREMENTAL = 1
+
 
 class Stats(C.Structure):
     _fields_ = [("num_blocks", C.c_int64), ("free_blocks", C.c_int64),
@@ -49,7 +51,7 @@ SIGNATURES = {
     "pkv_pool_stats": (C.c_int, [_vp, C.POINTER(Stats)]),
     "pkv_pool_export": (C.c_int, [_vp, _pi32, _pi32, _pi32]),
     "pkv_block_table_upload": (C.c_int, [_vp, _pi64, _i32, _i32, _vp, _vp, _pi32, _vp, _i32,
-                                         _pi32, _pi64, _vp]),
+                                         _pi32, _pi64, _i32, _vp]),
     "pkv_copy_blocks": (C.c_int, [_vp, _vp, _pi32, _i32, _i32, _i32, _i32, _i32, C.c_int, _vp]),
     "pkv_cache_append": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                    C.c_int, _vp]),

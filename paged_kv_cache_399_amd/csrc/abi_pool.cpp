@@ -3,10 +3,12 @@
 
 #include <algorithm>
 #include <climits>
+#include <cstddef>
 #include <cstdio>
 #include <cstring>
 #include <new>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "block_pool.hpp"
@@ -38,9 +40,21 @@ struct pkv_pool {
     hipEvent_t done = nullptr;  // recorded after the copies that read `host`
     bool pending = false;
   };
+  // What the last upload wrote into one row of a device table.
+  struct RowRecord {
+    int64_t seq = -1;
+    int32_t blocks = 0;   // entries [0, blocks) hold the sequence's table
+    uint32_t epoch = 0;   // the sequence's copy-on-write epoch at that time
+  };
+  struct TableRecord {
+    int32_t max_blocks = 0;
+    std::vector<RowRecord> rows;
+  };
   pkv::BlockPool pool;
   Stage stage[2];
   int next = 0;
+  std::unordered_map<const void*, TableRecord> tables;  // keyed by device table address
+  std::vector<int32_t> build;  // cacheable host buffer for full tables
 
   pkv_pool(int32_t nb, int32_t p, const int32_t* order) : pool(nb, p, order) {}
   ~pkv_pool() {
@@ -173,16 +187,80 @@ int pkv_pool_export(pkv_pool* pool, int32_t* free_order_out, int32_t* refcount_o
   PKV_TRY_END
 }
 
+namespace {
+
+// Full upload: the padded table, the lengths and the slot mapping through one
+// pinned staging round (double-buffered, reused after its copies finished).
+int upload_full(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs, int32_t max_blocks,
+                int32_t* d_table, int32_t* d_lens, const int32_t* slot_mapping, int32_t* d_slots,
+                int32_t n_slots, hipStream_t st) {
+  const pkv::BlockPool& bp = pool->pool;
+  const size_t table_words = (size_t)n_seqs * max_blocks;
+  const size_t need = (table_words + n_seqs + n_slots) * sizeof(int32_t);
+  if (need == 0) return PKV_OK;
+  pkv_pool::Stage& sg = pool->stage[pool->next];
+  if (sg.pending) {
+    if (hipEventSynchronize(sg.done) != hipSuccess)
+      return fail(PKV_ERR_HIP, "waiting for a previous upload failed");
+    sg.pending = false;
+  }
+  if (sg.bytes < need) {
+    if (sg.host) (void)hipHostFree(sg.host);
+    sg.host = nullptr;
+    sg.bytes = 0;
+    const size_t cap = std::max<size_t>(need, 4096);
+    if (hipHostMalloc(&sg.host, cap, hipHostMallocDefault) != hipSuccess)
+      return fail(PKV_ERR_HIP, "pinned staging allocation of %zu bytes failed", cap);
+    sg.bytes = cap;
+  }
+  if (!sg.done && hipEventCreateWithFlags(&sg.done, hipEventDisableTiming) != hipSuccess)
+    return fail(PKV_ERR_HIP, "event creation failed");
+  // rows are assembled in ordinary cached memory, then moved to pinned memory
+  // in one bulk copy (word-by-word writes to pinned memory are slow)
+  std::vector<int32_t>& b = pool->build;
+  b.resize(table_words + n_seqs);
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const std::vector<int32_t>& t = bp.table(seqs[i]);
+    int32_t* row = b.data() + (size_t)i * max_blocks;
+    std::copy(t.begin(), t.end(), row);
+    std::fill(row + t.size(), row + max_blocks, -1);
+    b[table_words + i] = (int32_t)bp.length(seqs[i]);
+  }
+  int32_t* tab = (int32_t*)sg.host;
+  int32_t* lens = tab + table_words;
+  int32_t* slots = lens + n_seqs;
+  std::memcpy(tab, b.data(), (table_words + n_seqs) * sizeof(int32_t));
+  if (n_slots) std::memcpy(slots, slot_mapping, (size_t)n_slots * sizeof(int32_t));
+  hipError_t e = hipSuccess;
+  if (table_words) e = hipMemcpyAsync(d_table, tab, table_words * 4, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess && n_seqs)
+    e = hipMemcpyAsync(d_lens, lens, (size_t)n_seqs * 4, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess && n_slots)
+    e = hipMemcpyAsync(d_slots, slots, (size_t)n_slots * 4, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipEventRecord(sg.done, st);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "upload failed: %s", hipGetErrorString(e));
+  sg.pending = true;
+  pool->next ^= 1;
+  return PKV_OK;
+}
+
+// Largest incremental patch sent as kernel-argument patches; anything bigger
+// goes through the full upload.
+constexpr size_t kMaxPatchLaunches = 16;
+
+}  // namespace
+
 int pkv_block_table_upload(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs,
                            int32_t max_blocks_per_seq, int32_t* d_block_table,
                            int32_t* d_context_lens, const int32_t* slot_mapping,
                            int32_t* d_slot_mapping, int32_t n_slots,
                            int32_t* max_context_len_out, int64_t* total_tokens_out,
-                           void* stream) {
+                           int32_t flags, void* stream) {
   PKV_TRY_BEGIN
   if (!pool) return fail(PKV_ERR_INVALID_ARG, "NULL pool");
   if (n_seqs < 0 || max_blocks_per_seq < 0 || n_slots < 0)
     return fail(PKV_ERR_INVALID_ARG, "negative size");
+  if (flags & ~PKV_UPLOAD_INCREMENTAL) return fail(PKV_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   if (n_seqs > 0 && (!seqs || !d_context_lens || (max_blocks_per_seq > 0 && !d_block_table)))
     return fail(PKV_ERR_INVALID_ARG, "NULL table / length pointer");
   if (n_slots > 0 && (!slot_mapping || !d_slot_mapping))
@@ -200,52 +278,89 @@ int pkv_block_table_upload(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs,
     total += L;
     longest = std::max<int32_t>(longest, (int32_t)L);
   }
-  const size_t table_bytes = (size_t)n_seqs * max_blocks_per_seq * sizeof(int32_t);
-  const size_t lens_bytes = (size_t)n_seqs * sizeof(int32_t);
-  const size_t slot_bytes = (size_t)n_slots * sizeof(int32_t);
-  const size_t need = table_bytes + lens_bytes + slot_bytes;
   hipStream_t st = (hipStream_t)stream;
 
-  if (need > 0) {
-    pkv_pool::Stage& sg = pool->stage[pool->next];
-    if (sg.pending) {
-      if (hipEventSynchronize(sg.done) != hipSuccess)
-        return fail(PKV_ERR_HIP, "waiting for a previous upload failed");
-      sg.pending = false;
-    }
-    if (sg.bytes < need) {
-      if (sg.host) (void)hipHostFree(sg.host);
-      sg.host = nullptr;
-      sg.bytes = 0;
-      size_t cap = std::max<size_t>(need, 4096);
-      if (hipHostMalloc(&sg.host, cap, hipHostMallocDefault) != hipSuccess)
-        return fail(PKV_ERR_HIP, "pinned staging allocation of %zu bytes failed", cap);
-      sg.bytes = cap;
-    }
-    if (!sg.done && hipEventCreateWithFlags(&sg.done, hipEventDisableTiming) != hipSuccess)
-      return fail(PKV_ERR_HIP, "event creation failed");
-    char* base = (char*)sg.host;
-    int32_t* tab = (int32_t*)base;
-    int32_t* lens = (int32_t*)(base + table_bytes);
-    int32_t* slots = (int32_t*)(base + table_bytes + lens_bytes);
-    for (int32_t i = 0; i < n_seqs; ++i) {
+  // Incremental: rows whose record names the same sequence at the same
+  // copy-on-write epoch get only their new entries; other rows are rewritten
+  // (entries plus -1 padding).  Lengths and slots are always sent.
+  bool full = !(flags & PKV_UPLOAD_INCREMENTAL) || n_seqs == 0;
+  std::vector<int32_t> ent, rst;
+  auto rec_it = pool->tables.find(d_block_table);
+  if (!full && (rec_it == pool->tables.end() || rec_it->second.max_blocks != max_blocks_per_seq))
+    full = true;
+  if (!full) {
+    const std::vector<pkv_pool::RowRecord>& rows = rec_it->second.rows;
+    const size_t budget = kMaxPatchLaunches * pkv::kPatchWords;
+    size_t words = (size_t)n_seqs + n_slots;
+    for (int32_t i = 0; i < n_seqs && !full; ++i) {
       const std::vector<int32_t>& t = bp.table(seqs[i]);
-      int32_t* row = tab + (size_t)i * max_blocks_per_seq;
-      std::copy(t.begin(), t.end(), row);
-      std::fill(row + t.size(), row + max_blocks_per_seq, -1);
-      lens[i] = (int32_t)bp.length(seqs[i]);
+      const int32_t n = (int32_t)t.size();
+      int32_t from = 0;
+      if (i < (int32_t)rows.size() && rows[i].seq == seqs[i] && rows[i].epoch == bp.epoch(seqs[i]) &&
+          rows[i].blocks <= n) {
+        from = rows[i].blocks;
+      } else {
+        rst.push_back(i);
+        rst.push_back(n);
+        words += 2;
+      }
+      for (int32_t j = from; j < n; ++j) {
+        ent.push_back(i);
+        ent.push_back(j);
+        ent.push_back(t[j]);
+      }
+      words += 3 * (size_t)(n - from);
+      if (words > budget) full = true;
     }
-    if (n_slots) std::memcpy(slots, slot_mapping, slot_bytes);
-    hipError_t e = hipSuccess;
-    if (table_bytes) e = hipMemcpyAsync(d_block_table, tab, table_bytes, hipMemcpyHostToDevice, st);
-    if (e == hipSuccess && lens_bytes)
-      e = hipMemcpyAsync(d_context_lens, lens, lens_bytes, hipMemcpyHostToDevice, st);
-    if (e == hipSuccess && slot_bytes)
-      e = hipMemcpyAsync(d_slot_mapping, slots, slot_bytes, hipMemcpyHostToDevice, st);
-    if (e == hipSuccess) e = hipEventRecord(sg.done, st);
-    if (e != hipSuccess) return fail(PKV_ERR_HIP, "upload failed: %s", hipGetErrorString(e));
-    sg.pending = true;
-    pool->next ^= 1;
+  }
+  if (full) {
+    int rc = upload_full(pool, seqs, n_seqs, max_blocks_per_seq, d_block_table, d_context_lens,
+                         slot_mapping, d_slot_mapping, n_slots, st);
+    if (rc) return rc;
+  } else {
+    // pack lengths, slots, entries and resets into kernel-argument patches
+    pkv::TablePatchArgs a;
+    const int32_t n_ent = (int32_t)(ent.size() / 3), n_rst = (int32_t)(rst.size() / 2);
+    int32_t li = 0, si = 0, ei = 0, ri = 0;
+    while (li < n_seqs || si < n_slots || ei < n_ent || ri < n_rst) {
+      std::memset(&a, 0, offsetof(pkv::TablePatchArgs, w));
+      a.table = d_block_table;
+      a.lens = d_context_lens;
+      a.slots = d_slot_mapping;
+      a.max_blocks = max_blocks_per_seq;
+      int32_t room = pkv::kPatchWords;
+      a.len0 = li;
+      a.n_len = std::min(room, n_seqs - li);
+      for (int32_t k = 0; k < a.n_len; ++k) a.w[k] = (int32_t)bp.length(seqs[li + k]);
+      li += a.n_len;
+      room -= a.n_len;
+      a.slot0 = si;
+      a.n_slot = std::min(room, n_slots - si);
+      if (a.n_slot) std::memcpy(a.w + a.n_len, slot_mapping + si, (size_t)a.n_slot * 4);
+      si += a.n_slot;
+      room -= a.n_slot;
+      int32_t* e = a.w + a.n_len + a.n_slot;
+      a.n_ent = std::min(room / 3, n_ent - ei);
+      if (a.n_ent) std::memcpy(e, ent.data() + 3 * (size_t)ei, (size_t)a.n_ent * 12);
+      ei += a.n_ent;
+      room -= 3 * a.n_ent;
+      a.n_reset = std::min(room / 2, n_rst - ri);
+      if (a.n_reset) std::memcpy(e + 3 * a.n_ent, rst.data() + 2 * (size_t)ri, (size_t)a.n_reset * 8);
+      ri += a.n_reset;
+      int rc = pkv::launch_table_patch(a, stream);
+      if (rc) return rc;
+    }
+  }
+  // remember what every row of this device table now holds
+  if (n_seqs > 0 && max_blocks_per_seq > 0) {
+    pkv_pool::TableRecord& tr = pool->tables[d_block_table];
+    tr.max_blocks = max_blocks_per_seq;
+    tr.rows.resize(n_seqs);
+    for (int32_t i = 0; i < n_seqs; ++i) {
+      tr.rows[i].seq = seqs[i];
+      tr.rows[i].blocks = (int32_t)bp.table(seqs[i]).size();
+      tr.rows[i].epoch = bp.epoch(seqs[i]);
+    }
   }
   if (max_context_len_out) *max_context_len_out = longest;
   if (total_tokens_out) *total_tokens_out = total;

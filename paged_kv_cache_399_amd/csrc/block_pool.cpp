@@ -117,6 +117,7 @@ int BlockPool::append(const int64_t* seqs, const int32_t* n_new, int32_t n_seqs,
         cow[2 * c + 1] = dst;
         ++c;
         s.table.back() = dst;
+        ++s.epoch;
       }
       const int32_t blk = s.table[L / P];
       slots[k++] = blk * (int32_t)P + off;

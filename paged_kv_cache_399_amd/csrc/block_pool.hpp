@@ -37,6 +37,8 @@ class BlockPool {
   }
   const std::vector<int32_t>& table(int64_t seq) const { return seqs_[seq].table; }
   int64_t length(int64_t seq) const { return seqs_[seq].length; }
+  // bumped whenever an existing table entry is replaced (copy-on-write)
+  uint32_t epoch(int64_t seq) const { return seqs_[seq].epoch; }
 
   int64_t free_count() const { return free_count_; }
   int64_t live_tokens() const { return live_tokens_; }
@@ -47,6 +49,7 @@ class BlockPool {
   struct Seq {
     bool live = false;
     int64_t length = 0;
+    uint32_t epoch = 0;
     std::vector<int32_t> table;
   };
 

@@ -11,6 +11,8 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 
 #include "device_common.hpp"
 #include "internal.hpp"
@@ -58,6 +60,105 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
   }
 }
 
+// Bulk appends (a prefill writes whole blocks).  Workgroup w takes the token
+// rows [w kWin, w kWin + kWin) and finds the runs of P rows whose slots fill
+// one whole block in order (a run starts at a row whose slot is a multiple of
+// P).  A run's key tile is a straight copy and its value tile is transposed
+// through LDS and written as full rows of P tokens, so HBM sees whole-sector
+// writes instead of one 2- or 4-byte write per value element.  Rows outside
+// runs (partial blocks, runs cut by the window edge, skipped or bad slots) are
+// copied element by element.  Runs write disjoint blocks, so the order in
+// which a workgroup takes them does not matter.
+constexpr int kTileLdsBytes = 32768;
+constexpr int kWin = 256;
+
+template <typename E>
+__global__ __launch_bounds__(256) void cache_append_tiles_kernel(
+    E* __restrict__ kc, E* __restrict__ vc, const E* __restrict__ kn, const E* __restrict__ vn,
+    const int32_t* __restrict__ slots, int32_t n_tokens, int64_t num_slots, int32_t hkv,
+    int32_t d, int32_t p, int32_t* __restrict__ err) {
+  __shared__ uint4 lds_raw[kTileLdsBytes / 16];
+  __shared__ int32_t ws[kWin], run_start[kWin], loose[kWin];
+  __shared__ int32_t covered[kWin];
+  __shared__ int32_t n_runs, n_loose;
+  E* tile = reinterpret_cast<E*>(lds_raw);
+  constexpr int V = 16 / sizeof(E);  // elements per 16-byte chunk
+  const int32_t hd = hkv * d;
+  const int32_t tid = threadIdx.x, nth = blockDim.x;
+  const int32_t n_win = (n_tokens + kWin - 1) / kWin;
+  for (int32_t wdx = blockIdx.x; wdx < n_win; wdx += gridDim.x) {
+    const int32_t i0 = wdx * kWin, cnt = min(kWin, n_tokens - i0);
+    for (int32_t t = tid; t < kWin; t += nth) {
+      ws[t] = t < cnt ? slots[i0 + t] : -1;
+      covered[t] = 0;
+    }
+    if (tid == 0) {
+      n_runs = 0;
+      n_loose = 0;
+    }
+    __syncthreads();
+    for (int32_t t = tid; t < cnt; t += nth) {
+      const int32_t s0 = ws[t];
+      bool ok = s0 >= 0 && s0 % p == 0 && t + p <= cnt && (int64_t)s0 + p <= num_slots;
+      for (int32_t j = 1; ok && j < p; ++j) ok = ws[t + j] == s0 + j;
+      if (ok) run_start[atomicAdd(&n_runs, 1)] = t;
+    }
+    __syncthreads();
+    for (int32_t c = tid; c < n_runs * p; c += nth) covered[run_start[c / p] + c % p] = 1;
+    __syncthreads();
+    for (int32_t t = tid; t < cnt; t += nth)
+      if (!covered[t]) loose[atomicAdd(&n_loose, 1)] = t;
+    __syncthreads();
+    // rows outside runs, element by element
+    for (int32_t e = tid; e < n_loose * hd; e += nth) {
+      const int32_t q = e / hd, r = e - q * hd;
+      const int32_t row = loose[q], sl = ws[row];
+      if (sl < 0) continue;
+      if ((int64_t)sl >= num_slots) {
+        if (r == 0) atomicOr(err, PKV_DEVERR_SLOT);
+        continue;
+      }
+      const int64_t blk = sl / p, off = sl % p;
+      const int32_t h = r / d, dd = r - h * d;
+      kc[((blk * hkv + h) * p + off) * d + dd] = kn[(int64_t)(i0 + row) * hd + r];
+      vc[((blk * hkv + h) * d + dd) * p + off] = vn[(int64_t)(i0 + row) * hd + r];
+    }
+    // whole-block runs
+    const int32_t dv = d / V, pv = p / V;
+    const int32_t per = p * dv;                             // 16-byte chunks per head tile
+    const int32_t hb = max(1, (kTileLdsBytes / 16) / per);  // heads per LDS pass
+    const int32_t nr = n_runs;
+    for (int32_t ri = 0; ri < nr; ++ri) {
+      const int32_t t0 = run_start[ri];
+      const int64_t blk = ws[t0] / p;
+      const int64_t row0 = i0 + t0;
+      for (int32_t h0 = 0; h0 < hkv; h0 += hb) {
+        const int32_t nh = min(hb, hkv - h0);
+        for (int32_t c = tid; c < nh * per; c += nth) {
+          const int32_t hh = c / per, r = c - hh * per, j = r / dv, x = r - j * dv;
+          const int64_t src = (row0 + j) * hd + (h0 + hh) * d;
+          reinterpret_cast<uint4*>(kc + (blk * hkv + h0 + hh) * p * d)[r] =
+              reinterpret_cast<const uint4*>(kn + src)[x];
+          lds_raw[c] = reinterpret_cast<const uint4*>(vn + src)[x];
+        }
+        __syncthreads();
+        const int32_t outc = d * pv;                        // 16-byte chunks per transposed tile
+        for (int32_t c = tid; c < nh * outc; c += nth) {
+          const int32_t hh = c / outc, r = c - hh * outc, dd = r / pv, j0 = (r - dd * pv) * V;
+          const E* srct = tile + (int64_t)hh * p * d;
+          E chunk[V];
+#pragma unroll
+          for (int k = 0; k < V; ++k) chunk[k] = srct[(j0 + k) * d + dd];
+          reinterpret_cast<uint4*>(vc + (blk * hkv + h0 + hh) * d * p)[r] =
+              *reinterpret_cast<const uint4*>(chunk);
+        }
+        __syncthreads();
+      }
+    }
+    __syncthreads();  // the next window reuses the shared lists
+  }
+}
+
 constexpr int kMaxPairsPerLaunch = 128;
 
 struct CopyPairs {
@@ -88,7 +189,32 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(W* __restrict__ kc, W*
   }
 }
 
+// Apply one block-table patch (incremental table upload).  The host has
+// checked every row, column and count against the table's shape.
+__global__ __launch_bounds__(256) void table_patch_kernel(TablePatchArgs p) {
+  const int32_t tid = threadIdx.x, nth = blockDim.x;
+  const int32_t* w = p.w;
+  for (int32_t i = tid; i < p.n_len; i += nth) p.lens[p.len0 + i] = w[i];
+  for (int32_t i = tid; i < p.n_slot; i += nth) p.slots[p.slot0 + i] = w[p.n_len + i];
+  const int32_t* e = w + p.n_len + p.n_slot;
+  for (int32_t i = tid; i < p.n_ent; i += nth)
+    p.table[(int64_t)e[3 * i] * p.max_blocks + e[3 * i + 1]] = e[3 * i + 2];
+  const int32_t* r = e + 3 * p.n_ent;
+  for (int32_t k = 0; k < p.n_reset; ++k) {
+    int32_t* row = p.table + (int64_t)r[2 * k] * p.max_blocks;
+    for (int32_t c = r[2 * k + 1] + tid; c < p.max_blocks; c += nth) row[c] = -1;
+  }
+}
+
 }  // namespace
+
+int launch_table_patch(const TablePatchArgs& args, void* stream) {
+  hipLaunchKernelGGL(table_patch_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, args);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "table patch launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
 }  // namespace pkv
 
 using pkv::fail;
@@ -111,8 +237,33 @@ extern "C" int pkv_cache_append(void* k_cache, void* v_cache, const void* k_new,
   const size_t es = pkv::dtype_size(dtype);
   const int32_t vec_ok = ((size_t)head_dim * es % 16 == 0) &&
                          ((uintptr_t)k_cache % 16 == 0) && ((uintptr_t)k_new % 16 == 0);
-  const int grid = (int)std::min<int32_t>(n_tokens, 1 << 16);
   hipStream_t st = (hipStream_t)stream;
+  // whole-block tile path for bulk appends (every row and tile 16-byte aligned)
+  const size_t tile_bytes = (size_t)block_size * head_dim * es;
+  const bool tiles_fit = vec_ok && ((size_t)block_size * es) % 16 == 0 &&
+                         tile_bytes <= (size_t)pkv::kTileLdsBytes && (uintptr_t)v_cache % 16 == 0 &&
+                         (uintptr_t)v_new % 16 == 0;
+  const char* mode = std::getenv("PKV_APPEND_TILES");
+  bool tiles = tiles_fit && n_tokens >= 4096;
+  if (mode && std::strcmp(mode, "on") == 0) tiles = tiles_fit;
+  if (mode && std::strcmp(mode, "off") == 0) tiles = false;
+  if (tiles) {
+    const int groups = (int)std::min<int64_t>((n_tokens + pkv::kWin - 1) / pkv::kWin, 1 << 16);
+    if (dtype == PKV_BF16)
+      hipLaunchKernelGGL(pkv::cache_append_tiles_kernel<uint16_t>, dim3(groups), dim3(256), 0, st,
+                         (uint16_t*)k_cache, (uint16_t*)v_cache, (const uint16_t*)k_new,
+                         (const uint16_t*)v_new, d_slot_mapping, n_tokens, num_slots, num_kv_heads,
+                         head_dim, block_size, err);
+    else
+      hipLaunchKernelGGL(pkv::cache_append_tiles_kernel<uint32_t>, dim3(groups), dim3(256), 0, st,
+                         (uint32_t*)k_cache, (uint32_t*)v_cache, (const uint32_t*)k_new,
+                         (const uint32_t*)v_new, d_slot_mapping, n_tokens, num_slots, num_kv_heads,
+                         head_dim, block_size, err);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "cache_append launch: %s", hipGetErrorString(e));
+    return PKV_OK;
+  }
+  const int grid = (int)std::min<int32_t>(n_tokens, 1 << 16);
   if (dtype == PKV_BF16)
     hipLaunchKernelGGL(pkv::cache_append_kernel<uint16_t>, dim3(grid), dim3(256), 0, st,
                        (uint16_t*)k_cache, (uint16_t*)v_cache, (const uint16_t*)k_new,

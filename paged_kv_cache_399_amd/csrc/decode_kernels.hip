@@ -53,9 +53,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct Plan {
-  int32_t* counts;     // [0] full units F, [1] ragged units R
+  int32_t* counts;     // [0] units to run (0 if the plan overflowed), [1] full units
   int32_t* seq_info;   // [3 * n_seqs]: first full row, number of full rows, ragged row or -1
-  int2* work;          // [max_units]: (sequence, partition index)
+  int4* work;          // [max_units]: (sequence, first token, end token, partitions of the sequence)
   float* part_ml;      // [max_units * Hq * 2]: running max (log2 units), sum
   float* part_o;       // [max_units * Hq * D]: normalised partial output
 };
@@ -119,33 +119,35 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Unit bookkeeping common to both partition kernels.
+// Unit bookkeeping common to both partition kernels: one 16-byte record.
 struct Unit {
-  int32_t b, part, t0, t1, nparts, valid;
+  int32_t b, t0, t1, nparts, valid;
 };
 
 __device__ __forceinline__ Unit decode_unit(const DecodeArgs& a, int32_t unit) {
   Unit u;
-  const int32_t F = a.plan.counts[0], R = a.plan.counts[1];
-  u.valid = unit < F || (unit >= a.max_units - R && unit < a.max_units);
+  u.valid = unit < a.plan.counts[0];
   if (!u.valid) return u;
-  const int2 w = a.plan.work[unit];
+  const int4 w = a.plan.work[unit];
   u.b = w.x;
-  u.part = w.y;
-  int64_t L = a.ctx[u.b];
-  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
-  u.t0 = u.part * a.part_tokens;
-  u.t1 = (int32_t)(L < (int64_t)u.t0 + a.part_tokens ? L : (int64_t)u.t0 + a.part_tokens);
-  const int32_t* si = a.plan.seq_info + 3 * u.b;
-  u.nparts = si[1] + (si[2] >= 0 ? 1 : 0);
+  u.t0 = w.y;
+  u.t1 = w.z;
+  u.nparts = w.w;
   return u;
 }
 
 // ---------------------------------------------------------------------------
 // Plan: per sequence, floor(L/T) full partitions and (L % T != 0 or L == 0)
-// one ragged partition.  Full units fill rows [0, F) in sequence order,
-// ragged units fill rows [max_units - R, max_units).  One workgroup.
+// one ragged partition.  Full units take rows [0, F) in sequence order, then
+// the ragged units follow longest first (bucketed by length), so the hardware
+// dispatcher, which starts workgroups in grid order as slots free up, runs a
+// longest-processing-time-first schedule and the launch ends on short units.
+// Row placement never changes results: partials are merged by partition
+// index.  One workgroup of kPlanThreads threads.
 // ---------------------------------------------------------------------------
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBuckets = 1024;  // one bucket per plan thread
+
 __device__ int32_t block_exclusive_scan(int32_t v, int32_t* smem, int32_t* total) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int nw = blockDim.x >> 6;
@@ -168,48 +170,76 @@ __device__ int32_t block_exclusive_scan(int32_t v, int32_t* smem, int32_t* total
   return before + x - v;
 }
 
-__global__ __launch_bounds__(1024) void plan_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
   __shared__ int32_t smem[16];
+  __shared__ int32_t bucket[kPlanBuckets];  // counts, then the next free row of each bucket
   const int32_t T = a.part_tokens;
   const int64_t cap = a.len_cap;
-  int32_t full_base = 0, ragged_base = 0;
-  for (int32_t base = 0; base < a.n_seqs; base += blockDim.x) {
-    const int32_t b = base + threadIdx.x;
+  const int tid = threadIdx.x;
+  bucket[tid] = 0;
+  __syncthreads();
+  auto length_of = [&](int32_t b, bool flag) -> int64_t {
+    int64_t L = a.ctx[b];
+    if (L < 0 || L > cap) {
+      if (flag) atomicOr(a.err, PKV_DEVERR_CONTEXT_LEN);
+      L = L < 0 ? 0 : cap;
+    }
+    return L;
+  };
+  // bucket 0 holds the longest ragged partitions (T - 1 tokens)
+  auto bucket_of = [&](int64_t L) -> int32_t {
+    return (int32_t)(((int64_t)(T - 1 - (int32_t)(L % T)) * kPlanBuckets) / T);
+  };
+
+  // pass 1: full rows in sequence order; ragged partitions counted per bucket
+  int32_t full_base = 0;
+  for (int32_t base = 0; base < a.n_seqs; base += kPlanThreads) {
+    const int32_t b = base + tid;
+    int64_t L = 0;
     int32_t nfull = 0, rag = 0;
     if (b < a.n_seqs) {
-      int64_t L = a.ctx[b];
-      if (L < 0 || L > cap) {
-        atomicOr(a.err, PKV_DEVERR_CONTEXT_LEN);
-        L = L < 0 ? 0 : cap;
-      }
+      L = length_of(b, true);
       nfull = (int32_t)(L / T);
       rag = (L % T != 0 || L == 0) ? 1 : 0;
     }
-    int32_t ftot, rtot;
+    int32_t ftot;
     const int32_t fo = full_base + block_exclusive_scan(nfull, smem, &ftot);
-    const int32_t ro = ragged_base + block_exclusive_scan(rag, smem, &rtot);
     if (b < a.n_seqs) {
-      const int32_t rrow = rag ? a.max_units - 1 - ro : -1;
       a.plan.seq_info[3 * b + 0] = fo;
       a.plan.seq_info[3 * b + 1] = nfull;
-      a.plan.seq_info[3 * b + 2] = rrow;
-      // rows must stay inside [0, F) and [max_units - R, max_units) without overlap
       for (int32_t j = 0; j < nfull; ++j)
-        if (fo + j < a.max_units) a.plan.work[fo + j] = make_int2(b, j);
-      if (rag && rrow >= 0) a.plan.work[rrow] = make_int2(b, nfull);
+        if (fo + j < a.max_units) a.plan.work[fo + j] = make_int4(b, j * T, (j + 1) * T, nfull + rag);
+      if (rag) atomicAdd(&bucket[bucket_of(L)], 1);
     }
     full_base += ftot;
-    ragged_base += rtot;
   }
-  if (threadIdx.x == 0) {
-    int32_t F = full_base, R = ragged_base;
-    if ((int64_t)F + R > a.max_units) {
-      atomicOr(a.err, PKV_DEVERR_WORK_OVERFLOW);
-      F = 0;  // run nothing rather than overlapping rows
-      R = 0;
+  __syncthreads();
+  const int32_t F = full_base;
+  int32_t R;
+  const int32_t cnt = bucket[tid];
+  const int32_t off = block_exclusive_scan(cnt, smem, &R);
+  bucket[tid] = F + off;
+  __syncthreads();
+  const bool overflow = (int64_t)F + R > a.max_units;
+
+  // pass 2: ragged rows, longest bucket first (order inside a bucket is free)
+  for (int32_t base = 0; base < a.n_seqs; base += kPlanThreads) {
+    const int32_t b = base + tid;
+    if (b < a.n_seqs) {
+      const int64_t L = length_of(b, false);
+      const int32_t nfull = (int32_t)(L / T);
+      int32_t row = -1;
+      if (L % T != 0 || L == 0) {
+        row = atomicAdd(&bucket[bucket_of(L)], 1);
+        if (!overflow) a.plan.work[row] = make_int4(b, nfull * T, (int32_t)L, nfull + 1);
+      }
+      a.plan.seq_info[3 * b + 2] = row;
     }
-    a.plan.counts[0] = F;
-    a.plan.counts[1] = R;
+  }
+  if (tid == 0) {
+    if (overflow) atomicOr(a.err, PKV_DEVERR_WORK_OVERFLOW);
+    a.plan.counts[0] = overflow ? 0 : F + R;  // run nothing rather than overlapping rows
+    a.plan.counts[1] = F;
   }
 }
 
@@ -580,7 +610,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   const int32_t f0 = si[0], nf = si[1], rr = si[2];
   const int32_t n = nf + (rr >= 0 ? 1 : 0);
   if (n <= 1) return;
-  if (a.plan.counts[0] + a.plan.counts[1] == 0) return;  // plan overflowed
+  if (a.plan.counts[0] == 0) return;  // plan overflowed
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int32_t D = a.d;
   float m_run = -INFINITY, s_run = 0.f, acc[DK];
@@ -719,7 +749,7 @@ int choose(int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t p, int32_
   int32_t W = 1;
   if (mfma) W = env_int("PKV_DECODE_WAVES", 4) == 8 ? 8 : 4;
   const int32_t tmin = mfma ? 32 * W : 64;
-  const int32_t tmax = mfma ? 512 * W : 512;
+  const int32_t tmax = mfma ? 16384 : 512;
   int32_t T;
   const int32_t forced = env_int("PKV_PARTITION_TOKENS", 0);
   if (env_is("PKV_DECODE_SPLIT", "off")) {
@@ -728,8 +758,11 @@ int choose(int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t p, int32_
   } else if (forced > 0) {
     T = std::max(tmin, pow2_floor(forced));
   } else {
-    // enough (partition, KV head) units for every compute unit to hold a few
-    const int64_t div = std::max(1, env_int("PKV_SPLIT_DIV", 8));
+    // The largest partition whose single unit still takes a small share of
+    // the whole launch (about half of it with two resident workgroups per
+    // compute unit): longer partitions mean fewer partial results written to
+    // HBM, shorter ones a shorter tail.
+    const int64_t div = std::max(1, env_int("PKV_SPLIT_DIV", 4));
     const int64_t want = total * hkv / ((int64_t)device_cu_count() * div);
     T = (int32_t)std::min<int64_t>(tmax, std::max<int64_t>(tmin, pow2_floor(std::max<int64_t>(want, 1))));
   }
@@ -757,7 +790,7 @@ Layout layout_of(int32_t n_seqs, int32_t hq, int32_t d, const Choice& c) {
   l.seq_info = off;
   off = align256(off + (size_t)3 * n_seqs * sizeof(int32_t));
   l.work = off;
-  off = align256(off + (size_t)c.max_units * sizeof(int2));
+  off = align256(off + (size_t)c.max_units * sizeof(int4));
   l.part_ml = off;
   if (c.need_partials) off = align256(off + (size_t)c.max_units * hq * 2 * sizeof(float));
   l.part_o = off;
@@ -894,13 +927,13 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.plan.counts = (int32_t*)(ws + lay.counts);
   a.plan.seq_info = (int32_t*)(ws + lay.seq_info);
-  a.plan.work = (int2*)(ws + lay.work);
+  a.plan.work = (int4*)(ws + lay.work);
   a.plan.part_ml = c.need_partials ? (float*)(ws + lay.part_ml) : nullptr;
   a.plan.part_o = c.need_partials ? (float*)(ws + lay.part_o) : nullptr;
   a.err = err;
 
   hipStream_t st = (hipStream_t)stream;
-  hipLaunchKernelGGL(pkv::plan_kernel, dim3(1), dim3(1024), 0, st, a);
+  hipLaunchKernelGGL(pkv::plan_kernel, dim3(1), dim3(pkv::kPlanThreads), 0, st, a);
   const int64_t waves = c.max_units * num_kv_heads;
   if (c.mfma) {
     const int32_t W = c.waves_per_group;

@@ -21,6 +21,22 @@ inline size_t dtype_size(pkv_dtype dt) { return dt == PKV_F32 ? 4 : 2; }
 
 inline bool dtype_valid(int dt) { return dt == PKV_F32 || dt == PKV_BF16; }
 
+// Block-table patch carried entirely in kernel arguments (no staging copy):
+// lens[len0 + i] = w[i] (i < n_len); slots[slot0 + i] = w[n_len + i]
+// (i < n_slot); then n_ent (row, col, value) triples; then n_reset (row, from)
+// pairs whose row entries [from, max_blocks) become -1.
+constexpr int kPatchWords = 896;
+struct TablePatchArgs {
+  int32_t* table;
+  int32_t* lens;
+  int32_t* slots;
+  int32_t max_blocks, n_len, len0, n_slot, slot0, n_ent, n_reset, unused;
+  int32_t w[kPatchWords];
+};
+
+// Enqueue one patch (defined with the device kernels).  Returns a status.
+int launch_table_patch(const TablePatchArgs& args, void* stream);
+
 }  // namespace pkv
 
 // Wrap every ABI body: converts stray C++ exceptions into status codes.

@@ -5,8 +5,8 @@ It owns a host block pool, the two device caches and the device-side metadata
 library calls together in the order a decode step needs them:
 
     append_slots (host) -> copy_blocks (copy-on-write) -> block_table_upload
-    (table, lengths and slot mapping in one staging round) -> cache_append ->
-    paged_attention_decode
+    (a full upload into a new table, then incremental patches of the new
+    entries, lengths and slot mapping) -> cache_append -> paged_attention_decode
 
 Everything that computes runs in libpkv.so; this class only keeps buffers and
 calls the binding.
@@ -103,6 +103,7 @@ class PagedKVCache:
         m.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=self.device)
         m.max_len = 0
         m.total = 0
+        m.uploaded = False   # the first upload into this new table is a full one
         self._meta = m
         return m
 
@@ -113,14 +114,17 @@ class PagedKVCache:
         if len(cow):
             copy_blocks(self.k_cache, self.v_cache, cow, stream)
         m.max_len, m.total = self.pool.block_table_upload(m.seqs, m.max_blocks, m.table, m.lens,
-                                                          slots, m.slots, stream)
+                                                          slots, m.slots, stream,
+                                                          incremental=m.uploaded)
+        m.uploaded = True
         cache_append(self.k_cache, self.v_cache, k_new, v_new, m.slots, stream)
         return slots
 
     def upload(self, m, stream=None):
         """Upload table and lengths without appending (e.g. after a prefill)."""
         m.max_len, m.total = self.pool.block_table_upload(m.seqs, m.max_blocks, m.table, m.lens,
-                                                          stream=stream)
+                                                          stream=stream, incremental=m.uploaded)
+        m.uploaded = True
 
     def attend(self, m, q, out, scale=None, stream=None):
         if m.max_len > m.ws_max_len or m.total > m.ws_total:

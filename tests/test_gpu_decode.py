@@ -271,3 +271,25 @@ def test_bad_indices_are_clamped_and_flagged():
         pkv.check_device_errors()
     assert "0x1" in str(e.value)
     assert pkv.check_device_errors() == 0
+
+
+def test_more_sequences_than_plan_threads(monkeypatch):
+    """1100 sequences: the plan walks the batch in several chunks and bucket-sorts
+    many ragged partitions; every output must still match the oracle."""
+    monkeypatch.setenv("PKV_PARTITION_TOKENS", "128")
+    cfg = DecodeConfig("many_seqs", 1100, 8, 2, 64, 16, "bf16", "uniform", length_lo=1,
+                       length_hi=600)
+    case = build_case(cfg, seed=6)
+    err = check_attention(case)
+    say(f"  1100 sequences: max err {err:.3e}")
+
+
+@pytest.mark.parametrize("part", ["256", "16384"])
+def test_long_partitions_span_several_table_windows(monkeypatch, part):
+    """Partitions longer than 64 blocks per wave walk several block-table windows."""
+    monkeypatch.setenv("PKV_PARTITION_TOKENS", part)
+    cfg = DecodeConfig("windows", 4, 16, 2, 128, 8, "bf16", "fixed",
+                       fixed_lengths=(9000, 4097, 2049, 513))
+    case = build_case(cfg, seed=7)
+    err = check_attention(case)
+    say(f"  part={part}: max err {err:.3e}")
