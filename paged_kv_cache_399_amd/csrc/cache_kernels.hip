@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void cache_append_tiles_kernel(
     for (int32_t c = tid; c < n_runs * p; c += nth) covered[run_start[c / p] + c % p] = 1;
     __syncthreads();
     for (int32_t t = tid; t < cnt; t += nth)
-      if (!covered[t]) loose[atomicAdd(&n_loose, 1)] = t;
+      if (!covered[t] && ws[t] >= 0) loose[atomicAdd(&n_loose, 1)] = t;
     __syncthreads();
     // rows outside runs, element by element
     for (int32_t e = tid; e < n_loose * hd; e += nth) {

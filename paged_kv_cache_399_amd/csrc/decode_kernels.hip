@@ -337,10 +337,25 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
     const int32_t krow_x = 8 * (n >> 2) + (n & 3);  // token of chain-X row n within the chunk
 
     // Loads of one chunk; addresses are clamped to the window's last token.
+    // A chunk spans at most NBC blocks; their ids are read from the window
+    // with uniform lane reads and each lane picks its own.
+    constexpr int NBC = CH / P > 1 ? CH / P : 1;
     auto issue = [&](Chunk& f, int32_t c0) {
+      const int32_t cb = min(c0, wlast) / P;  // uniform: the chunk's first block
+      int32_t bid[NBC];
+#pragma unroll
+      for (int k = 0; k < NBC; ++k) bid[k] = __builtin_amdgcn_readlane(tabv, min(cb + k - wb, 63));
+      auto pick = [&](int32_t t) -> int32_t {
+        const int32_t idx = t / P - cb;
+        int32_t v = bid[0];
+#pragma unroll
+        for (int k = 1; k < NBC; ++k) v = idx == k ? bid[k] : v;
+        return v;
+      };
       const int32_t tx = min(c0 + krow_x, wlast);
       const int32_t ty = min(c0 + krow_x + 4, wlast);
-      const int32_t pk = __shfl(tabv, tx / P - wb, 64);
+      // rows tx and ty (tx + 4 unless clamped) lie in one block: P >= 8
+      const int32_t pk = pick(tx);
       const uint16_t* kb = kc + (int64_t)pk * blk_stride + head_off + 8 * r;
       const uint16_t* kxp = kb + (tx % P) * D;
       const uint16_t* kyp = kb + (ty % P) * D;
@@ -351,7 +366,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
       }
       // values: tokens c0 + 8 r .. +7 of head_dim rows 16 j + n
       const int32_t tv = min(c0 + 8 * r, wlast);
-      const int32_t pv = __shfl(tabv, tv / P - wb, 64);
+      const int32_t pv = pick(tv);
       const uint16_t* vb = vc + (int64_t)pv * blk_stride + head_off + (int64_t)n * P + ((tv % P) & ~7);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) f.v[j] = load_stream16(vb + 16 * j * P);
@@ -466,6 +481,305 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
     const int32_t qh = g * G + h;
     if (u.nparts == 1) {
       store_f32((uint16_t*)a.out + ((int64_t)u.b * a.hq + qh) * D + dd, o * inv);
+    } else {
+      __builtin_nontemporal_store(o * inv, a.plan.part_o + ((int64_t)unit * a.hq + qh) * D + dd);
+      if (dd == 0) {
+        float* ml = a.plan.part_ml + ((int64_t)unit * a.hq + qh) * 2;
+        ml[0] = M * c;
+        ml[1] = sum;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Vector-ALU partition kernel for small head groups (G <= 4: multi-head
+// attention, or fp32 data), where the score and value products are too thin
+// for matrix cores.  Same unit / workgroup / LDS-combine structure as the
+// matrix-core kernel (W waves per (partition, KV head) unit).
+//
+// Scores: a key row of D elements is LPR = D / EPC lanes wide (EPC elements
+// per 16-byte piece), so one load instruction covers TPI = 64 / LPR tokens;
+// lane l holds piece l % LPR of token l / LPR.  Each lane forms partial dot
+// products with its piece of every query head, and the LPR lanes of a row are
+// summed with DPP row permutations (quad swaps, half-row and row mirrors).
+// The chunk maximum crosses rows with two or three shuffles.  The row's first
+// lane puts the probabilities in LDS; for the value product lane l owns head
+// dims l, l + 64, ... and reads every probability of the chunk back from LDS,
+// while its value loads are 16-byte runs of the token-minor value tile.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int moved = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false);
+  return v + __builtin_bit_cast(float, moved);
+}
+
+// sum over aligned groups of N lanes (N = 2, 4, 8, 16, 32), result in every lane
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if (N >= 2) v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  if (N >= 4) v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  if (N >= 8) v = dpp_add<0x141>(v);  // row_half_mirror: the other quad of the half-row
+  if (N >= 16) v = dpp_add<0x140>(v); // row_mirror: the other half of the row
+  if (N >= 32) v += __shfl_xor(v, 16, 64);
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ void unpack16(const uint4& x, float* f);
+template <>
+__device__ __forceinline__ void unpack16<uint16_t>(const uint4& x, float* f) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void unpack16<float>(const uint4& x, float* f) {
+  f[0] = __uint_as_float(x.x);
+  f[1] = __uint_as_float(x.y);
+  f[2] = __uint_as_float(x.z);
+  f[3] = __uint_as_float(x.w);
+}
+
+template <typename T, int D, int GMAX>
+__global__ __launch_bounds__(256) void decode_dpp_kernel(DecodeArgs a) {
+  constexpr int W = 4;                       // waves per workgroup
+  constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte piece
+  constexpr int LPR = D / EPC;               // lanes per key row
+  constexpr int TPI = 64 / LPR;              // tokens per load instruction
+  constexpr int CH = sizeof(T) == 2 ? 32 : 16;  // tokens per chunk
+  constexpr int KL = CH / TPI;               // key loads per lane per chunk
+  constexpr int DPL = D / 64;                // head dims per lane in the value product
+  constexpr int VP = CH / EPC;               // 16-byte value pieces per dim per chunk
+  constexpr int DP = D + 4;
+  static_assert(D % 64 == 0 && LPR >= 2 && LPR <= 32 && 64 % LPR == 0, "shape");
+  __shared__ float red_o[W][GMAX][DP];
+  __shared__ float red_m[W][GMAX], red_l[W][GMAX];
+  __shared__ float p_lds[W][GMAX][CH];
+
+  const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
+  const int32_t unit = blockIdx.x / a.hkv;
+  const int32_t g = blockIdx.x - unit * a.hkv;
+  if (unit >= a.max_units) return;  // uniform over the workgroup
+  const Unit u = decode_unit(a, unit);
+  if (!u.valid) return;             // uniform over the workgroup
+  const int32_t G = a.hq / a.hkv;
+  const int32_t P = a.p;
+  const int rr = lane / LPR, cc = lane % LPR;  // token within an instruction, piece within the row
+
+  const T* kc = (const T*)a.kc;
+  const T* vc = (const T*)a.vc;
+  const int64_t blk_stride = (int64_t)a.hkv * P * D;
+  const int64_t head_off = (int64_t)g * P * D;
+  const float c = a.scale_log2;
+
+  float acc[GMAX][DPL];
+  float m_run = -INFINITY;
+  float l_run[GMAX];
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) {
+    l_run[h] = 0.f;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) acc[h][j] = 0.f;
+  }
+  float mh[GMAX];
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) mh[h] = -INFINITY;
+
+  const int32_t TW = a.part_tokens / W;  // a multiple of CH
+  const int32_t s0 = u.t0 + w * TW;
+  const int32_t s1 = min(u.t1, s0 + TW);
+  if (s1 > s0) {
+    // this lane's piece of every query head, as fp32
+    float qf[GMAX][EPC];
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) {
+      uint4 x = uint4{0, 0, 0, 0};
+      if (h < G) x = *reinterpret_cast<const uint4*>((const T*)a.q + ((int64_t)u.b * a.hq + g * G + h) * D + cc * EPC);
+      unpack16<T>(x, qf[h]);
+    }
+    const int32_t* trow = a.table + (int64_t)u.b * a.max_blocks;
+    const int32_t last_blk = (s1 - 1) / P;
+    int32_t wb = 0, tabv = 0, wlast = 0;
+    auto load_window = [&](int32_t base) -> int32_t {
+      int32_t e = 0;
+      if (base + lane <= last_blk) {
+        e = trow[base + lane];
+        if ((uint32_t)e >= (uint32_t)a.num_blocks) {
+          atomicOr(a.err, PKV_DEVERR_TABLE_ENTRY);
+          e = 0;
+        }
+      }
+      return e;
+    };
+    int32_t vlast = 0, klast = 0;
+    struct Chunk {
+      uint4 kx[KL], vx[DPL][VP];
+    };
+    // loads of one chunk: key pieces, then value pieces, addresses clamped to
+    // the window (so the prefetch past its end stays in bounds)
+    // The TPI rows of one key load and the EPC tokens of one value piece lie
+    // in one block (TPI and EPC divide P), so each load's block id is
+    // wave-uniform and comes from a lane read, not a cross-lane shuffle.
+    auto issue = [&](Chunk& f, int32_t c0) {
+#pragma unroll
+      for (int i = 0; i < KL; ++i) {
+        const int32_t tb = min(c0 + TPI * i, klast);  // uniform, first row of the load
+        const int32_t pb = __builtin_amdgcn_readlane(tabv, tb / P - wb);
+        f.kx[i] = load_stream16((const uint16_t*)(kc + (int64_t)pb * blk_stride + head_off +
+                                                  (int64_t)(tb % P + rr) * D + cc * EPC));
+      }
+#pragma unroll
+      for (int k = 0; k < VP; ++k) {
+        const int32_t t = min(c0 + EPC * k, vlast);   // uniform
+        const int32_t pb = __builtin_amdgcn_readlane(tabv, t / P - wb);
+        const T* vrow = vc + (int64_t)pb * blk_stride + head_off + (t % P);
+#pragma unroll
+        for (int j = 0; j < DPL; ++j)
+          f.vx[j][k] = load_stream16((const uint16_t*)(vrow + (int64_t)(lane + 64 * j) * P));
+      }
+    };
+    auto compute = [&](Chunk& f, int32_t c0) {
+      // scores: partial dots, row sums
+      float sc[GMAX][KL];
+#pragma unroll
+      for (int i = 0; i < KL; ++i) {
+        float kf[EPC];
+        unpack16<T>(f.kx[i], kf);
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h) {
+          float d0 = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) d0 = fmaf(qf[h][e], kf[e], d0);
+          sc[h][i] = group_sum<LPR>(d0);
+        }
+      }
+      const bool ragged = c0 + CH > s1;  // uniform
+#pragma unroll
+      for (int i = 0; i < KL; ++i) {
+        const bool ok = !ragged || c0 + TPI * i + rr < s1;
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h) sc[h][i] = ok ? sc[h][i] : -INFINITY;
+      }
+      // chunk maximum per head: within the lane, then across the TPI rows
+      float alpha[GMAX];
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h) {
+        float x = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < KL; ++i) x = fmaxf(x, sc[h][i]);
+#pragma unroll
+        for (int o = LPR; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+        const float mn = fmaxf(mh[h], x);
+        alpha[h] = fast_exp2((mh[h] - mn) * c);
+        mh[h] = mn;
+      }
+      // probabilities -> LDS (first lane of each row), row partial sums
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h) {
+        const float mc = mh[h] * c;
+        float ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < KL; ++i) {
+          const float pr = fast_exp2(fmaf(sc[h][i], c, -mc));
+          ps += pr;
+          if (cc == 0) p_lds[w][h][TPI * i + rr] = pr;
+        }
+        l_run[h] = fmaf(l_run[h], alpha[h], ps);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // value product: lane owns dims lane + 64 j
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h)
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) acc[h][j] *= alpha[h];
+#pragma unroll
+      for (int k = 0; k < VP; ++k) {
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) {
+          float vf[EPC];
+          unpack16<T>(f.vx[j][k], vf);
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) {
+            // masked tokens: probability 0 and value 0, so stale data cannot leak
+            const float vv = (!ragged || c0 + EPC * k + e < s1) ? vf[e] : 0.f;
+#pragma unroll
+            for (int h = 0; h < GMAX; ++h) acc[h][j] = fmaf(p_lds[w][h][EPC * k + e], vv, acc[h][j]);
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    // windows of 64 blocks; the next chunk's loads are in flight while the
+    // current one is computed
+    Chunk f0, f1;
+    for (int32_t ws = s0; ws < s1;) {
+      wb = uniform(ws / P);
+      const int32_t we = min(s1, (wb + 64) * P);
+      wlast = we - 1;
+      // value pieces start at multiples of EPC inside a block; the window's
+      // last piece starts here
+      vlast = wlast - wlast % EPC;
+      // last key load of the window starts here (its rows stay in wlast's block)
+      klast = wlast - wlast % TPI;
+      tabv = load_window(wb);
+      int32_t c0 = ws;
+      issue(f0, c0);
+      while (true) {
+        issue(f1, c0 + CH);
+        compute(f0, c0);
+        c0 += CH;
+        if (c0 >= we) break;
+        issue(f0, c0 + CH);
+        compute(f1, c0);
+        c0 += CH;
+        if (c0 >= we) break;
+      }
+      ws = we;
+    }
+  }
+  // this wave's state -> LDS; lanes of one row hold the same token sums
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) {
+    float lt = l_run[h];
+#pragma unroll
+    for (int o = LPR; o < 64; o <<= 1) lt += __shfl_xor(lt, o, 64);
+    if (lane == 0) {
+      red_m[w][h] = mh[h];
+      red_l[w][h] = lt;
+    }
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) red_o[w][h][lane + 64 * j] = acc[h][j];
+  }
+  __syncthreads();
+  for (int32_t e = threadIdx.x; e < G * D; e += 64 * W) {
+    const int32_t h = e / D, dd = e - h * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < W; ++v)
+      if (red_l[v][h] > 0.f) M = fmaxf(M, red_m[v][h]);
+    float sum = 0.f, o = 0.f;
+#pragma unroll
+    for (int v = 0; v < W; ++v) {
+      const float lv = red_l[v][h];
+      if (lv > 0.f) {
+        const float wt = fast_exp2((red_m[v][h] - M) * c);
+        sum = fmaf(lv, wt, sum);
+        o = fmaf(wt, red_o[v][h][dd], o);
+      }
+    }
+    const float inv = sum > 0.f ? 1.f / sum : 0.f;
+    const int32_t qh = g * G + h;
+    if (u.nparts == 1) {
+      store_f32((T*)a.out + ((int64_t)u.b * a.hq + qh) * D + dd, o * inv);
     } else {
       __builtin_nontemporal_store(o * inv, a.plan.part_o + ((int64_t)unit * a.hq + qh) * D + dd);
       if (dd == 0) {
@@ -705,19 +1019,23 @@ int32_t pow2_floor(int64_t x) {
   return p;
 }
 
+enum Kind { kKindMfma, kKindDpp, kKindGeneric };
+
 struct Choice {
-  bool mfma;
-  int32_t waves_per_group;  // matrix-core path: waves sharing one unit
+  int kind;
+  int32_t waves_per_group;  // waves sharing one unit (matrix-core and DPP kernels)
   int32_t part_tokens;
   int64_t max_units;
   bool need_partials;
 };
 
-enum { kMathAuto, kMathValu, kMathMfma };
+enum { kMathAuto, kMathValu, kMathMfma, kMathDpp, kMathGeneric };
 
 int math_mode() {
-  if (env_is("PKV_DECODE_MATH", "valu")) return kMathValu;
+  if (env_is("PKV_DECODE_MATH", "valu")) return kMathValu;      // any vector-ALU kernel
   if (env_is("PKV_DECODE_MATH", "mfma")) return kMathMfma;
+  if (env_is("PKV_DECODE_MATH", "dpp")) return kMathDpp;
+  if (env_is("PKV_DECODE_MATH", "generic")) return kMathGeneric;
   return kMathAuto;
 }
 
@@ -726,30 +1044,52 @@ bool mfma_shape_ok(int32_t hq, int32_t hkv, int32_t d, int32_t p, pkv_dtype dt) 
   return dt == PKV_BF16 && (d == 64 || d == 128) && (p == 8 || p == 16 || p == 32) && G >= 1 && G <= 16;
 }
 
-bool valu_shape_ok(int32_t hq, int32_t hkv, int32_t d) { return d <= 256 && hq / hkv <= 16; }
+// DPP kernel: head_dim 64 / 128, head groups up to 4, block rows of whole
+// 16-byte pieces (block_size a multiple of 8 for bf16, of 4 for fp32)
+bool dpp_shape_ok(int32_t hq, int32_t hkv, int32_t d, int32_t p, pkv_dtype dt) {
+  const int32_t G = hq / hkv;
+  const int32_t epc = dt == PKV_BF16 ? 8 : 4;
+  return (d == 64 || d == 128) && G >= 1 && G <= 4 && p % epc == 0;
+}
+
+bool generic_shape_ok(int32_t hq, int32_t hkv, int32_t d) { return d <= 256 && hq / hkv <= 16; }
 
 int choose(int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t p, int32_t max_len,
            int64_t total, pkv_dtype dt, Choice* out) {
   const int mode = math_mode();
   const bool mshape = mfma_shape_ok(hq, hkv, d, p, dt);
-  bool mfma;
+  const bool dshape = dpp_shape_ok(hq, hkv, d, p, dt);
+  int kind;
   if (mode == kMathMfma) {
     if (!mshape) return fail(PKV_ERR_UNSUPPORTED, "matrix-core decode needs bf16, head_dim 64/128, block 8/16/32, G <= 16");
-    mfma = true;
+    kind = kKindMfma;
+  } else if (mode == kMathDpp) {
+    if (!dshape) return fail(PKV_ERR_UNSUPPORTED, "DPP decode needs head_dim 64/128, G <= 4, 16-byte block rows");
+    kind = kKindDpp;
+  } else if (mode == kMathGeneric) {
+    kind = kKindGeneric;
   } else if (mode == kMathValu) {
-    mfma = false;
+    kind = dshape ? kKindDpp : kKindGeneric;
+  } else if (mshape && hq / hkv >= 2) {
+    kind = kKindMfma;  // matrix cores only when a head group shares K/V
   } else {
-    mfma = mshape && hq / hkv >= 2;  // matrix cores only when a head group shares K/V
+    kind = dshape ? kKindDpp : kKindGeneric;
   }
-  if (!mfma && !valu_shape_ok(hq, hkv, d))
+  if (kind == kKindGeneric && !generic_shape_ok(hq, hkv, d))
     return fail(PKV_ERR_UNSUPPORTED, "decode supports head_dim <= 256 and Hq/Hkv <= 16");
   const int64_t L = std::max<int32_t>(max_len, 1);
   if (total < 0) total = (int64_t)n_seqs * L;
-  // matrix-core path: W waves share a partition of T tokens, T / W >= 32
-  int32_t W = 1;
-  if (mfma) W = env_int("PKV_DECODE_WAVES", 4) == 8 ? 8 : 4;
-  const int32_t tmin = mfma ? 32 * W : 64;
-  const int32_t tmax = mfma ? 16384 : 512;
+  // W waves share a partition of T tokens; each wave's share is whole chunks
+  int32_t W = 1, tmin = 64, tmax = 512;
+  if (kind == kKindMfma) {
+    W = env_int("PKV_DECODE_WAVES", 4) == 8 ? 8 : 4;
+    tmin = 32 * W;
+    tmax = 16384;
+  } else if (kind == kKindDpp) {
+    W = 4;
+    tmin = W * (dt == PKV_BF16 ? 32 : 16);
+    tmax = 16384;
+  }
   int32_t T;
   const int32_t forced = env_int("PKV_PARTITION_TOKENS", 0);
   if (env_is("PKV_DECODE_SPLIT", "off")) {
@@ -768,7 +1108,7 @@ int choose(int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t p, int32_
   }
   const int64_t by_len = (int64_t)n_seqs * ((L + T - 1) / T);
   const int64_t by_total = total / T + n_seqs;
-  out->mfma = mfma;
+  out->kind = kind;
   out->waves_per_group = W;
   out->part_tokens = T;
   out->max_units = std::max<int64_t>(1, std::min(by_len, by_total));
@@ -805,6 +1145,20 @@ void launch_mfma(const DecodeArgs& a, int32_t waves_per_group, int64_t groups, h
     hipLaunchKernelGGL((decode_mfma_kernel<D, P, 8>), dim3((unsigned)groups), dim3(512), 0, st, a);
   else
     hipLaunchKernelGGL((decode_mfma_kernel<D, P, 4>), dim3((unsigned)groups), dim3(256), 0, st, a);
+}
+
+template <typename T, int D>
+void launch_dpp_d(const DecodeArgs& a, int64_t groups, hipStream_t st) {
+  const int32_t G = a.hq / a.hkv;
+  if (G <= 1) hipLaunchKernelGGL((decode_dpp_kernel<T, D, 1>), dim3((unsigned)groups), dim3(256), 0, st, a);
+  else if (G <= 2) hipLaunchKernelGGL((decode_dpp_kernel<T, D, 2>), dim3((unsigned)groups), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((decode_dpp_kernel<T, D, 4>), dim3((unsigned)groups), dim3(256), 0, st, a);
+}
+
+template <typename T>
+void launch_dpp(const DecodeArgs& a, int64_t groups, hipStream_t st) {
+  if (a.d == 128) launch_dpp_d<T, 128>(a, groups, st);
+  else launch_dpp_d<T, 64>(a, groups, st);
 }
 
 template <typename T, int GMAX>
@@ -889,12 +1243,14 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   int rc = pkv::choose(n_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
                        total_context_tokens, dtype, &c);
   if (rc) return rc;
-  if (c.mfma) {
+  if (c.kind != pkv::kKindGeneric) {
     const uintptr_t mis = (uintptr_t)out | (uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache;
     if (mis % 16) {
-      if (pkv::math_mode() == pkv::kMathMfma)
-        return fail(PKV_ERR_UNSUPPORTED, "matrix-core decode needs 16-byte aligned buffers");
-      c.mfma = false;
+      const int mode = pkv::math_mode();
+      if (mode == pkv::kMathMfma || mode == pkv::kMathDpp)
+        return fail(PKV_ERR_UNSUPPORTED, "this decode kernel needs 16-byte aligned buffers");
+      // same partition length and workspace; the generic kernel takes any
+      c.kind = pkv::kKindGeneric;
     }
   }
   if ((int64_t)c.max_units * num_kv_heads > (int64_t)INT32_MAX)
@@ -935,7 +1291,7 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   hipStream_t st = (hipStream_t)stream;
   hipLaunchKernelGGL(pkv::plan_kernel, dim3(1), dim3(pkv::kPlanThreads), 0, st, a);
   const int64_t waves = c.max_units * num_kv_heads;
-  if (c.mfma) {
+  if (c.kind == pkv::kKindMfma) {
     const int32_t W = c.waves_per_group;
     if (head_dim == 128) {
       if (block_size == 8) pkv::launch_mfma<128, 8>(a, W, waves, st);
@@ -946,6 +1302,9 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
       else if (block_size == 16) pkv::launch_mfma<64, 16>(a, W, waves, st);
       else pkv::launch_mfma<64, 32>(a, W, waves, st);
     }
+  } else if (c.kind == pkv::kKindDpp) {
+    if (dtype == PKV_BF16) pkv::launch_dpp<uint16_t>(a, waves, st);
+    else pkv::launch_dpp<float>(a, waves, st);
   } else if (dtype == PKV_BF16) {
     pkv::launch_valu<uint16_t>(a, waves, st);
   } else {

@@ -113,6 +113,8 @@ SMALL_GQA = dataclasses.replace(CONFIGS["gqa"], name="gqa_small", batch=12, leng
 
 @pytest.mark.parametrize("env", [
     {"PKV_DECODE_MATH": "valu"},
+    {"PKV_DECODE_MATH": "generic"},
+    {"PKV_DECODE_MATH": "dpp"},
     {"PKV_DECODE_MATH": "mfma"},
     {"PKV_DECODE_SPLIT": "off"},
     {"PKV_PARTITION_TOKENS": "64"},
@@ -185,6 +187,25 @@ def test_edge_lengths(monkeypatch, dtype, hq, hkv, d, p, part):
     cfg = DecodeConfig(f"edge_{dtype}_{hq}_{hkv}_{d}_{p}", len(EDGE_LENGTHS), hq, hkv, d, p, dtype,
                        "fixed", fixed_lengths=tuple(EDGE_LENGTHS))
     case = build_case(cfg, seed=5)
+    err = check_attention(case)
+    say(f"  {cfg.name} part={part}: max err {err:.3e}")
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d,p", [
+    ("bf16", 4, 4, 128, 16), ("bf16", 6, 3, 64, 8), ("bf16", 9, 3, 128, 32),
+    ("bf16", 8, 2, 128, 16), ("f32", 8, 2, 128, 4), ("f32", 4, 4, 64, 16),
+    ("f32", 8, 8, 128, 32),
+])
+@pytest.mark.parametrize("part", ["256", "auto"])
+def test_dpp_kernel_shapes(monkeypatch, dtype, hq, hkv, d, p, part):
+    """The vector-ALU (DPP) kernel on every shape it takes: head groups 1-4
+    (3 runs padded in a 4-head slot), head_dim 64/128, block sizes 4-32."""
+    monkeypatch.setenv("PKV_DECODE_MATH", "dpp")
+    if part != "auto":
+        monkeypatch.setenv("PKV_PARTITION_TOKENS", part)
+    cfg = DecodeConfig(f"dpp_{dtype}_{hq}_{hkv}_{d}_{p}", len(EDGE_LENGTHS), hq, hkv, d, p, dtype,
+                       "fixed", fixed_lengths=tuple(EDGE_LENGTHS))
+    case = build_case(cfg, seed=8)
     err = check_attention(case)
     say(f"  {cfg.name} part={part}: max err {err:.3e}")
 
