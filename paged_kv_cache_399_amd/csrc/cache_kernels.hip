@@ -167,7 +167,13 @@ struct CopyPairs {
 };
 
 // grid (chunks, pairs): every block is one contiguous run of `words` words in
-// each cache, whatever the layout inside it.
+// each cache, whatever the layout inside it.  Each thread moves kCopyUnroll
+// words of each cache, all loads issued before the stores.  One word per
+// thread measured best: copy-on-write batches are small (a decode step copies
+// at most one block per sequence), so spreading them over more workgroups
+// beats deeper per-thread pipelines.
+constexpr int kCopyUnroll = 1;
+
 template <typename W>
 __global__ __launch_bounds__(256) void copy_blocks_kernel(W* __restrict__ kc, W* __restrict__ vc,
                                                           CopyPairs pairs, int64_t words,
@@ -182,10 +188,26 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(W* __restrict__ kc, W*
   const W* vs = vc + (int64_t)src * words;
   W* kd = kc + (int64_t)dst * words;
   W* vd = vc + (int64_t)dst * words;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    kd[i] = ks[i];
-    vd[i] = vs[i];
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i0 < words;
+       i0 += stride * kCopyUnroll) {
+    W k[kCopyUnroll], v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i < words) {
+        k[u] = ks[i];
+        v[u] = vs[i];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i < words) {
+        kd[i] = k[u];
+        vd[i] = v[u];
+      }
+    }
   }
 }
 
@@ -295,7 +317,8 @@ extern "C" int pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pair
   const int64_t bytes = (int64_t)num_kv_heads * block_size * head_dim * pkv::dtype_size(dtype);
   const bool vec = bytes % 16 == 0 && (uintptr_t)k_cache % 16 == 0 && (uintptr_t)v_cache % 16 == 0;
   const int64_t words = vec ? bytes / 16 : bytes / 2;
-  const int chunks = (int)std::max<int64_t>(1, std::min<int64_t>(64, (words + 255) / 256));
+  const int chunks = (int)std::max<int64_t>(
+      1, std::min<int64_t>(64, (words + 256 * pkv::kCopyUnroll - 1) / (256 * pkv::kCopyUnroll)));
   hipStream_t st = (hipStream_t)stream;
   for (int32_t base = 0; base < n_pairs; base += pkv::kMaxPairsPerLaunch) {
     const int32_t n = std::min(pkv::kMaxPairsPerLaunch, n_pairs - base);

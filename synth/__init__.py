@@ -47,6 +47,7 @@ import numpy as np
 __all__ = [
     "DecodeConfig", "CONFIGS", "stream_seed", "context_lengths", "pool_size",
     "free_order", "Workload", "make_workload", "bf16_bits", "to_numpy_f32",
+    "BeamConfig", "BEAM_CONFIGS", "BeamWorkload", "make_beam_workload",
 ]
 
 
@@ -223,3 +224,87 @@ def make_workload(cfg: DecodeConfig, seed: int = 0, device="cpu",
     sk = _draw(cfg, (extra_steps, cfg.batch, hkv, d), seed, "step_k", device)
     sv = _draw(cfg, (extra_steps, cfg.batch, hkv, d), seed, "step_v", device)
     return Workload(cfg, seed, lens, nb, order, q, pk, pv, ck, cv, cu, sk, sv)
+
+
+# --------------------------------------------------------------------------
+# Fan-out (beam-search / parallel-sample style) workload
+# --------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class BeamConfig:
+    """``groups`` prompts, each forked into ``fanout`` sequences that share it.
+
+    Prompt lengths are uniform in [length_lo, length_hi] and usually end inside
+    a block, so the first token each sharer appends copies that partly filled
+    block (all but the last sharer in call order).
+    """
+    name: str
+    groups: int
+    fanout: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    dtype: str
+    length_lo: int
+    length_hi: int
+    pool_headroom: float = 1.25
+    value_dist: str = "normal"      # N(0,1)
+
+    @property
+    def batch(self) -> int:
+        return self.groups * self.fanout
+
+
+BEAM_CONFIGS: Dict[str, BeamConfig] = {
+    "beam": BeamConfig("beam", 64, 4, 32, 8, 128, 16, "bf16", 128, 2048),
+}
+
+
+@dataclasses.dataclass
+class BeamWorkload:
+    cfg: BeamConfig
+    seed: int
+    prompt_lengths: np.ndarray    # int64[groups]
+    num_blocks: int
+    free_order: np.ndarray        # int32[num_blocks]
+    q: object                     # torch [batch, Hq, D]; sequence b belongs to group b // fanout
+    prompt_k: object              # torch [sum(prompt_lengths), Hkv, D]
+    prompt_v: object
+    cu: np.ndarray                # int64[groups + 1] prompt offsets
+    step_k: object                # torch [steps, batch, Hkv, D]
+    step_v: object
+
+    @property
+    def torch_dtype(self):
+        import torch
+        return torch.float32 if self.cfg.dtype == "f32" else torch.bfloat16
+
+    def seq_kv(self, b: int, steps: int):
+        """(k, v) of sequence b in logical order after ``steps`` appended tokens."""
+        import torch
+        gi = b // self.cfg.fanout
+        lo, hi = int(self.cu[gi]), int(self.cu[gi + 1])
+        k = torch.cat([self.prompt_k[lo:hi], self.step_k[:steps, b]], 0)
+        v = torch.cat([self.prompt_v[lo:hi], self.step_v[:steps, b]], 0)
+        return k, v
+
+
+def make_beam_workload(cfg: BeamConfig, seed: int = 0, device="cpu",
+                       steps: int = 1) -> BeamWorkload:
+    rng = _rng(seed, "lengths")
+    plen = rng.integers(cfg.length_lo, cfg.length_hi + 1, size=cfg.groups, dtype=np.int64)
+    p = cfg.block_size
+    # prompts once, then every sequence's own blocks for its appended tokens
+    # (a copied partial block plus the blocks its new tokens open)
+    need = sum(_pages(int(l), p) for l in plen)
+    need += sum(cfg.fanout * (_pages(int(l) + steps, p) - int(l) // p) for l in plen)
+    nb = int(math.ceil(cfg.pool_headroom * need))
+    order = free_order(nb, seed)
+    cu = np.zeros(cfg.groups + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(plen)
+    b = cfg.batch
+    hq, hkv, d = cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+    draw = lambda shape, stream: _draw(cfg, shape, seed, stream, device)  # noqa: E731
+    return BeamWorkload(cfg, seed, plen, nb, order, draw((b, hq, d), "q"),
+                        draw((int(cu[-1]), hkv, d), "k"), draw((int(cu[-1]), hkv, d), "v"), cu,
+                        draw((steps, b, hkv, d), "step_k"), draw((steps, b, hkv, d), "step_v"))
