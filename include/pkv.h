@@ -230,15 +230,32 @@ int pkv_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_
  *   d_context_lens   device int32[n_seqs], 0 <= L <= max_blocks_per_seq * P
  *   max_context_len  >= every L (host knowledge, used for sizing)
  *   total_context_tokens  sum of L, or -1 if unknown (sizing only)
- *   workspace        device, >= pkv_decode_workspace_bytes(...) bytes
- * Long contexts are cut into fixed partitions whose partial results are merged
- * by a second kernel; the summation order depends only on logical positions,
- * so results do not depend on where the blocks sit.  Arithmetic is fp32
- * (bf16 inputs: score and value products on matrix cores with fp32
- * accumulation).  Supported: head_dim <= 256, Hq % Hkv == 0, Hq / Hkv <= 16,
- * any block_size >= 1; fastest path: bf16, head_dim 64/128, block_size a
- * multiple of 8.  Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.  Bad
- * table entries or lengths are clamped in-bounds and flagged. */
+ *   workspace        device, >= pkv_decode_workspace_bytes(...) bytes,
+ *                    caller-owned scratch for one call at a time: calls that
+ *                    share a workspace must be ordered (same stream)
+ * Work decomposition: each sequence is cut into partitions of T tokens (T a
+ * power of two chosen from the batch's size, the same for every call with the
+ * same sizing arguments); a workgroup of four waves takes one (partition, KV
+ * head) unit and all query heads of that KV head, so every key/value byte is
+ * read once.  A plan kernel orders the units longest first; sequences with
+ * several partitions are combined by a merge kernel.  The summation order
+ * depends only on logical positions, T and the wave split, so results do not
+ * depend on where the blocks sit.  Arithmetic is fp32.  Kernel per shape:
+ *   - bf16, head_dim 64/128, block_size 8/16/32, 2 <= G <= 16: matrix cores
+ *     (score and value products as 16x16x32 bf16 MFMA, head group as N);
+ *   - G <= 4 (including multi-head, G = 1) or fp32, head_dim 64/128,
+ *     block_size * element size a multiple of 16 bytes: vector ALU with DPP
+ *     row reductions;
+ *   - anything else with head_dim <= 256 and G <= 16: a generic vector-ALU
+ *     kernel.
+ * The environment variable PKV_DECODE_MATH = mfma | dpp | generic | valu
+ * forces a kernel (UNSUPPORTED if the shape does not fit it); the matrix-core
+ * and DPP kernels also need 16-byte aligned q, out and caches (otherwise the
+ * generic kernel runs).  PKV_PARTITION_TOKENS forces T (rounded down to a
+ * power of two, at least one chunk per wave); PKV_DECODE_SPLIT=off makes
+ * every sequence a single partition.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.  Bad table entries or
+ * lengths are clamped in-bounds and flagged. */
 int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
                                const void* v_cache, const int32_t* d_block_table,
                                const int32_t* d_context_lens, int32_t n_seqs,
