@@ -18,8 +18,8 @@ Modules
                 caches after tokens are written at their slots.
 ``attention``   decode attention in float64 over each sequence's keys and
                 values in logical order, a pure-Python brute force for tiny
-                inputs, and the partition-and-merge identity for split
-                contexts.
+                inputs, the partition-and-merge identity for split contexts,
+                and causal attention of a chunk of appended tokens (prefill).
 
 Every function is pinned by ``tests/test_oracle_*.py`` to something other than
 itself: the numbers the pages print, closed forms, brute force and library
@@ -36,6 +36,9 @@ routines.  Pins per function:
                           float64, closed-form two-token case, L=1 and
                           equal-key special cases, GQA == repeated MHA.
 * attention.partitioned   equality with the unsplit definition.
+* attention.prefill       brute force, torch scaled_dot_product_attention with an
+                          explicit causal mask in float64, each row equal to
+                          decode over the keys it sees, single-key rows.
 """
 from . import accounting, attention, layout, pool_model  # noqa: F401
 from .pool_model import (PoolModel, PoolError, NoBlocks, BadSeq,  # noqa: F401

@@ -136,3 +136,33 @@ def partitioned(q, k, v, part_tokens: int, scale: float = None) -> np.ndarray:
     parts = [partition_stats(q, k[s:s + part_tokens], v[s:s + part_tokens], scale)
              for s in range(0, l, part_tokens)]
     return merge(parts)
+
+
+def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float = None) -> np.ndarray:
+    """Causal attention of a sequence's newest tokens, float64.
+
+    q [n, Hq, D] are the queries of the last n of the sequence's L tokens
+    (positions L - n .. L - 1); k / v [L, Hkv, D] are all L tokens in logical
+    order.  Query i sees keys 0 .. L - n + i: the tokens before it and itself,
+    which is what appending a chunk of tokens to a paged sequence and attending
+    from each of them computes.  Per KV head: scores [n, L], masked above the
+    causal boundary, softmax per row after subtracting the row maximum, times V.
+    """
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    n, hq, d = q.shape
+    l, hkv, d2 = k.shape
+    assert d2 == d and v.shape == k.shape and hq % hkv == 0 and n <= l
+    if scale is None:
+        scale = default_scale(d)
+    g = hq // hkv
+    out = np.zeros((n, hq, d), dtype=np.float64)
+    pos = (l - n) + np.arange(n)                          # absolute position of each query
+    visible = np.arange(l)[None, :] <= pos[:, None]       # [n, L]
+    for h in range(hq):
+        j = h // g
+        s = (q[:, h, :] @ k[:, j, :].T) * scale           # [n, L]
+        s = np.where(visible, s, -np.inf)
+        s -= s.max(axis=1, keepdims=True)
+        w = np.exp(s)
+        out[:, h, :] = (w @ v[:, j, :]) / w.sum(axis=1, keepdims=True)
+    return out

@@ -6,6 +6,7 @@ import pytest
 import torch
 
 from oracle import attention
+from oracle import attention as oatt
 
 
 def _rand(rng, *shape):
@@ -118,3 +119,66 @@ def test_bf16_inputs_convert_before_the_maths():
     ref = attention.decode(x[0].to(torch.float64).numpy(), x.to(torch.float64).numpy(),
                            x.to(torch.float64).numpy())
     assert np.array_equal(out, ref)
+
+
+def _prefill_brute(q, k, v):
+    """Pure-Python causal attention of the last n tokens (positions L - n ..)."""
+    q, k, v = oatt.as_f64(q).tolist(), oatt.as_f64(k).tolist(), oatt.as_f64(v).tolist()
+    n, hq, d = len(q), len(q[0]), len(q[0][0])
+    l, hkv = len(k), len(k[0])
+    g = hq // hkv
+    scale = 1.0 / math.sqrt(d)
+    out = []
+    for i in range(n):
+        last = l - n + i
+        row = []
+        for h in range(hq):
+            kv = h // g
+            sc = [scale * sum(q[i][h][x] * k[t][kv][x] for x in range(d)) for t in range(last + 1)]
+            top = max(sc)
+            w = [math.exp(s - top) for s in sc]
+            tot = sum(w)
+            row.append([sum(w[t] * v[t][kv][x] for t in range(last + 1)) / tot for x in range(d)])
+        out.append(row)
+    return out
+
+
+@pytest.mark.parametrize("hq,hkv,l,n,d", [(2, 1, 5, 5, 4), (4, 2, 7, 3, 8), (3, 3, 6, 1, 4)])
+def test_prefill_matches_brute_force(hq, hkv, l, n, d):
+    rng = np.random.default_rng(l * 10 + n)
+    q = rng.uniform(-1, 1, (n, hq, d))
+    k = rng.uniform(-1, 1, (l, hkv, d))
+    v = rng.uniform(-1, 1, (l, hkv, d))
+    assert np.allclose(oatt.prefill(q, k, v), np.array(_prefill_brute(q, k, v)), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("hq,hkv,l,n", [(8, 2, 40, 40), (4, 4, 33, 9), (6, 1, 17, 16)])
+def test_prefill_matches_torch_sdpa_with_causal_mask(hq, hkv, l, n):
+    import torch
+    rng = np.random.default_rng(hq + l)
+    d = 16
+    q = rng.standard_normal((n, hq, d))
+    k = rng.standard_normal((l, hkv, d))
+    v = rng.standard_normal((l, hkv, d))
+    g = hq // hkv
+    kt = torch.from_numpy(np.repeat(k, g, axis=1)).permute(1, 0, 2)      # [Hq, L, D]
+    vt = torch.from_numpy(np.repeat(v, g, axis=1)).permute(1, 0, 2)
+    qt = torch.from_numpy(q).permute(1, 0, 2)                           # [Hq, n, D]
+    mask = torch.arange(l)[None, :] <= (l - n + torch.arange(n))[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)
+    assert np.allclose(oatt.prefill(q, k, v), ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+
+
+def test_prefill_rows_are_decodes_over_the_visible_keys():
+    rng = np.random.default_rng(3)
+    l, n, hq, hkv, d = 30, 12, 8, 2, 8
+    q = rng.standard_normal((n, hq, d))
+    k = rng.standard_normal((l, hkv, d))
+    v = rng.standard_normal((l, hkv, d))
+    out = oatt.prefill(q, k, v)
+    for i in range(n):
+        last = l - n + i
+        assert np.allclose(out[i], oatt.decode(q[i], k[:last + 1], v[:last + 1]), rtol=0, atol=1e-13)
+    # the first token of a fresh sequence sees only itself: its value, exactly
+    first = oatt.prefill(q[:1], k[:1], v[:1])
+    assert np.array_equal(first[0], np.repeat(v[0], hq // hkv, axis=0))
