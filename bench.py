@@ -31,7 +31,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="long", help="tiny|small_mha|gqa|long|prefix|beam")
+    ap.add_argument("--config", default="long", help="tiny|small_mha|gqa|long|prefix|beam|prefill|prefill_chunk")
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -178,6 +178,83 @@ def run_beam(args):
     print(json.dumps(result), flush=True)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def run_prefill(args):
+    """Chunked / whole-prompt prefill: append the new tokens, then causal attention
+    from each of them; matrix-core bound, reported in TFLOP/s."""
+    import torch
+    from synth import PREFILL_CONFIGS, make_prefill_workload
+    from paged_kv_cache_399_amd import paged_attention_prefill
+    from paged_kv_cache_399_amd.session import PagedKVCache
+
+    cfg = PREFILL_CONFIGS[args.config]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = make_prefill_workload(cfg, args.seed, dev)
+    b, hq, hkv, d, p = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
+    kv = PagedKVCache(w.num_blocks, p, hkv, d, torch.bfloat16, dev, w.free_order, fill=0.0)
+    seqs = kv.new_sequences(b)
+    if cfg.context:
+        slots, _ = kv.pool.append_slots(seqs, [cfg.context] * b)
+        kv.write_slots(torch.from_numpy(slots).to(dev), w.ctx_k, w.ctx_v)
+    total = cfg.context + cfg.new
+    m = kv.prepare(seqs, -(-total // p), hq, total, b * total)
+    out = torch.empty_like(w.q)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    kv.extend(m, [cfg.new] * b, w.new_k, w.new_v, w.q, out, stream=stream)
+    torch.cuda.synchronize()
+    extend_ms = (time.perf_counter() - t0) * 1e3
+    # the attention alone, back to back on the final state
+    for _ in range(args.warmup):
+        paged_attention_prefill(out, w.q, kv.k_cache, kv.v_cache, m.table, m.lens, m.query_start,
+                                cfg.new, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        paged_attention_prefill(out, w.q, kv.k_cache, kv.v_cache, m.table, m.lens, m.query_start,
+                                cfg.new, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    keys_seen = b * sum(cfg.context + i + 1 for i in range(cfg.new))      # causal
+    flops = 4.0 * d * hq * keys_seen
+    tflops = flops / (ms * 1e-3) / 1e12
+    err = None
+    if args.check:
+        from oracle import attention as oatt
+        from synth import bf16_bits
+        worst = 0.0
+        for bi in (0, b - 1):
+            rows = slice(bi * cfg.new, (bi + 1) * cfg.new)
+            k = torch.cat([w.ctx_k[bi * cfg.context:(bi + 1) * cfg.context], w.new_k[rows]], 0)
+            v = torch.cat([w.ctx_v[bi * cfg.context:(bi + 1) * cfg.context], w.new_v[rows]], 0)
+            ref = oatt.prefill(bf16_bits(w.q[rows]), bf16_bits(k), bf16_bits(v))
+            worst = max(worst, float(np.abs(out[rows].double().cpu().numpy() - ref).max()))
+        err = worst
+    result = {
+        "metric": "paged prefill attention: TFLOP/s (% of dense bf16 matrix-core peak)",
+        "value": round(tflops, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": b, "context": cfg.context, "new_tokens": cfg.new,
+                   "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d, "block_size": p,
+                   "seed": args.seed, "parallelism": "single GPU"},
+        "tokens_per_s": round(b * cfg.new / (ms * 1e-3), 1),
+        "extend_ms_first_call": round(extend_ms, 3),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "paged_attention_prefill"},
+    }
+    if err is not None:
+        result["check_max_err"] = err
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -189,6 +266,9 @@ def main():
     from paged_kv_cache_399_amd.session import PagedKVCache
     if args.config in BEAM_CONFIGS:
         return run_beam(args)
+    from synth import PREFILL_CONFIGS
+    if args.config in PREFILL_CONFIGS:
+        return run_prefill(args)
 
     cfg = CONFIGS[args.config]
     if args.block_size:

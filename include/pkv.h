@@ -265,6 +265,35 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
                                int64_t total_context_tokens, float scale, pkv_dtype dtype,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Paged prefill attention: causal attention of the newest tokens of each
+ * sequence over everything it holds ("Fixed-Size KV Blocks": a prompt's
+ * blocks are handed out as its tokens arrive; "The Block Table Map": the
+ * kernel follows each table).  The new tokens must already be in the cache
+ * (pkv_cache_append).  For sequence b, n_b = d_query_start[b+1] -
+ * d_query_start[b] new tokens are the last n_b of its L_b = d_context_lens[b]
+ * tokens; query row d_query_start[b] + i (position L_b - n_b + i) attends keys
+ * 0 .. L_b - n_b + i:
+ *   out[row,h] = sum_{t <= L_b-n_b+i} softmax_t(scale * q[row,h] . K_b[t,g]) V_b[t,g]
+ * with K_b / V_b, g = h / G as in pkv_paged_attention_decode.
+ *   out, q            device [total new tokens, Hq, D], bf16
+ *   d_query_start     device int32[n_seqs + 1], nondecreasing, starting at 0
+ *   d_context_lens    device int32[n_seqs], n_b <= L_b <= max_blocks_per_seq * P
+ *   max_query_len     >= every n_b (host knowledge, sizes the grid)
+ * Both products run on matrix cores; key/value chunks of 32 tokens are staged
+ * once per workgroup in LDS and shared by a tile of queries.  Supported: bf16,
+ * head_dim 64 / 128, block_size a multiple of 8, G in {1, 2, 4, 8, 16},
+ * n_seqs <= 65535, 16-byte aligned q, out and caches.  A sequence whose length
+ * is out of range is skipped (its rows unwritten) and flagged
+ * (PKV_DEVERR_CONTEXT_LEN); bad table entries are clamped and flagged.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+int pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* d_block_table,
+                                const int32_t* d_context_lens, const int32_t* d_query_start,
+                                int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                int32_t max_blocks_per_seq, int32_t max_query_len, float scale,
+                                pkv_dtype dtype, void* stream);
+
 /* Synchronise `stream`, then read and clear the current device's error bits
  * (PKV_DEVERR_*) into *flags_out.  Returns PKV_ERR_DEVICE if any bit was set. */
 int pkv_check_device_errors(void* stream, int32_t* flags_out);

@@ -26,7 +26,8 @@ from ._lib import (DEVERR_CONTEXT_LEN, DEVERR_COPY_PAIR, DEVERR_SLOT,  # noqa: F
 lib = _lib.load()
 
 __all__ = ["PkvError", "BlockPool", "cache_append", "copy_blocks", "decode_workspace_bytes",
-           "paged_attention_decode", "check_device_errors", "version", "lib"]
+           "paged_attention_decode", "paged_attention_prefill", "check_device_errors", "version",
+           "lib"]
 
 
 class PkvError(RuntimeError):
@@ -285,6 +286,37 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens,
         _dev(block_table, "block_table"), _dev(context_lens, "context_lens"), b, hq, hkv, d, bs,
         nb, block_table.shape[1], int(max_context_len), int(total_context_tokens), float(scale),
         dt, _dev(workspace, "workspace"), workspace.numel(), _stream_ptr(stream)))
+    return out
+
+
+def paged_attention_prefill(out, q, k_cache, v_cache, block_table, context_lens, query_start,
+                            max_query_len: int, scale: Optional[float] = None, stream=None):
+    """Causal attention of each sequence's newest tokens over its whole paged context.
+
+    ``q`` / ``out`` are [total new tokens, Hq, D]; ``query_start`` is a device
+    int32 [n_seqs + 1] prefix of new-token counts; the new tokens must already
+    be in the cache.  Writes ``out`` and returns it.
+    """
+    import torch
+    nb, hkv, bs, d = _cache_shape(k_cache, v_cache)
+    nt, hq, d2 = q.shape
+    if d2 != d or tuple(out.shape) != (nt, hq, d):
+        raise ValueError("q / out must be [tokens, num_q_heads, head_dim]")
+    if q.dtype != k_cache.dtype or out.dtype != k_cache.dtype:
+        raise TypeError("q / out dtype must match the cache")
+    b = context_lens.numel()
+    if block_table.dim() != 2 or block_table.shape[0] != b or block_table.dtype != torch.int32:
+        raise ValueError("block_table must be int32 [n_seqs, max_blocks_per_seq]")
+    if context_lens.dtype != torch.int32 or query_start.dtype != torch.int32 or \
+            query_start.numel() != b + 1:
+        raise ValueError("context_lens int32 [n_seqs], query_start int32 [n_seqs + 1]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check(lib.pkv_paged_attention_prefill(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_table, "block_table"), _dev(context_lens, "context_lens"),
+        _dev(query_start, "query_start"), b, hq, hkv, d, bs, nb, block_table.shape[1],
+        int(max_query_len), float(scale), _dtype_code(q), _stream_ptr(stream)))
     return out
 
 

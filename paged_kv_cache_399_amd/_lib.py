@@ -60,6 +60,9 @@ SIGNATURES = {
     "pkv_paged_attention_decode": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                              _i32, _i32, _i32, _i32, _i64, C.c_float, C.c_int, _vp,
                                              C.c_size_t, _vp]),
+    "pkv_paged_attention_prefill": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                              _i32, _i32, _i32, _i32, _i32, C.c_float, C.c_int,
+                                              _vp]),
     "pkv_check_device_errors": (C.c_int, [_vp, _pi32]),
     "pkv_last_error": (C.c_char_p, []),
     "pkv_version": (C.c_char_p, []),

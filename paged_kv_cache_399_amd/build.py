@@ -20,7 +20,7 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
 HOST_SOURCES = ["block_pool.cpp", "abi_pool.cpp"]
-HIP_SOURCES = ["device_errors.hip", "cache_kernels.hip", "decode_kernels.hip"]
+HIP_SOURCES = ["device_errors.hip", "cache_kernels.hip", "decode_kernels.hip", "prefill_kernels.hip"]
 
 HOST_FLAGS = ["-O2", "-g", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-Wno-unused-parameter",
               "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include", f"-I{INCLUDE}", f"-I{CSRC}"]

@@ -1,0 +1,329 @@
+// Paged prefill attention for gfx950 (MI355X): causal attention of a chunk of
+// newly appended tokens over everything the sequence holds.
+//
+// The chunk's blocks are handed out as the tokens arrive ("PagedAttention
+// Internals", "Fixed-Size KV Blocks"; "pagedattention" topic page, third
+// paragraph) and cache_append has stored them; then for sequence b with L
+// tokens of which the last n are new, query i (position L - n + i) and query
+// head h (KV head g = h / G) computes
+//     out[i,h] = sum_{t <= L-n+i} softmax_t(scale * q[i,h] . K[t,g]) V[t,g]
+// with K / V reached through the block table as in decode.
+//
+// Unlike decode this is a dense contraction: every key/value chunk serves a
+// whole tile of queries, so it is staged once in LDS per workgroup and all
+// waves run both products on matrix cores from there.
+//
+// Work decomposition: grid (query tiles, sequences, KV heads); a workgroup
+// takes BT query tokens of one sequence and all G query heads of one KV head
+// (G * BT / 16 waves); wave w takes 16 query tokens of query head w % G.
+// Tiles are launched last-first: later tiles see more keys, so the dispatcher
+// starts the longest work first.
+//
+// Lane layout (as in the decode matrix-core kernel, with query tokens in the
+// 16-wide N dimension): lane l has n = l % 16 (its query column) and
+// r = l / 16.  For a 32-key chunk, two 16x16x32 MFMA chains produce the
+// scores of keys 8r .. 8r + 7 for query n; those eight probabilities are the B
+// operand of the value MFMA, whose A operand is the 16-byte run of the
+// token-minor value tile (dims 16 j + n, keys 8r .. 8r + 7).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const int32_t* table;
+  const int32_t* ctx;
+  const int32_t* qstart;
+  int32_t n_seqs, hq, hkv, p, num_blocks, max_blocks;
+  float scale_log2;  // scale * log2(e): scores are kept in log2 units
+  int32_t* err;
+};
+
+// Plain cached loads: a key/value chunk is read by every query tile of the
+// sequence, so unlike decode the second reader should find it in L2.
+__device__ __forceinline__ uint4 load16(const uint16_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int D, int G, int BT>
+__global__ __launch_bounds__(64 * G * BT / 16) void prefill_mfma_kernel(PrefillArgs a) {
+  constexpr int NW = G * BT / 16;  // waves
+  constexpr int NT = 64 * NW;      // threads
+  constexpr int CH = 32;           // keys per chunk
+  constexpr int KI = D / 32;       // score MFMA steps over head_dim
+  constexpr int NJ = D / 16;       // value MFMA output tiles over head_dim
+  constexpr int KS = D + 8;        // padded LDS key row (elements)
+  constexpr int VS = CH + 8;       // padded LDS value row (elements)
+  constexpr int KP = CH * D / 8;   // 16-byte key pieces per chunk
+  constexpr int VP = D * CH / 8;   // 16-byte value pieces per chunk
+  constexpr int PER = (KP + VP + NT - 1) / NT;
+  __shared__ __align__(16) uint16_t k_lds[2][CH * KS];
+  __shared__ __align__(16) uint16_t v_lds[2][D * VS];
+
+  const int32_t b = blockIdx.y, g = blockIdx.z;
+  const int32_t tile = (int32_t)gridDim.x - 1 - (int32_t)blockIdx.x;  // last tiles first
+  const int32_t q0 = a.qstart[b];
+  const int32_t n = a.qstart[b + 1] - q0;
+  if (n <= 0 || tile * BT >= n) return;  // uniform over the workgroup
+  const int32_t P = a.p;
+  int32_t L = a.ctx[b];
+  if (L < n || (int64_t)L > (int64_t)a.max_blocks * P) {
+    if (threadIdx.x == 0 && tile == 0) atomicOr(a.err, PKV_DEVERR_CONTEXT_LEN);
+    return;  // the sequence's rows are left unwritten
+  }
+  const int32_t base = L - n;  // position of query 0
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hh = w % G, ts = w / G;
+  const int nq = lane & 15, r = lane >> 4;
+  const int32_t head = g * G + hh;
+  const int32_t wq0 = tile * BT + ts * 16;           // this wave's first query
+  const int32_t qi = min(wq0 + nq, n - 1);           // columns past the end repeat the last query
+  const bool q_ok = wq0 + nq < n;
+  const int32_t qpos = base + qi;
+  const int32_t wave_kend = wq0 < n ? base + min(wq0 + 15, n - 1) + 1 : 0;  // keys [0, wave_kend)
+  const int32_t kend = base + min(tile * BT + BT - 1, n - 1) + 1;          // the workgroup's keys
+  const int32_t nchunks = (kend + CH - 1) / CH;
+  const float c = a.scale_log2;
+
+  // query fragments (B operand of the score MFMA): dims 32 i + 8 r of query qi
+  bf16x8 qf[KI];
+  {
+    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)(q0 + qi) * a.hq + head) * D + 8 * r;
+#pragma unroll
+    for (int i = 0; i < KI; ++i)
+      qf[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qrow + 32 * i));
+  }
+
+  const uint16_t* kc = (const uint16_t*)a.kc;
+  const uint16_t* vc = (const uint16_t*)a.vc;
+  const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
+  auto phys = [&](int32_t t) -> int64_t {
+    int32_t e = trow[t / P];
+    if ((uint32_t)e >= (uint32_t)a.num_blocks) {
+      atomicOr(a.err, PKV_DEVERR_TABLE_ENTRY);
+      e = 0;
+    }
+    return e;
+  };
+
+  // cooperative chunk staging: key rows and value-tile runs, 16-byte pieces
+  uint4 stage[PER];
+  auto gload = [&](int32_t c0) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int p = threadIdx.x + u * NT;
+      uint4 x = uint4{0, 0, 0, 0};
+      if (p < KP) {
+        const int key = p / (D / 8), dc = p % (D / 8);
+        const int32_t t = min(c0 + key, kend - 1);
+        x = load16(kc + (phys(t) * a.hkv + g) * P * D + (int64_t)(t % P) * D + dc * 8);
+      } else if (p < KP + VP) {
+        const int pp = p - KP;
+        const int dim = pp / (CH / 8), qq = pp % (CH / 8);
+        const int32_t t0 = c0 + 8 * qq;                       // 8 keys inside one block (P % 8 == 0)
+        const int32_t t = min(t0, (kend - 1) & ~7);
+        x = load16(vc + (phys(t) * a.hkv + g) * D * P + (int64_t)dim * P + (t % P));
+        // keys at or past the context end: zero, so unused slots cannot leak
+        const int32_t nv = t0 >= kend ? 0 : min(kend - t0, 8);
+        if (nv < 8) {
+          const uint32_t m0 = nv >= 2 ? 0xffffffffu : (nv == 1 ? 0x0000ffffu : 0u);
+          const uint32_t m1 = nv >= 4 ? 0xffffffffu : (nv == 3 ? 0x0000ffffu : 0u);
+          const uint32_t m2 = nv >= 6 ? 0xffffffffu : (nv == 5 ? 0x0000ffffu : 0u);
+          const uint32_t m3 = nv >= 8 ? 0xffffffffu : (nv == 7 ? 0x0000ffffu : 0u);
+          x.x &= m0;
+          x.y &= m1;
+          x.z &= m2;
+          x.w &= m3;
+        }
+      }
+      stage[u] = x;
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int p = threadIdx.x + u * NT;
+      if (p < KP) {
+        const int key = p / (D / 8), dc = p % (D / 8);
+        *reinterpret_cast<uint4*>(&k_lds[buf][key * KS + dc * 8]) = stage[u];
+      } else if (p < KP + VP) {
+        const int pp = p - KP;
+        const int dim = pp / (CH / 8), qq = pp % (CH / 8);
+        *reinterpret_cast<uint4*>(&v_lds[buf][dim * VS + qq * 8]) = stage[u];
+      }
+    }
+  };
+
+  f32x4 acc[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const int krow_x = 8 * (nq >> 2) + (nq & 3);  // key of chain-X row nq within the chunk
+  const int32_t wave_qpos0 = base + wq0;        // smallest query position of the wave
+
+  auto compute = [&](int buf, int32_t c0) {
+    const uint16_t* kl = k_lds[buf];
+    const uint16_t* vl = v_lds[buf];
+    f32x4 sx = {0.f, 0.f, 0.f, 0.f}, sy = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const bf16x8 ax = *reinterpret_cast<const bf16x8*>(&kl[krow_x * KS + 32 * i + 8 * r]);
+      const bf16x8 ay = *reinterpret_cast<const bf16x8*>(&kl[(krow_x + 4) * KS + 32 * i + 8 * r]);
+      sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, qf[i], sx, 0, 0, 0);
+      sy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ay, qf[i], sy, 0, 0, 0);
+    }
+    float s[8] = {sx[0], sx[1], sx[2], sx[3], sy[0], sy[1], sy[2], sy[3]};
+    if (c0 + CH - 1 > wave_qpos0) {  // uniform: the chunk reaches past some query's position
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[e] = c0 + 8 * r + e <= qpos ? s[e] : -INFINITY;
+    }
+    float cm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                     fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+    cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+    const float m_new = fmaxf(m_run, cm);  // finite: key 0 is in the first chunk of every query
+    const float alpha = fast_exp2((m_run - m_new) * c);
+    const float mc = m_new * c;
+    bf16x8 pb;
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const __bf16 x = (__bf16)fast_exp2(fmaf(s[e], c, -mc));
+      pb[e] = x;
+      psum += (float)x;
+    }
+    l_run = fmaf(l_run, alpha, psum);
+    m_run = m_new;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(&vl[(16 * j + nq) * VS + 8 * r]);
+      acc[j] *= alpha;
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, acc[j], 0, 0, 0);
+    }
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int32_t ci = 0; ci < nchunks; ++ci) {
+    const int32_t c0 = ci * CH;
+    const bool more = ci + 1 < nchunks;  // uniform
+    if (more) gload(c0 + CH);
+    if (c0 < wave_kend) compute(ci & 1, c0);  // uniform over the wave
+    if (more) lstore((ci + 1) & 1);
+    __syncthreads();
+  }
+
+  // totals over the four row groups, then the output rows of this lane's query
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  if (!q_ok) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  uint16_t* orow = (uint16_t*)a.out + ((int64_t)(q0 + qi) * a.hq + head) * D + 4 * r;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const __bf16 o0 = (__bf16)(acc[j][0] * inv), o1 = (__bf16)(acc[j][1] * inv);
+    const __bf16 o2 = (__bf16)(acc[j][2] * inv), o3 = (__bf16)(acc[j][3] * inv);
+    uint2 wv;
+    wv.x = (uint32_t)__builtin_bit_cast(uint16_t, o0) | ((uint32_t)__builtin_bit_cast(uint16_t, o1) << 16);
+    wv.y = (uint32_t)__builtin_bit_cast(uint16_t, o2) | ((uint32_t)__builtin_bit_cast(uint16_t, o3) << 16);
+    *reinterpret_cast<uint2*>(orow + 16 * j) = wv;
+  }
+}
+
+template <int D, int G>
+void launch_prefill_g(const PrefillArgs& a, int32_t max_q, hipStream_t st) {
+  constexpr int BT = G >= 4 ? 16 : 64 / G;
+  constexpr int NT = 64 * G * BT / 16;
+  const dim3 grid((unsigned)((max_q + BT - 1) / BT), (unsigned)a.n_seqs, (unsigned)a.hkv);
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, G, BT>), grid, dim3(NT), 0, st, a);
+}
+
+template <int D>
+void launch_prefill(const PrefillArgs& a, int32_t max_q, hipStream_t st) {
+  switch (a.hq / a.hkv) {
+    case 1: launch_prefill_g<D, 1>(a, max_q, st); break;
+    case 2: launch_prefill_g<D, 2>(a, max_q, st); break;
+    case 4: launch_prefill_g<D, 4>(a, max_q, st); break;
+    case 8: launch_prefill_g<D, 8>(a, max_q, st); break;
+    default: launch_prefill_g<D, 16>(a, max_q, st); break;
+  }
+}
+
+}  // namespace
+}  // namespace pkv
+
+using pkv::fail;
+
+extern "C" int pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
+                                           const void* v_cache, const int32_t* d_block_table,
+                                           const int32_t* d_context_lens,
+                                           const int32_t* d_query_start, int32_t n_seqs,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int32_t num_blocks, int32_t max_blocks_per_seq,
+                                           int32_t max_query_len, float scale, pkv_dtype dtype,
+                                           void* stream) {
+  PKV_TRY_BEGIN
+  if (n_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_blocks <= 0 || max_blocks_per_seq < 0 || max_query_len < 0)
+    return fail(PKV_ERR_INVALID_ARG, "bad sizes");
+  if (num_q_heads % num_kv_heads) return fail(PKV_ERR_INVALID_ARG, "num_q_heads % num_kv_heads != 0");
+  if (!pkv::dtype_valid(dtype)) return fail(PKV_ERR_INVALID_ARG, "bad dtype");
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(PKV_ERR_INVALID_ARG, "scale must be finite and positive");
+  const int32_t G = num_q_heads / num_kv_heads;
+  if (dtype != PKV_BF16 || (head_dim != 64 && head_dim != 128) || block_size % 8 != 0 ||
+      (G != 1 && G != 2 && G != 4 && G != 8 && G != 16))
+    return fail(PKV_ERR_UNSUPPORTED,
+                "prefill needs bf16, head_dim 64/128, block_size a multiple of 8, G in {1,2,4,8,16}");
+  if (n_seqs > 65535 || num_kv_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
+  if (n_seqs == 0 || max_query_len == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !d_context_lens || !d_query_start || !d_block_table)
+    return fail(PKV_ERR_INVALID_ARG, "NULL pointer");
+  const uintptr_t mis = (uintptr_t)out | (uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache;
+  if (mis % 16) return fail(PKV_ERR_UNSUPPORTED, "prefill needs 16-byte aligned buffers");
+  int32_t* err = nullptr;
+  int rc = pkv::device_error_word(&err);
+  if (rc) return rc;
+  pkv::PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.table = d_block_table;
+  a.ctx = d_context_lens;
+  a.qstart = d_query_start;
+  a.n_seqs = n_seqs;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.p = block_size;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.err = err;
+  hipStream_t st = (hipStream_t)stream;
+  if (head_dim == 128) pkv::launch_prefill<128>(a, max_query_len, st);
+  else pkv::launch_prefill<64>(a, max_query_len, st);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+  PKV_TRY_END
+}

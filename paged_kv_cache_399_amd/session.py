@@ -18,7 +18,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 from . import (BlockPool, cache_append, copy_blocks, decode_workspace_bytes,
-               paged_attention_decode)
+               paged_attention_decode, paged_attention_prefill)
 
 
 def _poison_value(dtype):
@@ -133,6 +133,33 @@ class PagedKVCache:
         # with it the summation order) is fixed for the life of the batch
         return paged_attention_decode(out, q, self.k_cache, self.v_cache, m.table, m.lens,
                                       m.ws_max_len, m.ws_total, scale, m.workspace, stream)
+
+    def extend(self, m, n_new, k_new, v_new, q, out, scale=None, stream=None):
+        """Append n_new[i] tokens to m.seqs[i] and attend causally from each of them.
+
+        Rows of k_new / v_new / q / out are the new tokens, sequence by
+        sequence in m.seqs order.  Slots on the host, copy-on-write copies,
+        table / length / slot upload, cache_append, then prefill attention.
+        """
+        import torch
+        n_new = np.asarray(n_new, dtype=np.int32)
+        slots, cow = self.pool.append_slots(m.seqs, n_new)
+        if len(cow):
+            copy_blocks(self.k_cache, self.v_cache, cow, stream)
+        if m.slots.numel() < max(len(slots), 1):
+            m.slots = torch.empty(len(slots), dtype=torch.int32, device=self.device)
+        m.max_len, m.total = self.pool.block_table_upload(m.seqs, m.max_blocks, m.table, m.lens,
+                                                          slots, m.slots, stream,
+                                                          incremental=m.uploaded)
+        m.uploaded = True
+        if len(slots):
+            cache_append(self.k_cache, self.v_cache, k_new, v_new, m.slots, stream)
+        qs = np.zeros(len(n_new) + 1, dtype=np.int32)
+        qs[1:] = np.cumsum(n_new)
+        m.query_start = torch.from_numpy(qs).to(self.device)
+        return paged_attention_prefill(out, q, self.k_cache, self.v_cache, m.table, m.lens,
+                                       m.query_start, int(n_new.max()) if len(n_new) else 0,
+                                       scale, stream)
 
     def close(self):
         self.pool.close()

@@ -48,6 +48,7 @@ __all__ = [
     "DecodeConfig", "CONFIGS", "stream_seed", "context_lengths", "pool_size",
     "free_order", "Workload", "make_workload", "bf16_bits", "to_numpy_f32",
     "BeamConfig", "BEAM_CONFIGS", "BeamWorkload", "make_beam_workload",
+    "PrefillConfig", "PREFILL_CONFIGS", "PrefillWorkload", "make_prefill_workload",
 ]
 
 
@@ -308,3 +309,54 @@ def make_beam_workload(cfg: BeamConfig, seed: int = 0, device="cpu",
     return BeamWorkload(cfg, seed, plen, nb, order, draw((b, hq, d), "q"),
                         draw((int(cu[-1]), hkv, d), "k"), draw((int(cu[-1]), hkv, d), "v"), cu,
                         draw((steps, b, hkv, d), "step_k"), draw((steps, b, hkv, d), "step_v"))
+
+
+# --------------------------------------------------------------------------
+# Prefill (appended chunk) workloads
+# --------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class PrefillConfig:
+    """``batch`` sequences holding ``context`` tokens each receive ``new`` more."""
+    name: str
+    batch: int
+    context: int
+    new: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    dtype: str = "bf16"
+    value_dist: str = "normal"
+
+
+PREFILL_CONFIGS: Dict[str, PrefillConfig] = {
+    # whole prompts: 16 fresh sequences of 2048 tokens, Llama-3-8B-like heads
+    "prefill": PrefillConfig("prefill", 16, 0, 2048, 32, 8, 128, 16),
+    # chunked prefill: 32 sequences holding 4096 tokens append 512 more
+    "prefill_chunk": PrefillConfig("prefill_chunk", 32, 4096, 512, 32, 8, 128, 16),
+}
+
+
+@dataclasses.dataclass
+class PrefillWorkload:
+    cfg: PrefillConfig
+    seed: int
+    num_blocks: int
+    free_order: np.ndarray
+    ctx_k: object      # torch [batch * context, Hkv, D], sequence-major
+    ctx_v: object
+    new_k: object      # torch [batch * new, Hkv, D]
+    new_v: object
+    q: object          # torch [batch * new, Hq, D]
+
+
+def make_prefill_workload(cfg: PrefillConfig, seed: int = 0, device="cpu") -> PrefillWorkload:
+    p = cfg.block_size
+    nb = int(math.ceil(1.25 * cfg.batch * _pages(cfg.context + cfg.new, p)))
+    hq, hkv, d = cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+    draw = lambda shape, stream: _draw(cfg, shape, seed, stream, device)  # noqa: E731
+    b = cfg.batch
+    return PrefillWorkload(cfg, seed, nb, free_order(nb, seed),
+                           draw((b * cfg.context, hkv, d), "k"), draw((b * cfg.context, hkv, d), "v"),
+                           draw((b * cfg.new, hkv, d), "new_k"), draw((b * cfg.new, hkv, d), "new_v"),
+                           draw((b * cfg.new, hq, d), "q"))
