@@ -33,6 +33,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="long", help="tiny|small_mha|gqa|long|prefix|beam|prefill|prefill_chunk")
     ap.add_argument("--block-size", type=int, default=None)
+    ap.add_argument("--sweep-block-sizes", default="",
+                    help="comma-separated block sizes: one decode JSON line per size (block-size study)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the CPU oracle baseline (0 = skip)")
@@ -269,10 +271,28 @@ def main():
     from synth import PREFILL_CONFIGS
     if args.config in PREFILL_CONFIGS:
         return run_prefill(args)
-
     cfg = CONFIGS[args.config]
+    if args.sweep_block_sizes:
+        # one line per block size, same schema, no CPU baseline; each size in
+        # a fresh child process so allocator state does not carry over (this
+        # process never touches the GPU)
+        import subprocess
+        rc = 0
+        for p in [int(x) for x in args.sweep_block_sizes.split(",")]:
+            cmd = [sys.executable, os.path.abspath(__file__), "--config", args.config,
+                   "--block-size", str(p), "--steps", str(args.steps), "--warmup", str(args.warmup),
+                   "--seed", str(args.seed), "--no-cpu-baseline"]
+            rc = rc or subprocess.run(cmd).returncode
+        sys.exit(rc)
     if args.block_size:
         cfg = cfg.with_block_size(args.block_size)
+    print(json.dumps(run_decode(args, cfg, cpu=True)), flush=True)
+
+
+def run_decode(args, cfg, cpu):
+    import torch
+    from synth import make_workload
+    from paged_kv_cache_399_amd.session import PagedKVCache
     dev = "cuda:0"
     torch.cuda.set_device(0)
     nsteps = args.warmup + args.steps
@@ -322,9 +342,12 @@ def main():
         del src, dst
     stream = torch.cuda.current_stream()
     frag = []
+    host_s = [0.0]
 
     def step(i):
+        h0 = time.perf_counter()
         kv.append_decode_tokens(meta, w.step_k[i], w.step_v[i], stream)
+        host_s[0] += time.perf_counter() - h0
         kv.attend(meta, w.q, out, stream=stream)
         frag.append(kv.pool.stats()["fragmentation"])
 
@@ -336,6 +359,7 @@ def main():
     # events inside the loop so nothing is added between the step's launches
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    host_s[0] = 0.0
     t0 = time.perf_counter()
     s0.record(stream)
     for i in range(args.steps):
@@ -403,6 +427,7 @@ def main():
         "gpu_ms_per_step": round(gpu_ms_step, 4),
         "decode_bytes_per_step": int(dbytes),
         "block_table_bytes_read": table_bytes,
+        "append_host_ms_per_step": round(host_s[0] * 1e3 / args.steps, 4),
         **extra,
         "fragmentation": round(float(np.mean(frag)), 6),
         "cache_append_prefill": {"tokens": int(priv.sum()), "ms": round(prefill_ms, 3),
@@ -414,9 +439,9 @@ def main():
     }
     if args.check:
         result["check_max_err"] = check_sample(w, kv, meta, out, cfg)
-    if not args.no_cpu_baseline and args.cpu_seconds > 0:
+    if cpu and not args.no_cpu_baseline and args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(w, cfg, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+    return result
 
 
 def check_sample(w, kv, meta, out, cfg):

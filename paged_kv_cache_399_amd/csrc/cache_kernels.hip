@@ -63,14 +63,18 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
 // Bulk appends (a prefill writes whole blocks).  Workgroup w takes the token
 // rows [w kWin, w kWin + kWin) and finds the runs of P rows whose slots fill
 // one whole block in order (a run starts at a row whose slot is a multiple of
-// P).  A run's key tile is a straight copy and its value tile is transposed
-// through LDS and written as full rows of P tokens, so HBM sees whole-sector
-// writes instead of one 2- or 4-byte write per value element.  Rows outside
-// runs (partial blocks, runs cut by the window edge, skipped or bad slots) are
-// copied element by element.  Runs write disjoint blocks, so the order in
-// which a workgroup takes them does not matter.
+// P).  A window owns every run that starts inside it, also one that reaches
+// up to P - 1 rows past its end, so window edges cut no run; rows covered by
+// a run the previous window owns are left to that window.  A run's key tile
+// is a straight copy and its value tile is transposed through LDS and written
+// as full rows of P tokens, so HBM sees whole-sector writes instead of one 2-
+// or 4-byte write per value element.  Rows outside runs (partial blocks,
+// skipped or bad slots) are copied element by element.  Runs write disjoint
+// blocks, so the order in which a workgroup takes them does not matter.
 constexpr int kTileLdsBytes = 32768;
 constexpr int kWin = 256;
+constexpr int kTileMaxBlock = 256;            // longest block the tile path takes
+constexpr int kHalo = kTileMaxBlock - 1;      // rows a window looks past either edge
 
 template <typename E>
 __global__ __launch_bounds__(256) void cache_append_tiles_kernel(
@@ -78,41 +82,46 @@ __global__ __launch_bounds__(256) void cache_append_tiles_kernel(
     const int32_t* __restrict__ slots, int32_t n_tokens, int64_t num_slots, int32_t hkv,
     int32_t d, int32_t p, int32_t* __restrict__ err) {
   __shared__ uint4 lds_raw[kTileLdsBytes / 16];
-  __shared__ int32_t ws[kWin], run_start[kWin], loose[kWin];
-  __shared__ int32_t covered[kWin];
+  __shared__ int32_t ws[kWin + 2 * kHalo];        // slots of rows [lo, hi)
+  __shared__ uint8_t covered[kWin + 2 * kHalo];
+  __shared__ int32_t run_start[kWin], loose[kWin];  // rows relative to the window start
   __shared__ int32_t n_runs, n_loose;
-  E* tile = reinterpret_cast<E*>(lds_raw);
   constexpr int V = 16 / sizeof(E);  // elements per 16-byte chunk
   const int32_t hd = hkv * d;
   const int32_t tid = threadIdx.x, nth = blockDim.x;
   const int32_t n_win = (n_tokens + kWin - 1) / kWin;
   for (int32_t wdx = blockIdx.x; wdx < n_win; wdx += gridDim.x) {
     const int32_t i0 = wdx * kWin, cnt = min(kWin, n_tokens - i0);
-    for (int32_t t = tid; t < kWin; t += nth) {
-      ws[t] = t < cnt ? slots[i0 + t] : -1;
-      covered[t] = 0;
+    const int32_t lo = max(0, i0 - (p - 1)), hi = min(n_tokens, i0 + cnt + (p - 1));
+    const int32_t ext = hi - lo, base = i0 - lo;  // window row t is ws[base + t]
+    for (int32_t x = tid; x < ext; x += nth) {
+      ws[x] = slots[lo + x];
+      covered[x] = 0;
     }
     if (tid == 0) {
       n_runs = 0;
       n_loose = 0;
     }
     __syncthreads();
-    for (int32_t t = tid; t < cnt; t += nth) {
-      const int32_t s0 = ws[t];
-      bool ok = s0 >= 0 && s0 % p == 0 && t + p <= cnt && (int64_t)s0 + p <= num_slots;
-      for (int32_t j = 1; ok && j < p; ++j) ok = ws[t + j] == s0 + j;
-      if (ok) run_start[atomicAdd(&n_runs, 1)] = t;
+    // runs starting in [lo, i0 + cnt): all mark their rows, the ones starting
+    // at or after i0 are this window's
+    for (int32_t x = tid; x < base + cnt; x += nth) {
+      const int32_t s0 = ws[x];
+      bool ok = s0 >= 0 && s0 % p == 0 && x + p <= ext && (int64_t)s0 + p <= num_slots;
+      for (int32_t j = 1; ok && j < p; ++j) ok = ws[x + j] == s0 + j;
+      if (ok) {
+        for (int32_t j = 0; j < p; ++j) covered[x + j] = 1;
+        if (x >= base) run_start[atomicAdd(&n_runs, 1)] = x - base;
+      }
     }
     __syncthreads();
-    for (int32_t c = tid; c < n_runs * p; c += nth) covered[run_start[c / p] + c % p] = 1;
-    __syncthreads();
     for (int32_t t = tid; t < cnt; t += nth)
-      if (!covered[t] && ws[t] >= 0) loose[atomicAdd(&n_loose, 1)] = t;
+      if (!covered[base + t] && ws[base + t] >= 0) loose[atomicAdd(&n_loose, 1)] = t;
     __syncthreads();
     // rows outside runs, element by element
     for (int32_t e = tid; e < n_loose * hd; e += nth) {
       const int32_t q = e / hd, r = e - q * hd;
-      const int32_t row = loose[q], sl = ws[row];
+      const int32_t row = loose[q], sl = ws[base + row];
       if (sl < 0) continue;
       if ((int64_t)sl >= num_slots) {
         if (r == 0) atomicOr(err, PKV_DEVERR_SLOT);
@@ -123,14 +132,19 @@ __global__ __launch_bounds__(256) void cache_append_tiles_kernel(
       kc[((blk * hkv + h) * p + off) * d + dd] = kn[(int64_t)(i0 + row) * hd + r];
       vc[((blk * hkv + h) * d + dd) * p + off] = vn[(int64_t)(i0 + row) * hd + r];
     }
-    // whole-block runs
+    // whole-block runs.  The value tile sits in LDS with token rows of
+    // d elements plus one 4-byte word: the transposed reads walk a column,
+    // and without the pad the lanes of one column (rows 256 bytes apart for
+    // head_dim 128 in bf16) would all hit one bank.
     const int32_t dv = d / V, pv = p / V;
     const int32_t per = p * dv;                             // 16-byte chunks per head tile
-    const int32_t hb = max(1, (kTileLdsBytes / 16) / per);  // heads per LDS pass
+    const int32_t rw = d * (int32_t)sizeof(E) / 4 + 1;      // LDS words per token row
+    const int32_t hb = max(1, (kTileLdsBytes / 4) / (p * rw));  // heads per LDS pass
+    uint32_t* tile_w = reinterpret_cast<uint32_t*>(lds_raw);
     const int32_t nr = n_runs;
     for (int32_t ri = 0; ri < nr; ++ri) {
       const int32_t t0 = run_start[ri];
-      const int64_t blk = ws[t0] / p;
+      const int64_t blk = ws[base + t0] / p;
       const int64_t row0 = i0 + t0;
       for (int32_t h0 = 0; h0 < hkv; h0 += hb) {
         const int32_t nh = min(hb, hkv - h0);
@@ -139,16 +153,22 @@ __global__ __launch_bounds__(256) void cache_append_tiles_kernel(
           const int64_t src = (row0 + j) * hd + (h0 + hh) * d;
           reinterpret_cast<uint4*>(kc + (blk * hkv + h0 + hh) * p * d)[r] =
               reinterpret_cast<const uint4*>(kn + src)[x];
-          lds_raw[c] = reinterpret_cast<const uint4*>(vn + src)[x];
+          const uint4 vv = reinterpret_cast<const uint4*>(vn + src)[x];
+          uint32_t* dst = tile_w + (hh * p + j) * rw + 4 * x;
+          dst[0] = vv.x;
+          dst[1] = vv.y;
+          dst[2] = vv.z;
+          dst[3] = vv.w;
         }
         __syncthreads();
         const int32_t outc = d * pv;                        // 16-byte chunks per transposed tile
         for (int32_t c = tid; c < nh * outc; c += nth) {
           const int32_t hh = c / outc, r = c - hh * outc, dd = r / pv, j0 = (r - dd * pv) * V;
-          const E* srct = tile + (int64_t)hh * p * d;
+          const E* srct = reinterpret_cast<const E*>(tile_w + hh * p * rw);
+          const int32_t es = rw * 4 / (int32_t)sizeof(E);   // elements per padded row (bf16: 2 rw)
           E chunk[V];
 #pragma unroll
-          for (int k = 0; k < V; ++k) chunk[k] = srct[(j0 + k) * d + dd];
+          for (int k = 0; k < V; ++k) chunk[k] = srct[(j0 + k) * es + dd];
           reinterpret_cast<uint4*>(vc + (blk * hkv + h0 + hh) * d * p)[r] =
               *reinterpret_cast<const uint4*>(chunk);
         }
@@ -261,8 +281,9 @@ extern "C" int pkv_cache_append(void* k_cache, void* v_cache, const void* k_new,
                          ((uintptr_t)k_cache % 16 == 0) && ((uintptr_t)k_new % 16 == 0);
   hipStream_t st = (hipStream_t)stream;
   // whole-block tile path for bulk appends (every row and tile 16-byte aligned)
-  const size_t tile_bytes = (size_t)block_size * head_dim * es;
+  const size_t tile_bytes = (size_t)block_size * (head_dim * es + 4);  // padded LDS rows
   const bool tiles_fit = vec_ok && ((size_t)block_size * es) % 16 == 0 &&
+                         block_size <= pkv::kTileMaxBlock &&
                          tile_bytes <= (size_t)pkv::kTileLdsBytes && (uintptr_t)v_cache % 16 == 0 &&
                          (uintptr_t)v_new % 16 == 0;
   const char* mode = std::getenv("PKV_APPEND_TILES");

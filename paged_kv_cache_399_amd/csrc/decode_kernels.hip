@@ -106,6 +106,18 @@ __device__ __forceinline__ uint4 load_stream16(const uint16_t* p) {
   return uint4{v.x, v.y, v.z, v.w};
 }
 
+__device__ __forceinline__ uint2 load_stream8(const uint16_t* p) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return uint2{v.x, v.y};
+}
+
+__device__ __forceinline__ uint32_t load_stream4(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
+__device__ __forceinline__ uint16_t load_stream2(const uint16_t* p) { return __builtin_nontemporal_load(p); }
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -278,9 +290,10 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int KI = Chunk::KI, NJ = Chunk::NJ;
   constexpr int CH = 32;     // tokens per chunk
   constexpr int DP = D + 4;  // padded LDS row of one head's accumulator
-  static_assert(P % 8 == 0 && (P <= CH ? CH % P == 0 : P % CH == 0), "block size");
+  static_assert((P < 8 || P % 8 == 0) && (P <= CH ? CH % P == 0 : P % CH == 0), "block size");
   __shared__ float red_o[W][16][DP];
   __shared__ float red_m[W][16], red_l[W][16];
+  __shared__ int32_t tab_lds[W][P < 8 ? 512 : 1];
 
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
@@ -320,20 +333,31 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
       }
     }
     const int32_t* trow = a.table + (int64_t)u.b * a.max_blocks;
-    // block-table window: lane i holds the entry of logical block wb + i
+    // Block-table window of 64 KW blocks, entry wb + 64 k + i read by lane i.
+    // Blocks of 8 tokens or more: one register (KW = 1), picked with uniform
+    // lane reads.  Shorter blocks: KW = 8 / P entries per lane, so a window
+    // still covers 512 tokens, kept in this wave's own LDS rows (written and
+    // read by this wave only; its LDS operations complete in order).
+    constexpr int KW = P < 8 ? 8 / P : 1;
     const int32_t last_blk = (s1 - 1) / P;
-    auto load_window = [&](int32_t base) -> int32_t {
-      int32_t e = 0;
-      if (base + lane <= last_blk) {
-        e = trow[base + lane];
-        if ((uint32_t)e >= (uint32_t)a.num_blocks) {
-          atomicOr(a.err, PKV_DEVERR_TABLE_ENTRY);
-          e = 0;
+    int32_t* tab_row = tab_lds[w];
+    int32_t tabv = 0;
+    auto load_window = [&](int32_t base) {
+#pragma unroll
+      for (int k = 0; k < KW; ++k) {
+        int32_t e = 0;
+        if (base + 64 * k + lane <= last_blk) {
+          e = trow[base + 64 * k + lane];
+          if ((uint32_t)e >= (uint32_t)a.num_blocks) {
+            atomicOr(a.err, PKV_DEVERR_TABLE_ENTRY);
+            e = 0;
+          }
         }
+        if constexpr (P >= 8) tabv = e;
+        else tab_row[64 * k + lane] = e;
       }
-      return e;
     };
-    int32_t wb = 0, tabv = 0, wlast = 0;
+    int32_t wb = 0, wlast = 0;
     const int32_t krow_x = 8 * (n >> 2) + (n & 3);  // token of chain-X row n within the chunk
 
     // Loads of one chunk; addresses are clamped to the window's last token.
@@ -341,35 +365,100 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
     // with uniform lane reads and each lane picks its own.
     constexpr int NBC = CH / P > 1 ? CH / P : 1;
     auto issue = [&](Chunk& f, int32_t c0) {
-      const int32_t cb = min(c0, wlast) / P;  // uniform: the chunk's first block
-      int32_t bid[NBC];
-#pragma unroll
-      for (int k = 0; k < NBC; ++k) bid[k] = __builtin_amdgcn_readlane(tabv, min(cb + k - wb, 63));
-      auto pick = [&](int32_t t) -> int32_t {
-        const int32_t idx = t / P - cb;
-        int32_t v = bid[0];
-#pragma unroll
-        for (int k = 1; k < NBC; ++k) v = idx == k ? bid[k] : v;
-        return v;
-      };
       const int32_t tx = min(c0 + krow_x, wlast);
       const int32_t ty = min(c0 + krow_x + 4, wlast);
-      // rows tx and ty (tx + 4 unless clamped) lie in one block: P >= 8
-      const int32_t pk = pick(tx);
-      const uint16_t* kb = kc + (int64_t)pk * blk_stride + head_off + 8 * r;
-      const uint16_t* kxp = kb + (tx % P) * D;
-      const uint16_t* kyp = kb + (ty % P) * D;
+      if constexpr (P >= 8) {
+        const int32_t cb = min(c0, wlast) / P;  // uniform: the chunk's first block
+        int32_t bid[NBC];
+        if constexpr (NBC <= 2) {
 #pragma unroll
-      for (int i = 0; i < KI; ++i) {
-        f.kx[i] = load_stream16(kxp + 32 * i);
-        f.ky[i] = load_stream16(kyp + 32 * i);
+          for (int k = 0; k < NBC; ++k) bid[k] = __builtin_amdgcn_readlane(tabv, min(cb + k - wb, 63));
+        }
+        auto pick = [&](int32_t t) -> int32_t {
+          if constexpr (NBC > 2) {
+            // more than two blocks per chunk: a lane permute of the window
+            return __builtin_amdgcn_ds_bpermute((t / P - wb) << 2, tabv);
+          } else {
+            const int32_t idx = t / P - cb;
+            int32_t v = bid[0];
+#pragma unroll
+            for (int k = 1; k < NBC; ++k) v = idx == k ? bid[k] : v;
+            return v;
+          }
+        };
+        // rows tx and ty (tx + 4 unless clamped) lie in one block: P >= 8
+        const int32_t pk = pick(tx);
+        const uint16_t* kb = kc + (int64_t)pk * blk_stride + head_off + 8 * r;
+        const uint16_t* kxp = kb + (tx % P) * D;
+        const uint16_t* kyp = kb + (ty % P) * D;
+#pragma unroll
+        for (int i = 0; i < KI; ++i) {
+          f.kx[i] = load_stream16(kxp + 32 * i);
+          f.ky[i] = load_stream16(kyp + 32 * i);
+        }
+        // values: tokens c0 + 8 r .. +7 of head_dim rows 16 j + n
+        const int32_t tv = min(c0 + 8 * r, wlast);
+        const int32_t pv = pick(tv);
+        const uint16_t* vb = vc + (int64_t)pv * blk_stride + head_off + (int64_t)n * P + ((tv % P) & ~7);
+        if constexpr (P > CH) {
+          // A value row of one dim spans several chunks: the chunks before
+          // the row's last use cached loads, so the next one finds the rest
+          // of the line in L2; the last reader streams (uniform branch).
+          if ((min(c0, wlast) % P) < P - CH) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) f.v[j] = *reinterpret_cast<const uint4*>(vb + 16 * j * P);
+          } else {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) f.v[j] = load_stream16(vb + 16 * j * P);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) f.v[j] = load_stream16(vb + 16 * j * P);
+        }
+      } else {
+        // Blocks of fewer than 8 tokens: each lane reads its entries from the
+        // wave's LDS window
+        auto pick = [&](int32_t t) -> int32_t { return tab_row[t / P - wb]; };
+        const uint16_t* kxp = kc + (int64_t)pick(tx) * blk_stride + head_off + 8 * r + (tx % P) * D;
+        const uint16_t* kyp = kc + (int64_t)pick(ty) * blk_stride + head_off + 8 * r + (ty % P) * D;
+#pragma unroll
+        for (int i = 0; i < KI; ++i) {
+          f.kx[i] = load_stream16(kxp + 32 * i);
+          f.ky[i] = load_stream16(kyp + 32 * i);
+        }
+        // values: tokens c0 + 8 r .. +7 of head_dim rows 16 j + n, as 8 / P
+        // runs of P tokens (2 P bytes) from as many blocks; each run starts a
+        // block, clamped to the block of the window's last token
+        constexpr int NPC = 8 / P;
+        const int32_t vlast_blk = wlast - wlast % P;
+        const uint16_t* vp[NPC];
+#pragma unroll
+        for (int pi = 0; pi < NPC; ++pi) {
+          const int32_t t = min(c0 + 8 * r + pi * P, vlast_blk);
+          vp[pi] = vc + (int64_t)pick(t) * blk_stride + head_off + (int64_t)n * P;
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          uint32_t wv[4];
+          if constexpr (P == 4) {
+#pragma unroll
+            for (int pi = 0; pi < 2; ++pi) {
+              const uint2 x = load_stream8(vp[pi] + 16 * j * P);
+              wv[2 * pi] = x.x;
+              wv[2 * pi + 1] = x.y;
+            }
+          } else if constexpr (P == 2) {
+#pragma unroll
+            for (int pi = 0; pi < 4; ++pi) wv[pi] = load_stream4(vp[pi] + 16 * j * P);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              wv[e] = (uint32_t)load_stream2(vp[2 * e] + 16 * j) |
+                      ((uint32_t)load_stream2(vp[2 * e + 1] + 16 * j) << 16);
+          }
+          f.v[j] = uint4{wv[0], wv[1], wv[2], wv[3]};
+        }
       }
-      // values: tokens c0 + 8 r .. +7 of head_dim rows 16 j + n
-      const int32_t tv = min(c0 + 8 * r, wlast);
-      const int32_t pv = pick(tv);
-      const uint16_t* vb = vc + (int64_t)pv * blk_stride + head_off + (int64_t)n * P + ((tv % P) & ~7);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) f.v[j] = load_stream16(vb + 16 * j * P);
     };
 
     auto compute = [&](Chunk& f, int32_t c0) {
@@ -428,9 +517,9 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
     // the prefetch past the window end reads clamped, in-bounds addresses.
     for (int32_t ws = s0; ws < s1;) {
       wb = uniform(ws / P);
-      const int32_t we = min(s1, (wb + 64) * P);
+      const int32_t we = min(s1, (wb + 64 * KW) * P);
       wlast = we - 1;
-      tabv = load_window(wb);
+      load_window(wb);
       Chunk f0, f1;
       int32_t c0 = ws;
       issue(f0, c0);
@@ -1041,7 +1130,8 @@ int math_mode() {
 
 bool mfma_shape_ok(int32_t hq, int32_t hkv, int32_t d, int32_t p, pkv_dtype dt) {
   const int32_t G = hq / hkv;
-  return dt == PKV_BF16 && (d == 64 || d == 128) && (p == 8 || p == 16 || p == 32) && G >= 1 && G <= 16;
+  return dt == PKV_BF16 && (d == 64 || d == 128) && (p == 1 || p == 2 || p == 4 || p == 8 || p == 16 || p == 32 || p == 64) &&
+         G >= 1 && G <= 16;
 }
 
 // DPP kernel: head_dim 64 / 128, head groups up to 4, block rows of whole
@@ -1061,7 +1151,7 @@ int choose(int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t p, int32_
   const bool dshape = dpp_shape_ok(hq, hkv, d, p, dt);
   int kind;
   if (mode == kMathMfma) {
-    if (!mshape) return fail(PKV_ERR_UNSUPPORTED, "matrix-core decode needs bf16, head_dim 64/128, block 8/16/32, G <= 16");
+    if (!mshape) return fail(PKV_ERR_UNSUPPORTED, "matrix-core decode needs bf16, head_dim 64/128, block size a power of two up to 64, G <= 16");
     kind = kKindMfma;
   } else if (mode == kMathDpp) {
     if (!dshape) return fail(PKV_ERR_UNSUPPORTED, "DPP decode needs head_dim 64/128, G <= 4, 16-byte block rows");
@@ -1145,6 +1235,19 @@ void launch_mfma(const DecodeArgs& a, int32_t waves_per_group, int64_t groups, h
     hipLaunchKernelGGL((decode_mfma_kernel<D, P, 8>), dim3((unsigned)groups), dim3(512), 0, st, a);
   else
     hipLaunchKernelGGL((decode_mfma_kernel<D, P, 4>), dim3((unsigned)groups), dim3(256), 0, st, a);
+}
+
+template <int D>
+void launch_mfma_p(const DecodeArgs& a, int32_t p, int32_t waves_per_group, int64_t groups, hipStream_t st) {
+  switch (p) {
+    case 1: launch_mfma<D, 1>(a, waves_per_group, groups, st); break;
+    case 2: launch_mfma<D, 2>(a, waves_per_group, groups, st); break;
+    case 4: launch_mfma<D, 4>(a, waves_per_group, groups, st); break;
+    case 8: launch_mfma<D, 8>(a, waves_per_group, groups, st); break;
+    case 16: launch_mfma<D, 16>(a, waves_per_group, groups, st); break;
+    case 32: launch_mfma<D, 32>(a, waves_per_group, groups, st); break;
+    default: launch_mfma<D, 64>(a, waves_per_group, groups, st); break;
+  }
 }
 
 template <typename T, int D>
@@ -1293,15 +1396,8 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   const int64_t waves = c.max_units * num_kv_heads;
   if (c.kind == pkv::kKindMfma) {
     const int32_t W = c.waves_per_group;
-    if (head_dim == 128) {
-      if (block_size == 8) pkv::launch_mfma<128, 8>(a, W, waves, st);
-      else if (block_size == 16) pkv::launch_mfma<128, 16>(a, W, waves, st);
-      else pkv::launch_mfma<128, 32>(a, W, waves, st);
-    } else {
-      if (block_size == 8) pkv::launch_mfma<64, 8>(a, W, waves, st);
-      else if (block_size == 16) pkv::launch_mfma<64, 16>(a, W, waves, st);
-      else pkv::launch_mfma<64, 32>(a, W, waves, st);
-    }
+    if (head_dim == 128) pkv::launch_mfma_p<128>(a, block_size, W, waves, st);
+    else pkv::launch_mfma_p<64>(a, block_size, W, waves, st);
   } else if (c.kind == pkv::kKindDpp) {
     if (dtype == PKV_BF16) pkv::launch_dpp<uint16_t>(a, waves, st);
     else pkv::launch_dpp<float>(a, waves, st);

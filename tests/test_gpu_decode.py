@@ -314,3 +314,32 @@ def test_long_partitions_span_several_table_windows(monkeypatch, part):
     case = build_case(cfg, seed=7)
     err = check_attention(case)
     say(f"  part={part}: max err {err:.3e}")
+
+
+@pytest.mark.parametrize("p", [1, 2, 4, 8, 16, 32, 64])
+@pytest.mark.parametrize("hq,hkv,d", [(16, 2, 128), (8, 4, 64)])
+@pytest.mark.parametrize("part", ["128", "auto"])
+def test_matrix_core_kernel_every_block_size(monkeypatch, p, hq, hkv, d, part):
+    """The matrix-core kernel for block sizes 1..64: below 8 tokens a value run
+    of 8 tokens spans several blocks, at 64 a block holds two chunks."""
+    monkeypatch.setenv("PKV_DECODE_MATH", "mfma")
+    if part != "auto":
+        monkeypatch.setenv("PKV_PARTITION_TOKENS", part)
+    cfg = DecodeConfig(f"mfma_p{p}_{hq}_{hkv}_{d}", len(EDGE_LENGTHS), hq, hkv, d, p, "bf16",
+                       "fixed", fixed_lengths=tuple(EDGE_LENGTHS))
+    case = build_case(cfg, seed=p)
+    err = check_attention(case)
+    say(f"  {cfg.name} part={part}: max err {err:.3e}")
+
+
+@pytest.mark.parametrize("p", [1, 2, 4, 64])
+def test_small_and_large_blocks_span_several_table_windows(monkeypatch, p):
+    """One wave walking many 512-token table windows (blocks under 8 tokens keep
+    the window in LDS) and, for 64-token blocks, 4096-token windows."""
+    monkeypatch.setenv("PKV_DECODE_MATH", "mfma")
+    monkeypatch.setenv("PKV_PARTITION_TOKENS", "16384")
+    cfg = DecodeConfig(f"windows_p{p}", 4, 16, 2, 128, p, "bf16", "fixed",
+                       fixed_lengths=(9000, 4097, 2049, 513))
+    case = build_case(cfg, seed=11)
+    err = check_attention(case)
+    say(f"  p={p}: max err {err:.3e}")
