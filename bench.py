@@ -31,7 +31,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="long", help="tiny|small_mha|gqa|long|prefix|beam|prefill|prefill_chunk")
+    ap.add_argument("--config", default="long", help="tiny|small_mha|gqa|long|prefix|beam|prefill|prefill_chunk|admission|admission_small")
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--sweep-block-sizes", default="",
                     help="comma-separated block sizes: one decode JSON line per size (block-size study)")
@@ -257,6 +257,55 @@ def run_prefill(args):
     print(json.dumps(result), flush=True)
 
 
+def run_admission(args):
+    """Replay a synthetic request trace under paged blocks and under up-front
+    reservation on the same KV slots (host only: the library's block pool)."""
+    from synth import ADMISSION_CONFIGS, make_admission_trace
+    from paged_kv_cache_399_amd import admission
+    cfg = ADMISSION_CONFIGS[args.config]
+    pr, ou, mx, fo = make_admission_trace(cfg, args.seed)
+    cap = cfg.num_blocks * cfg.block_size
+    t0 = time.perf_counter()
+    pg = admission.run_paged(cfg.num_blocks, cfg.block_size, pr, ou, fo)
+    t_paged = time.perf_counter() - t0
+    rs = admission.run_reserved(cap, pr, ou, mx)
+    sp, sr = pg.summary(), rs.summary()
+    result = {
+        "metric": "admission: mean sequences resident per step, paged blocks vs up-front reservation",
+        "value": round(sp["mean_running"], 2),
+        "unit": "sequences",
+        "n_gpus": 1, "steps": sp["steps"], "warmup": 0,
+        "ms_per_step": round(t_paged * 1e3 / max(sp["steps"], 1), 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int64", "data": "synthetic",
+        "config": {"workload": cfg.name, "requests": cfg.n_requests,
+                   "prompt": f"loguniform [{cfg.prompt_lo},{cfg.prompt_hi}]",
+                   "output": f"loguniform [{cfg.output_lo},{cfg.output_hi}]",
+                   "max_output": cfg.max_output, "num_blocks": cfg.num_blocks,
+                   "block_size": cfg.block_size, "kv_slots": cap, "seed": args.seed,
+                   "parallelism": "host only"},
+        "paged": sp,
+        "reserved": sr,
+        "resident_ratio": round(sp["mean_running"] / max(sr["mean_running"], 1e-9), 3),
+        "host_us_per_step_paged": round(t_paged * 1e6 / max(sp["steps"], 1), 1),
+        "roofline": None,
+    }
+    if not args.no_cpu_baseline and args.cpu_seconds > 0:
+        from oracle import admission as oad
+        n = 50
+        while True:
+            t0 = time.perf_counter()
+            oad.paged(cfg.num_blocks, cfg.block_size, pr, ou, fo, max_steps=n)
+            dt = time.perf_counter() - t0
+            if dt > args.cpu_seconds / 4 or n >= sp["steps"]:
+                break
+            n = min(sp["steps"], n * 4)
+        result["cpu_baseline"] = {"value": round(n / dt, 2), "unit": "steps/s", "cores": 1,
+                                  "kind": "oracle",
+                                  "sample": f"first {n} steps of the paged replay ({dt:.1f} s)"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -271,6 +320,9 @@ def main():
     from synth import PREFILL_CONFIGS
     if args.config in PREFILL_CONFIGS:
         return run_prefill(args)
+    from synth import ADMISSION_CONFIGS
+    if args.config in ADMISSION_CONFIGS:
+        return run_admission(args)
     cfg = CONFIGS[args.config]
     if args.sweep_block_sizes:
         # one line per block size, same schema, no CPU baseline; each size in

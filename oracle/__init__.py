@@ -16,6 +16,8 @@ Modules
                 tables, allocate-on-fill, fork / copy-on-write, release.
 ``layout``      slot arithmetic and the expected contents of the K and V
                 caches after tokens are written at their slots.
+``admission``   a synthetic request stream replayed step by step under paged
+                blocks (on ``pool_model``) and under up-front reservation.
 ``attention``   decode attention in float64 over each sequence's keys and
                 values in logical order, a pure-Python brute force for tiny
                 inputs, the partition-and-merge identity for split contexts,
@@ -39,7 +41,12 @@ routines.  Pins per function:
 * attention.prefill       brute force, torch scaled_dot_product_attention with an
                           explicit causal mask in float64, each row equal to
                           decode over the keys it sees, single-key rows.
+* admission.*             whole-batch closed forms for identical requests
+                          (reserved: cap // (prompt + limit) per wave; paged:
+                          requests of whole blocks), two traces worked by hand
+                          (one with preemptions), every output token generated
+                          once, waste under one block per resident sequence.
 """
-from . import accounting, attention, layout, pool_model  # noqa: F401
+from . import accounting, admission, attention, layout, pool_model  # noqa: F401
 from .pool_model import (PoolModel, PoolError, NoBlocks, BadSeq,  # noqa: F401
                          InvalidArg)

@@ -360,3 +360,46 @@ def make_prefill_workload(cfg: PrefillConfig, seed: int = 0, device="cpu") -> Pr
                            draw((b * cfg.context, hkv, d), "k"), draw((b * cfg.context, hkv, d), "v"),
                            draw((b * cfg.new, hkv, d), "new_k"), draw((b * cfg.new, hkv, d), "new_v"),
                            draw((b * cfg.new, hq, d), "q"))
+
+
+@dataclasses.dataclass(frozen=True)
+class AdmissionConfig:
+    """A stream of requests with log-uniform prompt and output lengths.
+
+    ``max_output`` is every request's declared output limit (what an up-front
+    reservation holds room for); the drawn output length never exceeds it.
+    The KV memory is ``num_blocks * block_size`` slots for both policies.
+    """
+    name: str
+    n_requests: int
+    prompt_lo: int
+    prompt_hi: int
+    output_lo: int
+    output_hi: int
+    max_output: int
+    num_blocks: int
+    block_size: int
+
+
+ADMISSION_CONFIGS: Dict[str, AdmissionConfig] = {
+    # 4096 requests, prompts and outputs log-uniform in [16, 1024], limit 2048,
+    # 2^18 KV slots (16384 blocks of 16 tokens)
+    "admission": AdmissionConfig("admission", 4096, 16, 1024, 16, 1024, 2048, 16384, 16),
+    # a small trace the pure-Python pool model replays in seconds
+    "admission_small": AdmissionConfig("admission_small", 300, 4, 200, 1, 200, 256, 512, 8),
+}
+
+
+def _loguniform_int(rng: np.random.Generator, lo: int, hi: int, n: int) -> np.ndarray:
+    out = np.floor(np.exp(rng.uniform(math.log(lo), math.log(hi + 1), size=n))).astype(np.int64)
+    return np.clip(out, lo, hi)
+
+
+def make_admission_trace(cfg: AdmissionConfig, seed: int = 0):
+    """(prompts, outputs, max_outputs, free_order) as int64 / int32 arrays."""
+    rng = _rng(seed, "admission")
+    prompts = _loguniform_int(rng, cfg.prompt_lo, cfg.prompt_hi, cfg.n_requests)
+    outputs = _loguniform_int(rng, cfg.output_lo, cfg.output_hi, cfg.n_requests)
+    outputs = np.minimum(outputs, cfg.max_output)
+    max_outputs = np.full(cfg.n_requests, cfg.max_output, dtype=np.int64)
+    return prompts, outputs, max_outputs, free_order(cfg.num_blocks, seed)
