@@ -33,6 +33,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="long", help="tiny|small_mha|gqa|long|prefix|beam|prefill|prefill_chunk|admission|admission_small")
     ap.add_argument("--block-size", type=int, default=None)
+    ap.add_argument("--layout", default="head_major", choices=["head_major", "token_major"],
+                    help="key cache order inside a block: [Hkv, P, D] or [P, Hkv, D]")
     ap.add_argument("--sweep-block-sizes", default="",
                     help="comma-separated block sizes: one decode JSON line per size (block-size study)")
     ap.add_argument("--seed", type=int, default=0)
@@ -333,7 +335,7 @@ def main():
         for p in [int(x) for x in args.sweep_block_sizes.split(",")]:
             cmd = [sys.executable, os.path.abspath(__file__), "--config", args.config,
                    "--block-size", str(p), "--steps", str(args.steps), "--warmup", str(args.warmup),
-                   "--seed", str(args.seed), "--no-cpu-baseline"]
+                   "--seed", str(args.seed), "--layout", args.layout, "--no-cpu-baseline"]
             rc = rc or subprocess.run(cmd).returncode
         sys.exit(rc)
     if args.block_size:
@@ -352,7 +354,8 @@ def run_decode(args, cfg, cpu):
     w = make_workload(cfg, args.seed, dev, extra_steps=nsteps)
     b, hq, hkv, d, p = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
     s = 2 if cfg.dtype == "bf16" else 4
-    kv = PagedKVCache(w.num_blocks, p, hkv, d, w.torch_dtype, dev, w.free_order, fill=0.0)
+    kv = PagedKVCache(w.num_blocks, p, hkv, d, w.torch_dtype, dev, w.free_order, fill=0.0,
+                      layout=args.layout)
     if cfg.prefix_len:
         root = kv.new_sequences(1)[0]
         kv.write([root], [cfg.prefix_len], w.prefix_k, w.prefix_v)
@@ -471,7 +474,7 @@ def run_decode(args, cfg, cpu):
             "head_dim": d, "block_size": p, "context_tokens": int(base.sum()),
             "max_context": int(base.max()), "seed": args.seed,
             "lengths": cfg.length_rule + (f" [{cfg.length_lo},{cfg.length_hi}]" if cfg.length_hi else ""),
-            "prefix_len": cfg.prefix_len, "parallelism": "single GPU",
+            "prefix_len": cfg.prefix_len, "k_layout": args.layout, "parallelism": "single GPU",
         },
         "decode_tokens_per_s": round(b / (ms_step * 1e-3), 1),
         "pct_of_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),

@@ -31,11 +31,16 @@
  *
  * Cache layout (the pages fix none; this library's choice):
  *   k_cache: [num_blocks, num_kv_heads, block_size, head_dim]   row-major
+ *            (PKV_LAYOUT_HEAD_MAJOR), or
+ *            [num_blocks, block_size, num_kv_heads, head_dim]   row-major
+ *            (PKV_LAYOUT_TOKEN_MAJOR: all heads of a token together)
  *   v_cache: [num_blocks, num_kv_heads, head_dim, block_size]   row-major
- *   i.e. each block stores its keys token-major and its values transposed
- *   (token-minor), so that the value product of decode attention reads
- *   contiguous runs of tokens.  Slot s = block (s / block_size), offset
- *   (s % block_size).
+ *   i.e. each block stores its keys as head_dim-contiguous rows and its values
+ *   transposed (token-minor), so that the value product of decode attention
+ *   reads contiguous runs of tokens of one head; the values keep that order in
+ *   both layouts.  A block is one contiguous run of num_kv_heads * block_size
+ *   * head_dim elements in each cache either way.  Slot s = block
+ *   (s / block_size), offset (s % block_size).
  *   q, out:          [n_seqs, num_q_heads, head_dim]
  *   k_new, v_new:    [n_tokens, num_kv_heads, head_dim]
  *   block table:     int32 [n_seqs, max_blocks_per_seq], unused entries -1
@@ -70,6 +75,9 @@ extern "C" {
 #define PKV_DEVERR_WORK_OVERFLOW 16/* more partitions than the workspace was sized */
 
 typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+/* Order of the key cache inside a block (see "Cache layout" above). */
+typedef enum { PKV_LAYOUT_HEAD_MAJOR = 0, PKV_LAYOUT_TOKEN_MAJOR = 1 } pkv_layout;
 
 typedef struct pkv_pool pkv_pool;
 
@@ -204,11 +212,13 @@ int pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t 
  * token goes into the current block ("Fixed-Size KV Blocks").  A negative
  * slot skips the token; a slot >= num_blocks * block_size is skipped and
  * flagged (PKV_DEVERR_SLOT).  Live slots must be distinct within one call.
- * Bit copy: no arithmetic on the values. */
+ * k_layout is the key cache's order (PKV_LAYOUT_*; any other value is
+ * INVALID_ARG); the decode and prefill calls that read the cache must pass
+ * the same one.  Bit copy: no arithmetic on the values. */
 int pkv_cache_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                      const int32_t* d_slot_mapping, int32_t n_tokens, int32_t num_blocks,
                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                     pkv_dtype dtype, void* stream);
+                     pkv_dtype dtype, pkv_layout k_layout, void* stream);
 
 /* Workspace bytes that pkv_paged_attention_decode needs for these arguments
  * (same meaning as there).  total_context_tokens may be -1 if unknown (a
@@ -263,7 +273,8 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
                                int32_t block_size, int32_t num_blocks,
                                int32_t max_blocks_per_seq, int32_t max_context_len,
                                int64_t total_context_tokens, float scale, pkv_dtype dtype,
-                               void* workspace, size_t workspace_bytes, void* stream);
+                               pkv_layout k_layout, void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 /* Paged prefill attention: causal attention of the newest tokens of each
  * sequence over everything it holds ("Fixed-Size KV Blocks": a prompt's
@@ -292,7 +303,7 @@ int pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
                                 int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                 int32_t max_blocks_per_seq, int32_t max_query_len, float scale,
-                                pkv_dtype dtype, void* stream);
+                                pkv_dtype dtype, pkv_layout k_layout, void* stream);
 
 /* Synchronise `stream`, then read and clear the current device's error bits
  * (PKV_DEVERR_*) into *flags_out.  Returns PKV_ERR_DEVICE if any bit was set. */

@@ -13,6 +13,9 @@ also uses, is:
 * ``v_cache[num_blocks, num_kv_heads, D, P]``: the same token's value vector is
   the column ``v_cache[blk, h, :, o]`` (each block stores its values
   transposed);
+* with ``token_major=True`` the key cache is ``k_cache[num_blocks, P,
+  num_kv_heads, D]`` instead (all heads of one token together), the row
+  ``k_cache[blk, o, h, :]``; values are unchanged;
 
 and slot ``s`` means block ``s // P``, offset ``s % P``.  A negative slot means
 "do not write".  Arrays are copied bit for bit (uint16 patterns for bf16).
@@ -29,11 +32,16 @@ def slot_of(table: Sequence[int], block_size: int, t: int) -> int:
     return int(table[t // block_size]) * block_size + t % block_size
 
 
+def _shape(k_cache, v_cache, token_major):
+    nb, hkv, d, p = v_cache.shape
+    assert k_cache.shape == ((nb, p, hkv, d) if token_major else (nb, hkv, p, d))
+    return nb, hkv, p, d
+
+
 def write_tokens(k_cache: np.ndarray, v_cache: np.ndarray, slots: Sequence[int],
-                 k: np.ndarray, v: np.ndarray) -> None:
+                 k: np.ndarray, v: np.ndarray, token_major: bool = False) -> None:
     """Store token i's K/V (``k[i]``, ``v[i]`` of shape [Hkv, D]) at ``slots[i]``."""
-    nb, hkv, p, d = k_cache.shape
-    assert v_cache.shape == (nb, hkv, d, p)
+    nb, hkv, p, d = _shape(k_cache, v_cache, token_major)
     assert k.shape == v.shape == (len(slots), hkv, d)
     for i, s in enumerate(slots):
         s = int(s)
@@ -41,19 +49,22 @@ def write_tokens(k_cache: np.ndarray, v_cache: np.ndarray, slots: Sequence[int],
             continue
         blk, off = divmod(s, p)
         for h in range(hkv):
-            k_cache[blk, h, off, :] = k[i, h, :]
+            if token_major:
+                k_cache[blk, off, h, :] = k[i, h, :]
+            else:
+                k_cache[blk, h, off, :] = k[i, h, :]
             v_cache[blk, h, :, off] = v[i, h, :]
 
 
 def read_sequence(k_cache: np.ndarray, v_cache: np.ndarray, table: Sequence[int],
-                  length: int):
+                  length: int, token_major: bool = False):
     """Gather a sequence's K/V back into logical order: ([L,Hkv,D], [L,Hkv,D])."""
-    nb, hkv, p, d = k_cache.shape
+    nb, hkv, p, d = _shape(k_cache, v_cache, token_major)
     ks = np.empty((length, hkv, d), dtype=k_cache.dtype)
     vs = np.empty((length, hkv, d), dtype=v_cache.dtype)
     for t in range(length):
         blk, off = divmod(slot_of(table, p, t), p)
-        ks[t] = k_cache[blk, :, off, :]
+        ks[t] = k_cache[blk, off, :, :] if token_major else k_cache[blk, :, off, :]
         vs[t] = v_cache[blk, :, :, off]
     return ks, vs
 

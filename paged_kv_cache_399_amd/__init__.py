@@ -203,32 +203,41 @@ class BlockPool:
         return mx.value, tot.value
 
 
-def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
+LAYOUTS = {"head_major": _lib.LAYOUT_HEAD_MAJOR, "token_major": _lib.LAYOUT_TOKEN_MAJOR}
+
+
+def _cache_shape(k_cache, v_cache, layout="head_major"):
+    """(num_blocks, Hkv, block_size, D, layout code); the value cache fixes the sizes."""
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
+    if k_cache.dim() != 4 or v_cache.dim() != 4:
+        raise ValueError("k_cache and v_cache must be 4-D")
+    nb, hkv, d, bs = v_cache.shape
+    want = (nb, bs, hkv, d) if layout == "token_major" else (nb, hkv, bs, d)
+    if tuple(k_cache.shape) != want:
+        raise ValueError(f"k_cache must be {want} for layout {layout!r} "
+                         "(v_cache is [num_blocks, num_kv_heads, head_dim, block_size])")
+    if v_cache.dtype != k_cache.dtype:
+        raise TypeError("k_cache and v_cache dtypes differ")
+    return nb, hkv, bs, d, LAYOUTS[layout]
+
+
+def copy_blocks(k_cache, v_cache, pairs, stream=None, layout="head_major") -> None:
     """Copy-on-write copies: pairs is host int [n, 2] of (src, dst) blocks."""
     p = _i32_array(pairs).reshape(-1)
     if p.size == 0:
         return
-    nb, hkv, bs, d = k_cache.shape
+    nb, hkv, bs, d, _ = _cache_shape(k_cache, v_cache, layout)
     _check(lib.pkv_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _p32(p),
                                p.size // 2, nb, hkv, d, bs, _dtype_code(k_cache),
                                _stream_ptr(stream)))
 
 
-def _cache_shape(k_cache, v_cache):
-    if k_cache.dim() != 4:
-        raise ValueError("k_cache must be [num_blocks, num_kv_heads, block_size, head_dim]")
-    nb, hkv, bs, d = k_cache.shape
-    if tuple(v_cache.shape) != (nb, hkv, d, bs):
-        raise ValueError("v_cache must be [num_blocks, num_kv_heads, head_dim, block_size]")
-    if v_cache.dtype != k_cache.dtype:
-        raise TypeError("k_cache and v_cache dtypes differ")
-    return nb, hkv, bs, d
-
-
-def cache_append(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None) -> None:
+def cache_append(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None,
+                 layout="head_major") -> None:
     """Write k_new/v_new [n, Hkv, D] at the device int32 slots (negative = skip)."""
     import torch
-    nb, hkv, bs, d = _cache_shape(k_cache, v_cache)
+    nb, hkv, bs, d, lay = _cache_shape(k_cache, v_cache, layout)
     n = k_new.shape[0]
     if tuple(k_new.shape) != (n, hkv, d) or tuple(v_new.shape) != (n, hkv, d):
         raise ValueError("k_new / v_new must be [n_tokens, num_kv_heads, head_dim]")
@@ -239,7 +248,7 @@ def cache_append(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None) -> N
     _check(lib.pkv_cache_append(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                                 _dev(k_new, "k_new"), _dev(v_new, "v_new"),
                                 _dev(slot_mapping, "slot_mapping"), n, nb, hkv, d, bs,
-                                _dtype_code(k_cache), _stream_ptr(stream)))
+                                _dtype_code(k_cache), lay, _stream_ptr(stream)))
 
 
 def decode_workspace_bytes(n_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
@@ -255,14 +264,15 @@ def decode_workspace_bytes(n_seqs: int, num_q_heads: int, num_kv_heads: int, hea
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens,
                            max_context_len: int, total_context_tokens: int = -1,
-                           scale: Optional[float] = None, workspace=None, stream=None):
+                           scale: Optional[float] = None, workspace=None, stream=None,
+                           layout="head_major"):
     """Decode attention over the paged cache; writes ``out`` [B, Hq, D] and returns it.
 
     ``workspace`` is a uint8 device tensor of at least decode_workspace_bytes(...)
     bytes; if None one is allocated with torch (plumbing only).
     """
     import torch
-    nb, hkv, bs, d = _cache_shape(k_cache, v_cache)
+    nb, hkv, bs, d, lay = _cache_shape(k_cache, v_cache, layout)
     b, hq, d2 = q.shape
     if d2 != d or tuple(out.shape) != (b, hq, d):
         raise ValueError("q / out must be [n_seqs, num_q_heads, head_dim]")
@@ -285,12 +295,13 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens,
         _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(block_table, "block_table"), _dev(context_lens, "context_lens"), b, hq, hkv, d, bs,
         nb, block_table.shape[1], int(max_context_len), int(total_context_tokens), float(scale),
-        dt, _dev(workspace, "workspace"), workspace.numel(), _stream_ptr(stream)))
+        dt, lay, _dev(workspace, "workspace"), workspace.numel(), _stream_ptr(stream)))
     return out
 
 
 def paged_attention_prefill(out, q, k_cache, v_cache, block_table, context_lens, query_start,
-                            max_query_len: int, scale: Optional[float] = None, stream=None):
+                            max_query_len: int, scale: Optional[float] = None, stream=None,
+                            layout="head_major"):
     """Causal attention of each sequence's newest tokens over its whole paged context.
 
     ``q`` / ``out`` are [total new tokens, Hq, D]; ``query_start`` is a device
@@ -298,7 +309,7 @@ def paged_attention_prefill(out, q, k_cache, v_cache, block_table, context_lens,
     be in the cache.  Writes ``out`` and returns it.
     """
     import torch
-    nb, hkv, bs, d = _cache_shape(k_cache, v_cache)
+    nb, hkv, bs, d, lay = _cache_shape(k_cache, v_cache, layout)
     nt, hq, d2 = q.shape
     if d2 != d or tuple(out.shape) != (nt, hq, d):
         raise ValueError("q / out must be [tokens, num_q_heads, head_dim]")
@@ -316,7 +327,7 @@ def paged_attention_prefill(out, q, k_cache, v_cache, block_table, context_lens,
         _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(block_table, "block_table"), _dev(context_lens, "context_lens"),
         _dev(query_start, "query_start"), b, hq, hkv, d, bs, nb, block_table.shape[1],
-        int(max_query_len), float(scale), _dtype_code(q), _stream_ptr(stream)))
+        int(max_query_len), float(scale), _dtype_code(q), lay, _stream_ptr(stream)))
     return out
 
 

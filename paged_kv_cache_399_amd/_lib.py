@@ -27,6 +27,8 @@ F32 = 0
 BF16 = 1
 
 UPLOAD_INCREMENTAL = 1
+LAYOUT_HEAD_MAJOR = 0
+LAYOUT_TOKEN_MAJOR = 1
 
 
 class Stats(C.Structure):
@@ -54,15 +56,15 @@ SIGNATURES = {
                                          _pi32, _pi64, _i32, _vp]),
     "pkv_copy_blocks": (C.c_int, [_vp, _vp, _pi32, _i32, _i32, _i32, _i32, _i32, C.c_int, _vp]),
     "pkv_cache_append": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
-                                   C.c_int, _vp]),
+                                   C.c_int, C.c_int, _vp]),
     "pkv_decode_workspace_bytes": (C.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i64, C.c_int,
                                              C.POINTER(C.c_size_t)]),
     "pkv_paged_attention_decode": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
-                                             _i32, _i32, _i32, _i32, _i64, C.c_float, C.c_int, _vp,
-                                             C.c_size_t, _vp]),
+                                             _i32, _i32, _i32, _i32, _i64, C.c_float, C.c_int,
+                                             C.c_int, _vp, C.c_size_t, _vp]),
     "pkv_paged_attention_prefill": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                               _i32, _i32, _i32, _i32, _i32, C.c_float, C.c_int,
-                                              _vp]),
+                                              C.c_int, _vp]),
     "pkv_check_device_errors": (C.c_int, [_vp, _pi32]),
     "pkv_last_error": (C.c_char_p, []),
     "pkv_version": (C.c_char_p, []),
@@ -79,6 +81,15 @@ def load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python paged_kv_cache_399_amd/build.py` (hipcc, gfx950)")
+    # The library must run on the same HIP runtime as torch: it takes torch's
+    # device pointers and stream handles.  torch ships its own libamdhip64 /
+    # libhsa-runtime64; loading torch first makes the library's dependency
+    # resolve to those already-loaded copies (same soname) instead of a second
+    # runtime from the system ROCm, which would find the GPU already taken.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = C.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

@@ -27,7 +27,7 @@ template <typename E>
 __global__ __launch_bounds__(256) void cache_append_kernel(
     E* __restrict__ kc, E* __restrict__ vc, const E* __restrict__ kn, const E* __restrict__ vn,
     const int32_t* __restrict__ slots, int32_t n_tokens, int64_t num_slots, int32_t hkv,
-    int32_t d, int32_t p, int32_t vec_ok, int32_t* __restrict__ err) {
+    int32_t d, int32_t p, KStrides ks, int32_t vec_ok, int32_t* __restrict__ err) {
   const int32_t hd = hkv * d;
   for (int32_t tok = blockIdx.x; tok < n_tokens; tok += gridDim.x) {
     const int32_t s = slots[tok];
@@ -45,12 +45,12 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
       for (int32_t i = threadIdx.x; i < nvec; i += blockDim.x) {
         const int32_t e = i * V, h = e / d, dd = e % d;
         const uint4 x = *reinterpret_cast<const uint4*>(ksrc + e);
-        *reinterpret_cast<uint4*>(kc + ((blk * hkv + h) * p + off) * d + dd) = x;
+        *reinterpret_cast<uint4*>(kc + blk * hd * p + h * ks.head + off * ks.tok + dd) = x;
       }
     } else {
       for (int32_t e = threadIdx.x; e < hd; e += blockDim.x) {
         const int32_t h = e / d, dd = e % d;
-        kc[((blk * hkv + h) * p + off) * d + dd] = ksrc[e];
+        kc[blk * hd * p + h * ks.head + off * ks.tok + dd] = ksrc[e];
       }
     }
     for (int32_t e = threadIdx.x; e < hd; e += blockDim.x) {
@@ -80,7 +80,7 @@ template <typename E>
 __global__ __launch_bounds__(256) void cache_append_tiles_kernel(
     E* __restrict__ kc, E* __restrict__ vc, const E* __restrict__ kn, const E* __restrict__ vn,
     const int32_t* __restrict__ slots, int32_t n_tokens, int64_t num_slots, int32_t hkv,
-    int32_t d, int32_t p, int32_t* __restrict__ err) {
+    int32_t d, int32_t p, KStrides ks, int32_t* __restrict__ err) {
   __shared__ uint4 lds_raw[kTileLdsBytes / 16];
   __shared__ int32_t ws[kWin + 2 * kHalo];        // slots of rows [lo, hi)
   __shared__ uint8_t covered[kWin + 2 * kHalo];
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void cache_append_tiles_kernel(
       }
       const int64_t blk = sl / p, off = sl % p;
       const int32_t h = r / d, dd = r - h * d;
-      kc[((blk * hkv + h) * p + off) * d + dd] = kn[(int64_t)(i0 + row) * hd + r];
+      kc[blk * hd * p + h * ks.head + off * ks.tok + dd] = kn[(int64_t)(i0 + row) * hd + r];
       vc[((blk * hkv + h) * d + dd) * p + off] = vn[(int64_t)(i0 + row) * hd + r];
     }
     // whole-block runs.  The value tile sits in LDS with token rows of
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void cache_append_tiles_kernel(
         for (int32_t c = tid; c < nh * per; c += nth) {
           const int32_t hh = c / per, r = c - hh * per, j = r / dv, x = r - j * dv;
           const int64_t src = (row0 + j) * hd + (h0 + hh) * d;
-          reinterpret_cast<uint4*>(kc + (blk * hkv + h0 + hh) * p * d)[r] =
+          *reinterpret_cast<uint4*>(kc + blk * hd * p + (h0 + hh) * ks.head + j * ks.tok + x * V) =
               reinterpret_cast<const uint4*>(kn + src)[x];
           const uint4 vv = reinterpret_cast<const uint4*>(vn + src)[x];
           uint32_t* dst = tile_w + (hh * p + j) * rw + 4 * x;
@@ -264,11 +264,13 @@ using pkv::fail;
 extern "C" int pkv_cache_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                                 const int32_t* d_slot_mapping, int32_t n_tokens, int32_t num_blocks,
                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                                pkv_dtype dtype, void* stream) {
+                                pkv_dtype dtype, pkv_layout k_layout, void* stream) {
   PKV_TRY_BEGIN
   if (n_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0)
     return fail(PKV_ERR_INVALID_ARG, "bad sizes");
   if (!pkv::dtype_valid(dtype)) return fail(PKV_ERR_INVALID_ARG, "bad dtype");
+  if (!pkv::layout_valid(k_layout)) return fail(PKV_ERR_INVALID_ARG, "bad key layout");
+  const pkv::KStrides ks = pkv::k_strides(k_layout, num_kv_heads, block_size, head_dim);
   if (n_tokens == 0) return PKV_OK;
   if (!k_cache || !v_cache || !k_new || !v_new || !d_slot_mapping)
     return fail(PKV_ERR_INVALID_ARG, "NULL pointer");
@@ -296,12 +298,12 @@ extern "C" int pkv_cache_append(void* k_cache, void* v_cache, const void* k_new,
       hipLaunchKernelGGL(pkv::cache_append_tiles_kernel<uint16_t>, dim3(groups), dim3(256), 0, st,
                          (uint16_t*)k_cache, (uint16_t*)v_cache, (const uint16_t*)k_new,
                          (const uint16_t*)v_new, d_slot_mapping, n_tokens, num_slots, num_kv_heads,
-                         head_dim, block_size, err);
+                         head_dim, block_size, ks, err);
     else
       hipLaunchKernelGGL(pkv::cache_append_tiles_kernel<uint32_t>, dim3(groups), dim3(256), 0, st,
                          (uint32_t*)k_cache, (uint32_t*)v_cache, (const uint32_t*)k_new,
                          (const uint32_t*)v_new, d_slot_mapping, n_tokens, num_slots, num_kv_heads,
-                         head_dim, block_size, err);
+                         head_dim, block_size, ks, err);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "cache_append launch: %s", hipGetErrorString(e));
     return PKV_OK;
@@ -311,12 +313,12 @@ extern "C" int pkv_cache_append(void* k_cache, void* v_cache, const void* k_new,
     hipLaunchKernelGGL(pkv::cache_append_kernel<uint16_t>, dim3(grid), dim3(256), 0, st,
                        (uint16_t*)k_cache, (uint16_t*)v_cache, (const uint16_t*)k_new,
                        (const uint16_t*)v_new, d_slot_mapping, n_tokens, num_slots, num_kv_heads,
-                       head_dim, block_size, vec_ok, err);
+                       head_dim, block_size, ks, vec_ok, err);
   else
     hipLaunchKernelGGL(pkv::cache_append_kernel<uint32_t>, dim3(grid), dim3(256), 0, st,
                        (uint32_t*)k_cache, (uint32_t*)v_cache, (const uint32_t*)k_new,
                        (const uint32_t*)v_new, d_slot_mapping, n_tokens, num_slots, num_kv_heads,
-                       head_dim, block_size, vec_ok, err);
+                       head_dim, block_size, ks, vec_ok, err);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "cache_append launch: %s", hipGetErrorString(e));
   return PKV_OK;

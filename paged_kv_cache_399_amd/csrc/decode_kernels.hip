@@ -68,6 +68,7 @@ struct DecodeArgs {
   const int32_t* table;
   const int32_t* ctx;
   int32_t n_seqs, hq, hkv, d, p, num_blocks, max_blocks, part_tokens, max_units;
+  KStrides ks;       // key cache: elements between KV heads, between tokens
   int64_t len_cap;   // min(max_blocks * p, max_context_len): longer contexts are clamped
   float scale_log2;  // scale * log2(e): scores are kept in log2 units
   Plan plan;
@@ -310,7 +311,9 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
   const uint16_t* kc = (const uint16_t*)a.kc;
   const uint16_t* vc = (const uint16_t*)a.vc;
   const int64_t blk_stride = (int64_t)a.hkv * P * D;  // elements per physical block
-  const int64_t head_off = (int64_t)g * P * D;
+  const int64_t head_off = (int64_t)g * P * D;        // value tile of head g
+  const int64_t khead_off = (int64_t)g * a.ks.head;   // first key row of head g
+  const int32_t ktok = a.ks.tok;                      // elements between key rows
 
   f32x4 acc[NJ];
 #pragma unroll
@@ -388,9 +391,9 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
         };
         // rows tx and ty (tx + 4 unless clamped) lie in one block: P >= 8
         const int32_t pk = pick(tx);
-        const uint16_t* kb = kc + (int64_t)pk * blk_stride + head_off + 8 * r;
-        const uint16_t* kxp = kb + (tx % P) * D;
-        const uint16_t* kyp = kb + (ty % P) * D;
+        const uint16_t* kb = kc + (int64_t)pk * blk_stride + khead_off + 8 * r;
+        const uint16_t* kxp = kb + (tx % P) * ktok;
+        const uint16_t* kyp = kb + (ty % P) * ktok;
 #pragma unroll
         for (int i = 0; i < KI; ++i) {
           f.kx[i] = load_stream16(kxp + 32 * i);
@@ -419,8 +422,8 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
         // Blocks of fewer than 8 tokens: each lane reads its entries from the
         // wave's LDS window
         auto pick = [&](int32_t t) -> int32_t { return tab_row[t / P - wb]; };
-        const uint16_t* kxp = kc + (int64_t)pick(tx) * blk_stride + head_off + 8 * r + (tx % P) * D;
-        const uint16_t* kyp = kc + (int64_t)pick(ty) * blk_stride + head_off + 8 * r + (ty % P) * D;
+        const uint16_t* kxp = kc + (int64_t)pick(tx) * blk_stride + khead_off + 8 * r + (tx % P) * ktok;
+        const uint16_t* kyp = kc + (int64_t)pick(ty) * blk_stride + khead_off + 8 * r + (ty % P) * ktok;
 #pragma unroll
         for (int i = 0; i < KI; ++i) {
           f.kx[i] = load_stream16(kxp + 32 * i);
@@ -663,7 +666,8 @@ __global__ __launch_bounds__(256) void decode_dpp_kernel(DecodeArgs a) {
   const T* kc = (const T*)a.kc;
   const T* vc = (const T*)a.vc;
   const int64_t blk_stride = (int64_t)a.hkv * P * D;
-  const int64_t head_off = (int64_t)g * P * D;
+  const int64_t head_off = (int64_t)g * P * D;       // value tile of head g
+  const int64_t khead_off = (int64_t)g * a.ks.head;  // first key row of head g
   const float c = a.scale_log2;
 
   float acc[GMAX][DPL];
@@ -719,8 +723,8 @@ __global__ __launch_bounds__(256) void decode_dpp_kernel(DecodeArgs a) {
       for (int i = 0; i < KL; ++i) {
         const int32_t tb = min(c0 + TPI * i, klast);  // uniform, first row of the load
         const int32_t pb = __builtin_amdgcn_readlane(tabv, tb / P - wb);
-        f.kx[i] = load_stream16((const uint16_t*)(kc + (int64_t)pb * blk_stride + head_off +
-                                                  (int64_t)(tb % P + rr) * D + cc * EPC));
+        f.kx[i] = load_stream16((const uint16_t*)(kc + (int64_t)pb * blk_stride + khead_off +
+                                                  (int64_t)(tb % P + rr) * a.ks.tok + cc * EPC));
       }
 #pragma unroll
       for (int k = 0; k < VP; ++k) {
@@ -928,7 +932,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
     for (int h = 0; h < GMAX; ++h) s[h] = 0.f;
     if (valid) {
-      const T* kr = kc + ((phys_of(t) * a.hkv + g) * P + t % P) * D;
+      const T* kr = kc + phys_of(t) * a.hkv * P * D + (int64_t)g * a.ks.head + (int64_t)(t % P) * a.ks.tok;
       for (int32_t dd = 0; dd < D; ++dd) {
         const float kv = load_f32(kr + dd);
 #pragma unroll
@@ -1326,8 +1330,8 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
                                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                           int32_t max_blocks_per_seq, int32_t max_context_len,
                                           int64_t total_context_tokens, float scale,
-                                          pkv_dtype dtype, void* workspace, size_t workspace_bytes,
-                                          void* stream) {
+                                          pkv_dtype dtype, pkv_layout k_layout, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
   PKV_TRY_BEGIN
   if (n_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
       num_blocks <= 0 || max_blocks_per_seq < 0 || max_context_len < 0)
@@ -1335,6 +1339,7 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   if (num_q_heads % num_kv_heads) return fail(PKV_ERR_INVALID_ARG, "num_q_heads % num_kv_heads != 0");
   if (num_q_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "more than 65535 query heads");
   if (!pkv::dtype_valid(dtype)) return fail(PKV_ERR_INVALID_ARG, "bad dtype");
+  if (!pkv::layout_valid(k_layout)) return fail(PKV_ERR_INVALID_ARG, "bad key layout");
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(PKV_ERR_INVALID_ARG, "scale must be finite and positive");
   if (n_seqs == 0) return PKV_OK;
@@ -1378,6 +1383,7 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   a.hkv = num_kv_heads;
   a.d = head_dim;
   a.p = block_size;
+  a.ks = pkv::k_strides(k_layout, num_kv_heads, block_size, head_dim);
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks_per_seq;
   a.part_tokens = c.part_tokens;

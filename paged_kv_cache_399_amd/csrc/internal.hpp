@@ -21,6 +21,18 @@ inline size_t dtype_size(pkv_dtype dt) { return dt == PKV_F32 ? 4 : 2; }
 
 inline bool dtype_valid(int dt) { return dt == PKV_F32 || dt == PKV_BF16; }
 
+inline bool layout_valid(int l) { return l == PKV_LAYOUT_HEAD_MAJOR || l == PKV_LAYOUT_TOKEN_MAJOR; }
+
+// Element strides of the key cache inside a block: between KV heads and
+// between tokens (a token's head_dim row is contiguous in both layouts).
+struct KStrides {
+  int32_t head, tok;
+};
+inline KStrides k_strides(int layout, int32_t hkv, int32_t p, int32_t d) {
+  if (layout == PKV_LAYOUT_TOKEN_MAJOR) return KStrides{d, hkv * d};
+  return KStrides{p * d, d};
+}
+
 // Block-table patch carried entirely in kernel arguments (no staging copy):
 // lens[len0 + i] = w[i] (i < n_len); slots[slot0 + i] = w[n_len + i]
 // (i < n_slot); then n_ent (row, col, value) triples; then n_reset (row, from)

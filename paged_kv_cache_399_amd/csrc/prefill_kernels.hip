@@ -49,6 +49,7 @@ struct PrefillArgs {
   const int32_t* ctx;
   const int32_t* qstart;
   int32_t n_seqs, hq, hkv, p, num_blocks, max_blocks;
+  KStrides ks;       // key cache: elements between KV heads, between tokens
   float scale_log2;  // scale * log2(e): scores are kept in log2 units
   int32_t* err;
 };
@@ -133,7 +134,8 @@ __global__ __launch_bounds__(64 * G * BT / 16) void prefill_mfma_kernel(PrefillA
       if (p < KP) {
         const int key = p / (D / 8), dc = p % (D / 8);
         const int32_t t = min(c0 + key, kend - 1);
-        x = load16(kc + (phys(t) * a.hkv + g) * P * D + (int64_t)(t % P) * D + dc * 8);
+        x = load16(kc + phys(t) * a.hkv * P * D + (int64_t)g * a.ks.head + (int64_t)(t % P) * a.ks.tok +
+                   dc * 8);
       } else if (p < KP + VP) {
         const int pp = p - KP;
         const int dim = pp / (CH / 8), qq = pp % (CH / 8);
@@ -280,13 +282,14 @@ extern "C" int pkv_paged_attention_prefill(void* out, const void* q, const void*
                                            int32_t head_dim, int32_t block_size,
                                            int32_t num_blocks, int32_t max_blocks_per_seq,
                                            int32_t max_query_len, float scale, pkv_dtype dtype,
-                                           void* stream) {
+                                           pkv_layout k_layout, void* stream) {
   PKV_TRY_BEGIN
   if (n_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
       num_blocks <= 0 || max_blocks_per_seq < 0 || max_query_len < 0)
     return fail(PKV_ERR_INVALID_ARG, "bad sizes");
   if (num_q_heads % num_kv_heads) return fail(PKV_ERR_INVALID_ARG, "num_q_heads % num_kv_heads != 0");
   if (!pkv::dtype_valid(dtype)) return fail(PKV_ERR_INVALID_ARG, "bad dtype");
+  if (!pkv::layout_valid(k_layout)) return fail(PKV_ERR_INVALID_ARG, "bad key layout");
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(PKV_ERR_INVALID_ARG, "scale must be finite and positive");
   const int32_t G = num_q_heads / num_kv_heads;
@@ -315,6 +318,7 @@ extern "C" int pkv_paged_attention_prefill(void* out, const void* q, const void*
   a.hq = num_q_heads;
   a.hkv = num_kv_heads;
   a.p = block_size;
+  a.ks = pkv::k_strides(k_layout, num_kv_heads, block_size, head_dim);
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks_per_seq;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);

@@ -28,13 +28,20 @@ def _poison_value(dtype):
 
 class PagedKVCache:
     def __init__(self, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
-                 dtype, device="cuda", free_order=None, fill: Optional[float] = None):
+                 dtype, device="cuda", free_order=None, fill: Optional[float] = None,
+                 layout: str = "head_major"):
         import torch
         self.pool = BlockPool(num_blocks, block_size, free_order)
         self.num_blocks, self.block_size = num_blocks, block_size
         self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
         self.dtype, self.device = dtype, torch.device(device)
-        shape_k = (num_blocks, num_kv_heads, block_size, head_dim)
+        self.layout = layout
+        if layout == "token_major":
+            shape_k = (num_blocks, block_size, num_kv_heads, head_dim)
+        elif layout == "head_major":
+            shape_k = (num_blocks, num_kv_heads, block_size, head_dim)
+        else:
+            raise ValueError("layout must be 'head_major' or 'token_major'")
         shape_v = (num_blocks, num_kv_heads, head_dim, block_size)
         self.k_cache = torch.empty(shape_k, dtype=dtype, device=self.device)
         self.v_cache = torch.empty(shape_v, dtype=dtype, device=self.device)
@@ -70,15 +77,15 @@ class PagedKVCache:
         import torch
         slots, cow = self.pool.append_slots(seqs, n_new)
         if len(cow):
-            copy_blocks(self.k_cache, self.v_cache, cow, stream)
+            copy_blocks(self.k_cache, self.v_cache, cow, stream, self.layout)
         if len(slots):
             d = torch.from_numpy(slots).to(self.device, non_blocking=False)
-            cache_append(self.k_cache, self.v_cache, k, v, d, stream)
+            cache_append(self.k_cache, self.v_cache, k, v, d, stream, self.layout)
         return slots
 
     def write_slots(self, slots_dev, k, v, stream=None) -> None:
         """Store rows of k/v at device slots (negative slots skip their row)."""
-        cache_append(self.k_cache, self.v_cache, k, v, slots_dev, stream)
+        cache_append(self.k_cache, self.v_cache, k, v, slots_dev, stream, self.layout)
 
     # -- decode step ---------------------------------------------------------
     class Meta:
@@ -112,12 +119,12 @@ class PagedKVCache:
         ones = np.ones(len(m.seqs), dtype=np.int32)
         slots, cow = self.pool.append_slots(m.seqs, ones)
         if len(cow):
-            copy_blocks(self.k_cache, self.v_cache, cow, stream)
+            copy_blocks(self.k_cache, self.v_cache, cow, stream, self.layout)
         m.max_len, m.total = self.pool.block_table_upload(m.seqs, m.max_blocks, m.table, m.lens,
                                                           slots, m.slots, stream,
                                                           incremental=m.uploaded)
         m.uploaded = True
-        cache_append(self.k_cache, self.v_cache, k_new, v_new, m.slots, stream)
+        cache_append(self.k_cache, self.v_cache, k_new, v_new, m.slots, stream, self.layout)
         return slots
 
     def upload(self, m, stream=None):
@@ -132,7 +139,8 @@ class PagedKVCache:
         # the sizing hints stay the prepared ones, so the partition size (and
         # with it the summation order) is fixed for the life of the batch
         return paged_attention_decode(out, q, self.k_cache, self.v_cache, m.table, m.lens,
-                                      m.ws_max_len, m.ws_total, scale, m.workspace, stream)
+                                      m.ws_max_len, m.ws_total, scale, m.workspace, stream,
+                                      self.layout)
 
     def extend(self, m, n_new, k_new, v_new, q, out, scale=None, stream=None):
         """Append n_new[i] tokens to m.seqs[i] and attend causally from each of them.
@@ -145,7 +153,7 @@ class PagedKVCache:
         n_new = np.asarray(n_new, dtype=np.int32)
         slots, cow = self.pool.append_slots(m.seqs, n_new)
         if len(cow):
-            copy_blocks(self.k_cache, self.v_cache, cow, stream)
+            copy_blocks(self.k_cache, self.v_cache, cow, stream, self.layout)
         if m.slots.numel() < max(len(slots), 1):
             m.slots = torch.empty(len(slots), dtype=torch.int32, device=self.device)
         m.max_len, m.total = self.pool.block_table_upload(m.seqs, m.max_blocks, m.table, m.lens,
@@ -153,13 +161,13 @@ class PagedKVCache:
                                                           incremental=m.uploaded)
         m.uploaded = True
         if len(slots):
-            cache_append(self.k_cache, self.v_cache, k_new, v_new, m.slots, stream)
+            cache_append(self.k_cache, self.v_cache, k_new, v_new, m.slots, stream, self.layout)
         qs = np.zeros(len(n_new) + 1, dtype=np.int32)
         qs[1:] = np.cumsum(n_new)
         m.query_start = torch.from_numpy(qs).to(self.device)
         return paged_attention_prefill(out, q, self.k_cache, self.v_cache, m.table, m.lens,
                                        m.query_start, int(n_new.max()) if len(n_new) else 0,
-                                       scale, stream)
+                                       scale, stream, self.layout)
 
     def close(self):
         self.pool.close()

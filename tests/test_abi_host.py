@@ -68,18 +68,23 @@ def test_decode_argument_validation_without_device():
     assert out.value > 0
     # decode with NULL buffers, non-positive scale
     args = [None] * 6 + [4, 32, 8, 128, 16, 64, 8, 100, -1]
-    assert lib.pkv_paged_attention_decode(*args, 0.1, L.BF16, None, 0, None) == L.ERR_INVALID_ARG
+    assert lib.pkv_paged_attention_decode(*args, 0.1, L.BF16, 0, None, 0, None) == L.ERR_INVALID_ARG
     fake = ctypes.c_void_p(0x1000)
     args = [fake] * 6 + [4, 32, 8, 128, 16, 64, 8, 100, -1]
-    assert lib.pkv_paged_attention_decode(*args, -1.0, L.BF16, fake, 1 << 30, None) == L.ERR_INVALID_ARG
+    assert lib.pkv_paged_attention_decode(*args, -1.0, L.BF16, 0, fake, 1 << 30, None) == L.ERR_INVALID_ARG
     # context longer than the table can hold
     args = [fake] * 6 + [4, 32, 8, 128, 16, 64, 2, 100, -1]
-    assert lib.pkv_paged_attention_decode(*args, 0.1, L.BF16, fake, 1 << 30, None) == L.ERR_INVALID_ARG
+    assert lib.pkv_paged_attention_decode(*args, 0.1, L.BF16, 0, fake, 1 << 30, None) == L.ERR_INVALID_ARG
     # workspace too small
     args = [fake] * 6 + [4, 32, 8, 128, 16, 64, 8, 100, -1]
-    assert lib.pkv_paged_attention_decode(*args, 0.1, L.BF16, fake, 16, None) == L.ERR_WORKSPACE
+    assert lib.pkv_paged_attention_decode(*args, 0.1, L.BF16, 0, fake, 16, None) == L.ERR_WORKSPACE
     # cache_append / copy_blocks reject bad shapes before touching the device
-    assert lib.pkv_cache_append(fake, fake, fake, fake, fake, 4, 0, 8, 128, 16, L.BF16, None) == L.ERR_INVALID_ARG
+    assert lib.pkv_cache_append(fake, fake, fake, fake, fake, 4, 0, 8, 128, 16, L.BF16, 0, None) == L.ERR_INVALID_ARG
+    # an unknown key layout is refused by every call that reads or writes the cache
+    assert lib.pkv_cache_append(fake, fake, fake, fake, fake, 4, 8, 8, 128, 16, L.BF16, 2, None) == L.ERR_INVALID_ARG
+    assert lib.pkv_paged_attention_decode(*args, 0.1, L.BF16, 2, fake, 1 << 30, None) == L.ERR_INVALID_ARG
+    assert lib.pkv_paged_attention_prefill(*([fake] * 7), 4, 32, 8, 128, 16, 64, 8, 100, 0.1, L.BF16,
+                                           -1, None) == L.ERR_INVALID_ARG
     assert lib.pkv_copy_blocks(fake, fake, None, 1, 8, 8, 128, 16, 7, None) == L.ERR_INVALID_ARG
 
 

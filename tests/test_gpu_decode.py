@@ -343,3 +343,29 @@ def test_small_and_large_blocks_span_several_table_windows(monkeypatch, p):
     case = build_case(cfg, seed=11)
     err = check_attention(case)
     say(f"  p={p}: max err {err:.3e}")
+
+
+@pytest.mark.parametrize("math", ["mfma", "dpp", "generic"])
+@pytest.mark.parametrize("dtype,hq,hkv,d,p", [
+    ("bf16", 16, 4, 128, 16), ("bf16", 8, 2, 64, 4), ("bf16", 16, 8, 128, 64), ("f32", 8, 2, 64, 16),
+])
+def test_token_major_key_layout(monkeypatch, math, dtype, hq, hkv, d, p):
+    """Keys stored [blocks, P, Hkv, D] on every decode kernel that takes the shape:
+    caches bit for bit against the oracle's token-major layout, attention
+    against float64, and the output bit for bit equal to the head-major run."""
+    import torch
+    if math == "mfma" and dtype != "bf16":
+        pytest.skip("matrix-core kernel is bf16 only")
+    if math == "dpp" and (hq // hkv > 4 or (dtype == "bf16" and p % 8)):
+        pytest.skip("DPP kernel takes head groups up to 4 and 16-byte block rows")
+    monkeypatch.setenv("PKV_DECODE_MATH", math)
+    cfg = DecodeConfig(f"tm_{math}_{dtype}_{hq}_{hkv}_{d}_{p}", len(EDGE_LENGTHS), hq, hkv, d, p,
+                       dtype, "fixed", fixed_lengths=tuple(EDGE_LENGTHS))
+    case = build_case(cfg, seed=13, fill=7.0, layout="token_major")
+    kc, vc, (pfx, pre, dec) = expected_caches(case, _fill_bits(case, 7.0))
+    assert _bits_equal(host_bits(case.kv.k_cache), kc)
+    assert _bits_equal(host_bits(case.kv.v_cache), vc)
+    err = check_attention(case)
+    head = build_case(cfg, seed=13, fill=7.0)
+    assert torch.equal(case.out, head.out)
+    say(f"  {cfg.name}: max err {err:.3e}")
