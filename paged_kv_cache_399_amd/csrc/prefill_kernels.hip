@@ -13,18 +13,23 @@
 // whole tile of queries, so it is staged once in LDS per workgroup and all
 // waves run both products on matrix cores from there.
 //
-// Work decomposition: grid (query tiles, sequences, KV heads); a workgroup
-// takes BT query tokens of one sequence and all G query heads of one KV head
-// (G * BT / 16 waves); wave w takes 16 query tokens of query head w % G.
-// Tiles are launched last-first: later tiles see more keys, so the dispatcher
-// starts the longest work first.
+// Work decomposition: grid (query tiles, sequences, KV heads x head halves);
+// a workgroup of four waves takes 128 query rows: BT = 128 / GW query tokens
+// of GW query heads of one KV head (GW = G, or 8 halves of a 16-head group).
+// Wave w takes two 16-row tiles, k = 2w and 2w + 1, tile k being tokens
+// 16 (k / GW) .. + 15 of head k % GW, so every key / value fragment a wave
+// reads from LDS feeds two matrix-core products.  Tiles are launched
+// last-first: later tiles see more keys, so the dispatcher starts the longest
+// work first.
 //
 // Lane layout (as in the decode matrix-core kernel, with query tokens in the
 // 16-wide N dimension): lane l has n = l % 16 (its query column) and
-// r = l / 16.  For a 32-key chunk, two 16x16x32 MFMA chains produce the
-// scores of keys 8r .. 8r + 7 for query n; those eight probabilities are the B
-// operand of the value MFMA, whose A operand is the 16-byte run of the
-// token-minor value tile (dims 16 j + n, keys 8r .. 8r + 7).
+// r = l / 16.  For a 32-key chunk, two 16x16x32 MFMA chains per tile produce
+// the scores of keys 8r .. 8r + 7 for query n; those eight probabilities are
+// the B operand of the value MFMA, whose A operand is the 16-byte run of the
+// token-minor value tile (dims 16 j + n, keys 8r .. 8r + 7).  The maximum and
+// the sum over a query's 32 keys cross the four row groups with two lane
+// swaps (32 apart, then 16 apart) on the vector ALU.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -62,200 +67,295 @@ __device__ __forceinline__ uint4 load16(const uint16_t* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int D, int G, int BT>
-__global__ __launch_bounds__(64 * G * BT / 16) void prefill_mfma_kernel(PrefillArgs a) {
-  constexpr int NW = G * BT / 16;  // waves
-  constexpr int NT = 64 * NW;      // threads
-  constexpr int CH = 32;           // keys per chunk
-  constexpr int KI = D / 32;       // score MFMA steps over head_dim
-  constexpr int NJ = D / 16;       // value MFMA output tiles over head_dim
-  constexpr int KS = D + 8;        // padded LDS key row (elements)
-  constexpr int VS = CH + 8;       // padded LDS value row (elements)
-  constexpr int KP = CH * D / 8;   // 16-byte key pieces per chunk
-  constexpr int VP = D * CH / 8;   // 16-byte value pieces per chunk
-  constexpr int PER = (KP + VP + NT - 1) / NT;
+// How far (log2 units) a chunk's maximum score may exceed the running
+// reference before the reference moves and the accumulators are rescaled.
+constexpr float kRefSlack = 8.f;
+
+// Pairwise reductions with lane swaps on the vector ALU: v_permlane32_swap
+// exchanges the upper half of one register with the lower half of another;
+// with both operands equal, its two results hold the values of lanes l and
+// l ^ 32 (v_permlane16_swap: of 16-lane rows, l and l ^ 16), in the same
+// order in every lane, so both lanes of a pair get the same bits.
+__device__ __forceinline__ float pair_max32(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto x = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)x[0]), __builtin_bit_cast(float, (uint32_t)x[1]));
+}
+__device__ __forceinline__ float pair_max16(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto x = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)x[0]), __builtin_bit_cast(float, (uint32_t)x[1]));
+}
+__device__ __forceinline__ float pair_sum32(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto x = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)x[0]) + __builtin_bit_cast(float, (uint32_t)x[1]);
+}
+__device__ __forceinline__ float pair_sum16(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto x = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)x[0]) + __builtin_bit_cast(float, (uint32_t)x[1]);
+}
+
+template <int D, int GW>
+__global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
+  constexpr int NT = 256;             // threads: four waves
+  constexpr int BT = 16 * (8 / GW);   // query tokens per workgroup
+  constexpr int CH = 32;              // keys per chunk
+  constexpr int KI = D / 32;          // score MFMA steps over head_dim
+  constexpr int NJ = D / 16;          // value MFMA output tiles over head_dim
+  constexpr int KS = D + 8;           // padded LDS key row (elements)
+  constexpr int VS = CH + 8;          // padded LDS value row (elements)
+  constexpr int KU = CH * D / 8 / NT; // 16-byte key pieces per thread per chunk
+  constexpr int VU = D * CH / 8 / NT; // 16-byte value pieces per thread per chunk
+  constexpr int TW = 1024;            // block-table window (entries)
+  static_assert(KU >= 1 && VU >= 1, "chunk pieces");
   __shared__ __align__(16) uint16_t k_lds[2][CH * KS];
   __shared__ __align__(16) uint16_t v_lds[2][D * VS];
+  __shared__ int32_t tab[TW];
 
-  const int32_t b = blockIdx.y, g = blockIdx.z;
+  const int32_t G = a.hq / a.hkv;
+  const int32_t halves = G / GW;
+  const int32_t b = blockIdx.y, g = blockIdx.z / halves, hpart = blockIdx.z - g * halves;
   const int32_t tile = (int32_t)gridDim.x - 1 - (int32_t)blockIdx.x;  // last tiles first
   const int32_t q0 = a.qstart[b];
   const int32_t n = a.qstart[b + 1] - q0;
   if (n <= 0 || tile * BT >= n) return;  // uniform over the workgroup
   const int32_t P = a.p;
-  int32_t L = a.ctx[b];
+  const int32_t L = a.ctx[b];
   if (L < n || (int64_t)L > (int64_t)a.max_blocks * P) {
-    if (threadIdx.x == 0 && tile == 0) atomicOr(a.err, PKV_DEVERR_CONTEXT_LEN);
+    if (threadIdx.x == 0 && tile == 0 && hpart == 0) atomicOr(a.err, PKV_DEVERR_CONTEXT_LEN);
     return;  // the sequence's rows are left unwritten
   }
   const int32_t base = L - n;  // position of query 0
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int hh = w % G, ts = w / G;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nq = lane & 15, r = lane >> 4;
-  const int32_t head = g * G + hh;
-  const int32_t wq0 = tile * BT + ts * 16;           // this wave's first query
-  const int32_t qi = min(wq0 + nq, n - 1);           // columns past the end repeat the last query
-  const bool q_ok = wq0 + nq < n;
-  const int32_t qpos = base + qi;
-  const int32_t wave_kend = wq0 < n ? base + min(wq0 + 15, n - 1) + 1 : 0;  // keys [0, wave_kend)
-  const int32_t kend = base + min(tile * BT + BT - 1, n - 1) + 1;          // the workgroup's keys
-  const int32_t nchunks = (kend + CH - 1) / CH;
   const float c = a.scale_log2;
 
+  // this wave's two tiles
+  int32_t head[2], tok0[2], qi[2], qpos[2];
+  bool on[2];
+  int32_t wave_last = -1;  // last query (within the chunk of new tokens) of the wave
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int k = 2 * w + t;
+    head[t] = g * G + hpart * GW + k % GW;
+    tok0[t] = tile * BT + 16 * (k / GW);
+    on[t] = tok0[t] < n;  // uniform
+    qi[t] = min(tok0[t] + nq, n - 1);  // columns past the end repeat the last query
+    qpos[t] = base + qi[t];
+    if (on[t]) wave_last = max(wave_last, min(tok0[t] + 15, n - 1));
+  }
+  const int32_t wave_kend = wave_last >= 0 ? base + wave_last + 1 : 0;         // keys [0, wave_kend)
+  const int32_t kend = base + min(tile * BT + BT - 1, n - 1) + 1;             // the workgroup's keys
+  const int32_t nchunks = (kend + CH - 1) / CH;
+
   // query fragments (B operand of the score MFMA): dims 32 i + 8 r of query qi
-  bf16x8 qf[KI];
-  {
-    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)(q0 + qi) * a.hq + head) * D + 8 * r;
+  bf16x8 qf[2][KI];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)(q0 + qi[t]) * a.hq + head[t]) * D + 8 * r;
 #pragma unroll
     for (int i = 0; i < KI; ++i)
-      qf[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qrow + 32 * i));
+      qf[t][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qrow + 32 * i));
   }
 
   const uint16_t* kc = (const uint16_t*)a.kc;
   const uint16_t* vc = (const uint16_t*)a.vc;
   const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
-  auto phys = [&](int32_t t) -> int64_t {
-    int32_t e = trow[t / P];
-    if ((uint32_t)e >= (uint32_t)a.num_blocks) {
-      atomicOr(a.err, PKV_DEVERR_TABLE_ENTRY);
-      e = 0;
+  const int64_t blk_stride = (int64_t)a.hkv * P * D;
+  const int64_t khead = (int64_t)g * a.ks.head, vhead = (int64_t)g * P * D;
+  const int32_t last_blk = (kend - 1) / P;
+
+  // block-table window: tab[i] = physical block of logical block wb + i
+  int32_t wb = 0;
+  auto load_tab = [&](int32_t first) {
+    for (int i = tid; i < TW; i += NT) {
+      const int32_t lb = first + i;
+      int32_t e = 0;
+      if (lb <= last_blk) {
+        e = trow[lb];
+        if ((uint32_t)e >= (uint32_t)a.num_blocks) {
+          atomicOr(a.err, PKV_DEVERR_TABLE_ENTRY);
+          e = 0;
+        }
+      }
+      tab[i] = e;
     }
-    return e;
   };
 
   // cooperative chunk staging: key rows and value-tile runs, 16-byte pieces
-  uint4 stage[PER];
+  uint4 kst[KU], vst[VU];
   auto gload = [&](int32_t c0) {
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int p = threadIdx.x + u * NT;
-      uint4 x = uint4{0, 0, 0, 0};
-      if (p < KP) {
-        const int key = p / (D / 8), dc = p % (D / 8);
-        const int32_t t = min(c0 + key, kend - 1);
-        x = load16(kc + phys(t) * a.hkv * P * D + (int64_t)g * a.ks.head + (int64_t)(t % P) * a.ks.tok +
-                   dc * 8);
-      } else if (p < KP + VP) {
-        const int pp = p - KP;
-        const int dim = pp / (CH / 8), qq = pp % (CH / 8);
-        const int32_t t0 = c0 + 8 * qq;                       // 8 keys inside one block (P % 8 == 0)
-        const int32_t t = min(t0, (kend - 1) & ~7);
-        x = load16(vc + (phys(t) * a.hkv + g) * D * P + (int64_t)dim * P + (t % P));
-        // keys at or past the context end: zero, so unused slots cannot leak
-        const int32_t nv = t0 >= kend ? 0 : min(kend - t0, 8);
-        if (nv < 8) {
-          const uint32_t m0 = nv >= 2 ? 0xffffffffu : (nv == 1 ? 0x0000ffffu : 0u);
-          const uint32_t m1 = nv >= 4 ? 0xffffffffu : (nv == 3 ? 0x0000ffffu : 0u);
-          const uint32_t m2 = nv >= 6 ? 0xffffffffu : (nv == 5 ? 0x0000ffffu : 0u);
-          const uint32_t m3 = nv >= 8 ? 0xffffffffu : (nv == 7 ? 0x0000ffffu : 0u);
-          x.x &= m0;
-          x.y &= m1;
-          x.z &= m2;
-          x.w &= m3;
-        }
+    for (int u = 0; u < KU; ++u) {
+      const int p = tid + u * NT;
+      const int key = p / (D / 8), dc = p % (D / 8);
+      const int32_t t = min(c0 + key, kend - 1);
+      const int64_t blk = tab[t / P - wb];
+      kst[u] = load16(kc + blk * blk_stride + khead + (int64_t)(t % P) * a.ks.tok + dc * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < VU; ++u) {
+      const int p = tid + u * NT;
+      const int dim = p / (CH / 8), qq = p % (CH / 8);
+      const int32_t t0 = c0 + 8 * qq;                 // 8 keys inside one block (P % 8 == 0)
+      const int32_t t = min(t0, (kend - 1) & ~7);
+      const int64_t blk = tab[t / P - wb];
+      uint4 x = load16(vc + blk * blk_stride + vhead + (int64_t)dim * P + (t % P));
+      // keys at or past the context end: zero, so unused slots cannot leak
+      const int32_t nv = t0 >= kend ? 0 : min(kend - t0, 8);
+      if (nv < 8) {
+        const uint32_t m0 = nv >= 2 ? 0xffffffffu : (nv == 1 ? 0x0000ffffu : 0u);
+        const uint32_t m1 = nv >= 4 ? 0xffffffffu : (nv == 3 ? 0x0000ffffu : 0u);
+        const uint32_t m2 = nv >= 6 ? 0xffffffffu : (nv == 5 ? 0x0000ffffu : 0u);
+        const uint32_t m3 = nv >= 8 ? 0xffffffffu : (nv == 7 ? 0x0000ffffu : 0u);
+        x.x &= m0;
+        x.y &= m1;
+        x.z &= m2;
+        x.w &= m3;
       }
-      stage[u] = x;
+      vst[u] = x;
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int p = threadIdx.x + u * NT;
-      if (p < KP) {
-        const int key = p / (D / 8), dc = p % (D / 8);
-        *reinterpret_cast<uint4*>(&k_lds[buf][key * KS + dc * 8]) = stage[u];
-      } else if (p < KP + VP) {
-        const int pp = p - KP;
-        const int dim = pp / (CH / 8), qq = pp % (CH / 8);
-        *reinterpret_cast<uint4*>(&v_lds[buf][dim * VS + qq * 8]) = stage[u];
-      }
+    for (int u = 0; u < KU; ++u) {
+      const int p = tid + u * NT;
+      const int key = p / (D / 8), dc = p % (D / 8);
+      *reinterpret_cast<uint4*>(&k_lds[buf][key * KS + dc * 8]) = kst[u];
+    }
+#pragma unroll
+    for (int u = 0; u < VU; ++u) {
+      const int p = tid + u * NT;
+      const int dim = p / (CH / 8), qq = p % (CH / 8);
+      *reinterpret_cast<uint4*>(&v_lds[buf][dim * VS + qq * 8]) = vst[u];
     }
   };
 
-  f32x4 acc[NJ];
+  f32x4 acc[2][NJ];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
   const int krow_x = 8 * (nq >> 2) + (nq & 3);  // key of chain-X row nq within the chunk
-  const int32_t wave_qpos0 = base + wq0;        // smallest query position of the wave
 
   auto compute = [&](int buf, int32_t c0) {
     const uint16_t* kl = k_lds[buf];
     const uint16_t* vl = v_lds[buf];
-    f32x4 sx = {0.f, 0.f, 0.f, 0.f}, sy = {0.f, 0.f, 0.f, 0.f};
+    f32x4 sx[2], sy[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) sx[t] = sy[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
       const bf16x8 ax = *reinterpret_cast<const bf16x8*>(&kl[krow_x * KS + 32 * i + 8 * r]);
       const bf16x8 ay = *reinterpret_cast<const bf16x8*>(&kl[(krow_x + 4) * KS + 32 * i + 8 * r]);
-      sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, qf[i], sx, 0, 0, 0);
-      sy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ay, qf[i], sy, 0, 0, 0);
-    }
-    float s[8] = {sx[0], sx[1], sx[2], sx[3], sy[0], sy[1], sy[2], sy[3]};
-    if (c0 + CH - 1 > wave_qpos0) {  // uniform: the chunk reaches past some query's position
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s[e] = c0 + 8 * r + e <= qpos ? s[e] : -INFINITY;
+      for (int t = 0; t < 2; ++t) {
+        sx[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, qf[t][i], sx[t], 0, 0, 0);
+        sy[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ay, qf[t][i], sy[t], 0, 0, 0);
+      }
     }
-    float cm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
-                     fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-    cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
-    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
-    const float m_new = fmaxf(m_run, cm);  // finite: key 0 is in the first chunk of every query
-    const float alpha = fast_exp2((m_run - m_new) * c);
-    const float mc = m_new * c;
-    bf16x8 pb;
-    float psum = 0.f;
+    bf16x8 pb[2];
+    float alpha[2];
+    bool rescale[2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const __bf16 x = (__bf16)fast_exp2(fmaf(s[e], c, -mc));
-      pb[e] = x;
-      psum += (float)x;
+    for (int t = 0; t < 2; ++t) {
+      float s[8] = {sx[t][0], sx[t][1], sx[t][2], sx[t][3], sy[t][0], sy[t][1], sy[t][2], sy[t][3]};
+      if (c0 + CH - 1 > base + tok0[t]) {  // uniform: the chunk reaches past some query's position
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] = c0 + 8 * r + e <= qpos[t] ? s[e] : -INFINITY;
+      }
+      float cm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                       fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+      cm = pair_max16(pair_max32(cm));
+      // The reference maximum m_run moves only when a chunk's maximum exceeds
+      // it by more than 2^8 (in probability): until then probabilities are
+      // at most 256, and accumulator and sum share the stale reference, so
+      // nothing needs rescaling.  Finite after the first chunk (key 0 lies in
+      // the first chunk of every query), which always moves it.
+      rescale[t] = __builtin_amdgcn_ballot_w64((cm - m_run[t]) * c > kRefSlack) != 0;  // uniform
+      alpha[t] = 1.f;
+      if (rescale[t]) {
+        const float m_new = fmaxf(m_run[t], cm);
+        alpha[t] = fast_exp2((m_run[t] - m_new) * c);
+        m_run[t] = m_new;
+      }
+      const float mc = m_run[t] * c;
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const __bf16 x = (__bf16)fast_exp2(fmaf(s[e], c, -mc));
+        pb[t][e] = x;
+        psum += (float)x;
+      }
+      l_run[t] = fmaf(l_run[t], alpha[t], psum);
     }
-    l_run = fmaf(l_run, alpha, psum);
-    m_run = m_new;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (rescale[t]) {  // rare, one uniform branch
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[t][j] *= alpha[t];
+      }
+    }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const bf16x8 av = *reinterpret_cast<const bf16x8*>(&vl[(16 * j + nq) * VS + 8 * r]);
-      acc[j] *= alpha;
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, acc[j], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[t], acc[t][j], 0, 0, 0);
     }
   };
 
+  load_tab(0);
+  __syncthreads();
   gload(0);
   lstore(0);
   __syncthreads();
   for (int32_t ci = 0; ci < nchunks; ++ci) {
     const int32_t c0 = ci * CH;
     const bool more = ci + 1 < nchunks;  // uniform
+    if (more && min(c0 + 2 * CH, kend) - 1 >= (wb + TW) * P) {
+      // the next chunk leaves the table window; every read of it is behind
+      // the last barrier
+      wb = (c0 + CH) / P;
+      load_tab(wb);
+      __syncthreads();
+    }
     if (more) gload(c0 + CH);
     if (c0 < wave_kend) compute(ci & 1, c0);  // uniform over the wave
     if (more) lstore((ci + 1) & 1);
     __syncthreads();
   }
 
-  // totals over the four row groups, then the output rows of this lane's query
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  if (!q_ok) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  uint16_t* orow = (uint16_t*)a.out + ((int64_t)(q0 + qi) * a.hq + head) * D + 4 * r;
+  // totals over the four row groups, then the output rows of each tile
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const __bf16 o0 = (__bf16)(acc[j][0] * inv), o1 = (__bf16)(acc[j][1] * inv);
-    const __bf16 o2 = (__bf16)(acc[j][2] * inv), o3 = (__bf16)(acc[j][3] * inv);
-    uint2 wv;
-    wv.x = (uint32_t)__builtin_bit_cast(uint16_t, o0) | ((uint32_t)__builtin_bit_cast(uint16_t, o1) << 16);
-    wv.y = (uint32_t)__builtin_bit_cast(uint16_t, o2) | ((uint32_t)__builtin_bit_cast(uint16_t, o3) << 16);
-    *reinterpret_cast<uint2*>(orow + 16 * j) = wv;
+  for (int t = 0; t < 2; ++t) {
+    if (!on[t]) continue;  // uniform
+    const float l_tot = pair_sum16(pair_sum32(l_run[t]));
+    if (tok0[t] + nq >= n) continue;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t* orow = (uint16_t*)a.out + ((int64_t)(q0 + qi[t]) * a.hq + head[t]) * D + 4 * r;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const __bf16 o0 = (__bf16)(acc[t][j][0] * inv), o1 = (__bf16)(acc[t][j][1] * inv);
+      const __bf16 o2 = (__bf16)(acc[t][j][2] * inv), o3 = (__bf16)(acc[t][j][3] * inv);
+      uint2 wv;
+      wv.x = (uint32_t)__builtin_bit_cast(uint16_t, o0) | ((uint32_t)__builtin_bit_cast(uint16_t, o1) << 16);
+      wv.y = (uint32_t)__builtin_bit_cast(uint16_t, o2) | ((uint32_t)__builtin_bit_cast(uint16_t, o3) << 16);
+      *reinterpret_cast<uint2*>(orow + 16 * j) = wv;
+    }
   }
 }
 
-template <int D, int G>
+template <int D, int GW>
 void launch_prefill_g(const PrefillArgs& a, int32_t max_q, hipStream_t st) {
-  constexpr int BT = G >= 4 ? 16 : 64 / G;
-  constexpr int NT = 64 * G * BT / 16;
-  const dim3 grid((unsigned)((max_q + BT - 1) / BT), (unsigned)a.n_seqs, (unsigned)a.hkv);
-  hipLaunchKernelGGL((prefill_mfma_kernel<D, G, BT>), grid, dim3(NT), 0, st, a);
+  constexpr int BT = 16 * (8 / GW);
+  const int32_t halves = (a.hq / a.hkv) / GW;
+  const dim3 grid((unsigned)((max_q + BT - 1) / BT), (unsigned)a.n_seqs, (unsigned)(a.hkv * halves));
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, GW>), grid, dim3(256), 0, st, a);
 }
 
 template <int D>
@@ -264,8 +364,7 @@ void launch_prefill(const PrefillArgs& a, int32_t max_q, hipStream_t st) {
     case 1: launch_prefill_g<D, 1>(a, max_q, st); break;
     case 2: launch_prefill_g<D, 2>(a, max_q, st); break;
     case 4: launch_prefill_g<D, 4>(a, max_q, st); break;
-    case 8: launch_prefill_g<D, 8>(a, max_q, st); break;
-    default: launch_prefill_g<D, 16>(a, max_q, st); break;
+    default: launch_prefill_g<D, 8>(a, max_q, st); break;  // 8, or 16 in two halves
   }
 }
 
