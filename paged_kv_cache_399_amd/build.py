@@ -28,6 +28,10 @@ HOST_FLAGS = ["-O2", "-g", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-Wno-unus
 HIP_FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}"]
+# Per-file additions.  Prefill attention never loads a key or value past a
+# sequence's end and masks scores with -inf, never NaN; without NaN semantics
+# each fmaxf is one instruction instead of two input canonicalisations plus one.
+HIP_FILE_FLAGS = {"prefill_kernels.hip": ["-fno-honor-nans"]}
 
 
 def _run(cmd):
@@ -48,7 +52,7 @@ def build(verbose: bool = False) -> str:
         jobs.append([gxx, *HOST_FLAGS, "-c", os.path.join(CSRC, s),
                      "-o", os.path.join(BUILD, s + ".o")])
     for s in HIP_SOURCES:
-        jobs.append([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, s),
+        jobs.append([hipcc, *HIP_FLAGS, *HIP_FILE_FLAGS.get(s, []), "-c", os.path.join(CSRC, s),
                      "-o", os.path.join(BUILD, s + ".o")])
     with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         outs = list(ex.map(_run, jobs))

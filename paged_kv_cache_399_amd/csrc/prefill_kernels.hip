@@ -53,7 +53,7 @@ struct PrefillArgs {
   const int32_t* table;
   const int32_t* ctx;
   const int32_t* qstart;
-  int32_t n_seqs, hq, hkv, p, num_blocks, max_blocks;
+  int32_t n_seqs, hq, hkv, p, lp, num_blocks, max_blocks;  // p = 1 << lp
   KStrides ks;       // key cache: elements between KV heads, between tokens
   float scale_log2;  // scale * log2(e): scores are kept in log2 units
   int32_t* err;
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   const int32_t q0 = a.qstart[b];
   const int32_t n = a.qstart[b + 1] - q0;
   if (n <= 0 || tile * BT >= n) return;  // uniform over the workgroup
-  const int32_t P = a.p;
+  const int32_t P = a.p, lp = a.lp;  // block size, a power of two
   const int32_t L = a.ctx[b];
   if (L < n || (int64_t)L > (int64_t)a.max_blocks * P) {
     if (threadIdx.x == 0 && tile == 0 && hpart == 0) atomicOr(a.err, PKV_DEVERR_CONTEXT_LEN);
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   const int32_t* trow = a.table + (int64_t)b * a.max_blocks;
   const int64_t blk_stride = (int64_t)a.hkv * P * D;
   const int64_t khead = (int64_t)g * a.ks.head, vhead = (int64_t)g * P * D;
-  const int32_t last_blk = (kend - 1) / P;
+  const int32_t last_blk = (kend - 1) >> lp;
 
   // block-table window: tab[i] = physical block of logical block wb + i
   int32_t wb = 0;
@@ -193,8 +193,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
       const int p = tid + u * NT;
       const int key = p / (D / 8), dc = p % (D / 8);
       const int32_t t = min(c0 + key, kend - 1);
-      const int64_t blk = tab[t / P - wb];
-      kst[u] = load16(kc + blk * blk_stride + khead + (int64_t)(t % P) * a.ks.tok + dc * 8);
+      const int64_t blk = tab[(t >> lp) - wb];
+      kst[u] = load16(kc + blk * blk_stride + khead + (int64_t)(t & (P - 1)) * a.ks.tok + dc * 8);
     }
 #pragma unroll
     for (int u = 0; u < VU; ++u) {
@@ -202,8 +202,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
       const int dim = p / (CH / 8), qq = p % (CH / 8);
       const int32_t t0 = c0 + 8 * qq;                 // 8 keys inside one block (P % 8 == 0)
       const int32_t t = min(t0, (kend - 1) & ~7);
-      const int64_t blk = tab[t / P - wb];
-      uint4 x = load16(vc + blk * blk_stride + vhead + (int64_t)dim * P + (t % P));
+      const int64_t blk = tab[(t >> lp) - wb];
+      uint4 x = load16(vc + blk * blk_stride + vhead + (int64_t)dim * P + (t & (P - 1)));
       // keys at or past the context end: zero, so unused slots cannot leak
       const int32_t nv = t0 >= kend ? 0 : min(kend - t0, 8);
       if (nv < 8) {
@@ -284,12 +284,12 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
         m_run[t] = m_new;
       }
       const float mc = m_run[t] * c;
-      float psum = 0.f;
+      float psum = 0.f;  // of the fp32 probabilities; the products take them rounded to bf16
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const __bf16 x = (__bf16)fast_exp2(fmaf(s[e], c, -mc));
-        pb[t][e] = x;
-        psum += (float)x;
+        const float x = fast_exp2(fmaf(s[e], c, -mc));
+        pb[t][e] = (__bf16)x;
+        psum += x;
       }
       l_run[t] = fmaf(l_run[t], alpha[t], psum);
     }
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     if (more && min(c0 + 2 * CH, kend) - 1 >= (wb + TW) * P) {
       // the next chunk leaves the table window; every read of it is behind
       // the last barrier
-      wb = (c0 + CH) / P;
+      wb = (c0 + CH) >> lp;
       load_tab(wb);
       __syncthreads();
     }
@@ -392,10 +392,12 @@ extern "C" int pkv_paged_attention_prefill(void* out, const void* q, const void*
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(PKV_ERR_INVALID_ARG, "scale must be finite and positive");
   const int32_t G = num_q_heads / num_kv_heads;
-  if (dtype != PKV_BF16 || (head_dim != 64 && head_dim != 128) || block_size % 8 != 0 ||
+  const bool pow2 = block_size >= 8 && block_size <= 256 && (block_size & (block_size - 1)) == 0;
+  if (dtype != PKV_BF16 || (head_dim != 64 && head_dim != 128) || !pow2 ||
       (G != 1 && G != 2 && G != 4 && G != 8 && G != 16))
     return fail(PKV_ERR_UNSUPPORTED,
-                "prefill needs bf16, head_dim 64/128, block_size a multiple of 8, G in {1,2,4,8,16}");
+                "prefill needs bf16, head_dim 64/128, block_size a power of two in [8, 256], "
+                "G in {1,2,4,8,16}");
   if (n_seqs > 65535 || num_kv_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
   if (n_seqs == 0 || max_query_len == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !d_context_lens || !d_query_start || !d_block_table)
@@ -417,6 +419,7 @@ extern "C" int pkv_paged_attention_prefill(void* out, const void* q, const void*
   a.hq = num_q_heads;
   a.hkv = num_kv_heads;
   a.p = block_size;
+  a.lp = __builtin_ctz((unsigned)block_size);
   a.ks = pkv::k_strides(k_layout, num_kv_heads, block_size, head_dim);
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks_per_seq;
