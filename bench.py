@@ -29,8 +29,8 @@ HBM_PEAK_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="long", help="tiny|small_mha|gqa|long|prefix|beam|prefill|prefill_chunk|admission|admission_small")
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--layout", default="head_major", choices=["head_major", "token_major"],
@@ -259,7 +259,37 @@ def run_prefill(args):
     }
     if err is not None:
         result["check_max_err"] = err
+    if not args.no_cpu_baseline and args.cpu_seconds > 0:
+        result["cpu_baseline"] = prefill_cpu_baseline(w, cfg, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def prefill_cpu_baseline(w, cfg, budget_s):
+    """The float64 oracle's prefill on host cores over whole sequences until the budget is spent."""
+    from oracle import attention as oatt
+    from synth import bf16_bits
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    spent, flops, done = 0.0, 0.0, 0
+    for bi in range(cfg.batch):
+        rows = slice(bi * cfg.new, (bi + 1) * cfg.new)
+        k = np.concatenate([bf16_bits(w.ctx_k[bi * cfg.context:(bi + 1) * cfg.context]), bf16_bits(w.new_k[rows])])
+        v = np.concatenate([bf16_bits(w.ctx_v[bi * cfg.context:(bi + 1) * cfg.context]), bf16_bits(w.new_v[rows])])
+        q = bf16_bits(w.q[rows])
+        t0 = time.perf_counter()
+        oatt.prefill(q, k, v)
+        spent += time.perf_counter() - t0
+        flops += 4.0 * cfg.head_dim * cfg.num_q_heads * sum(cfg.context + i + 1 for i in range(cfg.new))
+        done += 1
+        if spent >= budget_s:
+            break
+    return {"value": round(flops / spent / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {cfg.batch} sequences, float64 numpy causal attention, {spent:.1f}s",
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count()}
 
 
 def run_admission(args):
