@@ -115,3 +115,15 @@ def test_token_major_key_layout(hq, hkv, d, p):
     assert err <= BF16_TOL
     head, _, _ = _run(hq, hkv, d, p, ctx, new, seed=p + d)
     assert torch.equal(out, head)
+
+
+@pytest.mark.parametrize("p", [8, 16])
+def test_contexts_longer_than_the_table_window(p):
+    """Contexts past 1024 blocks make the kernel move its block-table window
+    (every 1024 blocks) while it walks the keys."""
+    ctx = [9000, 300, 17000 if p == 16 else 8190]
+    new = [40, 77, 33]
+    out, ref, _ = _run(16, 4, 128, p, ctx, new, seed=p + 1)
+    err = float(np.abs(out.double().cpu().numpy() - ref).max())
+    say(f"  p={p}: max err {err:.3e}")
+    assert err <= BF16_TOL
