@@ -293,7 +293,8 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
  * Both products run on matrix cores; key/value chunks of 32 tokens are staged
  * once per workgroup in LDS and shared by a tile of queries.  Supported: bf16,
  * head_dim 64 / 128, block_size a power of two from 8 to 256, G in {1, 2, 4, 8, 16},
- * n_seqs <= 65535, 16-byte aligned q, out and caches.  A sequence whose length
+ * fewer than 2^24 workgroups (n_seqs x Hkv x query tiles of 128 / G tokens),
+ * 16-byte aligned q, out and caches.  A sequence whose length
  * is out of range is skipped (its rows unwritten) and flagged
  * (PKV_DEVERR_CONTEXT_LEN); bad table entries are clamped and flagged.
  * Errors: INVALID_ARG, UNSUPPORTED, HIP. */

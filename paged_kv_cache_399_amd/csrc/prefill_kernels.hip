@@ -54,6 +54,7 @@ struct PrefillArgs {
   const int32_t* ctx;
   const int32_t* qstart;
   int32_t n_seqs, hq, hkv, p, lp, num_blocks, max_blocks;  // p = 1 << lp
+  int32_t n_tiles;   // query tiles per sequence (ceil(max_query_len / tokens per workgroup))
   KStrides ks;       // key cache: elements between KV heads, between tokens
   float scale_log2;  // scale * log2(e): scores are kept in log2 units
   int32_t* err;
@@ -70,6 +71,8 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // How far (log2 units) a chunk's maximum score may exceed the running
 // reference before the reference moves and the accumulators are rescaled.
 constexpr float kRefSlack = 8.f;
+
+constexpr int kXcds = 8;  // accelerator complex dies (separate L2 caches) on MI355X
 
 // Pairwise reductions with lane swaps on the vector ALU: v_permlane32_swap
 // exchanges the upper half of one register with the lower half of another;
@@ -116,8 +119,18 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
 
   const int32_t G = a.hq / a.hkv;
   const int32_t halves = G / GW;
-  const int32_t b = blockIdx.y, g = blockIdx.z / halves, hpart = blockIdx.z - g * halves;
-  const int32_t tile = (int32_t)gridDim.x - 1 - (int32_t)blockIdx.x;  // last tiles first
+  // XCD-aware order: workgroup L runs on XCD L % 8.  Group (sequence, KV
+  // head, head half) j is pinned to XCD j % 8, so all query tiles that read
+  // its keys and values share one L2; an XCD runs its groups one after the
+  // other, each group's tiles last first (longest work first), so the
+  // workgroups resident on an XCD read a few groups' keys and values at once.
+  const int32_t n_groups = a.n_seqs * a.hkv * halves;
+  const int32_t xcd = (int32_t)blockIdx.x % kXcds, slot = (int32_t)blockIdx.x / kXcds;
+  const int32_t group = (slot / a.n_tiles) * kXcds + xcd;
+  if (group >= n_groups) return;  // padding of the last XCD row (uniform)
+  const int32_t tile = a.n_tiles - 1 - slot % a.n_tiles;
+  const int32_t b = group / (a.hkv * halves), gz = group - b * (a.hkv * halves);
+  const int32_t g = gz / halves, hpart = gz - g * halves;
   const int32_t q0 = a.qstart[b];
   const int32_t n = a.qstart[b + 1] - q0;
   if (n <= 0 || tile * BT >= n) return;  // uniform over the workgroup
@@ -351,11 +364,13 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
 }
 
 template <int D, int GW>
-void launch_prefill_g(const PrefillArgs& a, int32_t max_q, hipStream_t st) {
+void launch_prefill_g(PrefillArgs a, int32_t max_q, hipStream_t st) {
   constexpr int BT = 16 * (8 / GW);
-  const int32_t halves = (a.hq / a.hkv) / GW;
-  const dim3 grid((unsigned)((max_q + BT - 1) / BT), (unsigned)a.n_seqs, (unsigned)(a.hkv * halves));
-  hipLaunchKernelGGL((prefill_mfma_kernel<D, GW>), grid, dim3(256), 0, st, a);
+  const int64_t halves = (a.hq / a.hkv) / GW;
+  a.n_tiles = (max_q + BT - 1) / BT;
+  const int64_t n_groups = (int64_t)a.n_seqs * a.hkv * halves;
+  const int64_t wgs = (n_groups + kXcds - 1) / kXcds * kXcds * a.n_tiles;
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, GW>), dim3((unsigned)wgs), dim3(256), 0, st, a);
 }
 
 template <int D>
@@ -398,7 +413,13 @@ extern "C" int pkv_paged_attention_prefill(void* out, const void* q, const void*
     return fail(PKV_ERR_UNSUPPORTED,
                 "prefill needs bf16, head_dim 64/128, block_size a power of two in [8, 256], "
                 "G in {1,2,4,8,16}");
-  if (n_seqs > 65535 || num_kv_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
+  {
+    const int64_t bt = 16 * 8 / std::min<int32_t>(G, 8);
+    const int64_t groups = (int64_t)n_seqs * num_kv_heads * (G > 8 ? 2 : 1);
+    // one-dimensional grid: workgroups x 256 threads must stay below 2^32
+    if (((groups + 7) / 8 * 8) * ((max_query_len + bt - 1) / bt) >= (int64_t)1 << 24)
+      return fail(PKV_ERR_UNSUPPORTED, "grid too large (2^24 workgroups)");
+  }
   if (n_seqs == 0 || max_query_len == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !d_context_lens || !d_query_start || !d_block_table)
     return fail(PKV_ERR_INVALID_ARG, "NULL pointer");
