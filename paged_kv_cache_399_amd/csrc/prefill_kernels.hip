@@ -27,9 +27,10 @@
 // r = l / 16.  For a 32-key chunk, two 16x16x32 MFMA chains per tile produce
 // the scores of keys 8r .. 8r + 7 for query n; those eight probabilities are
 // the B operand of the value MFMA, whose A operand is the 16-byte run of the
-// token-minor value tile (dims 16 j + n, keys 8r .. 8r + 7).  The maximum and
-// the sum over a query's 32 keys cross the four row groups with two lane
-// swaps (32 apart, then 16 apart) on the vector ALU.
+// token-minor value tile (dims 16 j + n, keys 8r .. 8r + 7).  The maximum over
+// a query's 32 keys crosses the four row groups with two lane swaps (32
+// apart, then 16 apart) on the vector ALU; the sum comes from one more
+// product with an all-ones A operand.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -74,7 +75,7 @@ constexpr float kRefSlack = 8.f;
 
 constexpr int kXcds = 8;  // accelerator complex dies (separate L2 caches) on MI355X
 
-// Pairwise reductions with lane swaps on the vector ALU: v_permlane32_swap
+// Pairwise maxima with lane swaps on the vector ALU: v_permlane32_swap
 // exchanges the upper half of one register with the lower half of another;
 // with both operands equal, its two results hold the values of lanes l and
 // l ^ 32 (v_permlane16_swap: of 16-lane rows, l and l ^ 16), in the same
@@ -88,16 +89,6 @@ __device__ __forceinline__ float pair_max16(float v) {
   const uint32_t u = __builtin_bit_cast(uint32_t, v);
   const auto x = __builtin_amdgcn_permlane16_swap(u, u, false, false);
   return fmaxf(__builtin_bit_cast(float, (uint32_t)x[0]), __builtin_bit_cast(float, (uint32_t)x[1]));
-}
-__device__ __forceinline__ float pair_sum32(float v) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, v);
-  const auto x = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __builtin_bit_cast(float, (uint32_t)x[0]) + __builtin_bit_cast(float, (uint32_t)x[1]);
-}
-__device__ __forceinline__ float pair_sum16(float v) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, v);
-  const auto x = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  return __builtin_bit_cast(float, (uint32_t)x[0]) + __builtin_bit_cast(float, (uint32_t)x[1]);
 }
 
 template <int D, int GW>
@@ -252,7 +243,14 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY};
+  // Row sums on the matrix cores: an all-ones A operand turns the value
+  // product into sum_k p_k, in every row of the tile (the bf16-rounded
+  // probabilities that the numerator uses, summed in fp32).
+  f32x4 lsum[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
   const int krow_x = 8 * (nq >> 2) + (nq & 3);  // key of chain-X row nq within the chunk
 
   auto compute = [&](int buf, int32_t c0) {
@@ -297,22 +295,19 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
         m_run[t] = m_new;
       }
       const float mc = m_run[t] * c;
-      float psum = 0.f;  // of the fp32 probabilities; the products take them rounded to bf16
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = fast_exp2(fmaf(s[e], c, -mc));
-        pb[t][e] = (__bf16)x;
-        psum += x;
-      }
-      l_run[t] = fmaf(l_run[t], alpha[t], psum);
+      for (int e = 0; e < 8; ++e) pb[t][e] = (__bf16)fast_exp2(fmaf(s[e], c, -mc));
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       if (rescale[t]) {  // rare, one uniform branch
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[t][j] *= alpha[t];
+        lsum[t] *= alpha[t];
       }
     }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[t], lsum[t], 0, 0, 0);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const bf16x8 av = *reinterpret_cast<const bf16x8*>(&vl[(16 * j + nq) * VS + 8 * r]);
@@ -347,7 +342,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     if (!on[t]) continue;  // uniform
-    const float l_tot = pair_sum16(pair_sum32(l_run[t]));
+    const float l_tot = lsum[t][0];  // every row of the ones product holds the column's sum
     if (tok0[t] + nq >= n) continue;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* orow = (uint16_t*)a.out + ((int64_t)(q0 + qi[t]) * a.hq + head[t]) * D + 4 * r;
