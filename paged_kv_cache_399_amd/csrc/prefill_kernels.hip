@@ -95,7 +95,8 @@ template <int D, int GW>
 __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int NT = 256;             // threads: four waves
   constexpr int BT = 16 * (8 / GW);   // query tokens per workgroup
-  constexpr int CH = 32;              // keys per chunk
+  constexpr int NH = 2;               // 32-key halves per chunk
+  constexpr int CH = 32 * NH;         // keys per chunk
   constexpr int KI = D / 32;          // score MFMA steps over head_dim
   constexpr int NJ = D / 16;          // value MFMA output tiles over head_dim
   constexpr int KS = D + 8;           // padded LDS key row (elements)
@@ -256,31 +257,48 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   auto compute = [&](int buf, int32_t c0) {
     const uint16_t* kl = k_lds[buf];
     const uint16_t* vl = v_lds[buf];
-    f32x4 sx[2], sy[2];
+    f32x4 sx[2][NH], sy[2][NH];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) sx[t] = sy[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int i = 0; i < KI; ++i) {
-      const bf16x8 ax = *reinterpret_cast<const bf16x8*>(&kl[krow_x * KS + 32 * i + 8 * r]);
-      const bf16x8 ay = *reinterpret_cast<const bf16x8*>(&kl[(krow_x + 4) * KS + 32 * i + 8 * r]);
+      for (int h = 0; h < NH; ++h) sx[t][h] = sy[t][h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        sx[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, qf[t][i], sx[t], 0, 0, 0);
-        sy[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ay, qf[t][i], sy[t], 0, 0, 0);
+    for (int h = 0; h < NH; ++h) {
+#pragma unroll
+      for (int i = 0; i < KI; ++i) {
+        const bf16x8 ax = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x) * KS + 32 * i + 8 * r]);
+        const bf16x8 ay = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x + 4) * KS + 32 * i + 8 * r]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          sx[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, qf[t][i], sx[t][h], 0, 0, 0);
+          sy[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ay, qf[t][i], sy[t][h], 0, 0, 0);
+        }
       }
     }
-    bf16x8 pb[2];
+    bf16x8 pb[2][NH];
     float alpha[2];
     bool rescale[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      float s[8] = {sx[t][0], sx[t][1], sx[t][2], sx[t][3], sy[t][0], sy[t][1], sy[t][2], sy[t][3]};
+      float s[NH][8];
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[h][e] = sx[t][h][e];
+          s[h][e + 4] = sy[t][h][e];
+        }
       if (c0 + CH - 1 > base + tok0[t]) {  // uniform: the chunk reaches past some query's position
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s[e] = c0 + 8 * r + e <= qpos[t] ? s[e] : -INFINITY;
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s[h][e] = c0 + 32 * h + 8 * r + e <= qpos[t] ? s[h][e] : -INFINITY;
       }
-      float cm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
-                       fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+      float cm = s[0][0];
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cm = fmaxf(cm, s[h][e]);
       cm = pair_max16(pair_max32(cm));
       // The reference maximum m_run moves only when a chunk's maximum exceeds
       // it by more than 2^8 (in probability): until then probabilities are
@@ -296,7 +314,9 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
       }
       const float mc = m_run[t] * c;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[t][e] = (__bf16)fast_exp2(fmaf(s[e], c, -mc));
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[t][h][e] = (__bf16)fast_exp2(fmaf(s[h][e], c, -mc));
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -307,13 +327,19 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
       }
     }
 #pragma unroll
-    for (int t = 0; t < 2; ++t) lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[t], lsum[t], 0, 0, 0);
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+        lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[t][h], lsum[t], 0, 0, 0);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const bf16x8 av = *reinterpret_cast<const bf16x8*>(&vl[(16 * j + nq) * VS + 8 * r]);
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-        acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[t], acc[t][j], 0, 0, 0);
+      for (int h = 0; h < NH; ++h) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&vl[(16 * j + nq) * VS + 32 * h + 8 * r]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[t][h], acc[t][j], 0, 0, 0);
+      }
     }
   };
 
