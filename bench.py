@@ -170,6 +170,7 @@ def run_beam(args):
         "decode_tokens_per_s_stream": round(b / (gpu_ms_step * 1e-3), 1),
         "decode_ms": round(dec_ms, 4),
         "decode_ms_cold_median": round(cold_ms, 4),
+        "decode_ms_graph": round(graph_ms, 4),
         "GB_per_s_cold": round(dbytes / (cold_ms * 1e-3) / 1e9, 1),
         "decode_bytes_per_step": int(dbytes), "decode_unique_bytes": int(ubytes),
         "unique_GB_per_s": round(ubytes / (dec_ms * 1e-3) / 1e9, 1),
@@ -482,6 +483,19 @@ def run_decode(args, cfg, cpu):
         cold.append(c0.elapsed_time(c1))
     del scratch
     cold_ms = float(np.median(cold))
+    # timed region 4: the same decode replayed from a HIP graph (plan,
+    # partition and merge captured once), `steps` back-to-back replays
+    graph = kv.capture_attend(meta, w.q, out)
+    graph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / args.steps
+    del graph
     log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step wall, {gpu_ms_step:.3f} ms/step "
         f"on the stream, decode alone {dec_ms:.3f} ms (cold caches, median: {cold_ms:.3f} ms)")
 
@@ -529,6 +543,7 @@ def run_decode(args, cfg, cpu):
         "pct_of_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
         "decode_ms": round(dec_ms, 4),
         "decode_ms_cold_median": round(cold_ms, 4),
+        "decode_ms_graph": round(graph_ms, 4),
         "GB_per_s_cold": round(dbytes / (cold_ms * 1e-3) / 1e9, 1),
         "gpu_ms_per_step": round(gpu_ms_step, 4),
         "decode_bytes_per_step": int(dbytes),

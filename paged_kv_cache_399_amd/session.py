@@ -142,6 +142,28 @@ class PagedKVCache:
                                       m.ws_max_len, m.ws_total, scale, m.workspace, stream,
                                       self.layout)
 
+    def capture_attend(self, m, q, out, scale=None):
+        """Record one decode call (plan, partition, merge kernels) into a HIP graph.
+
+        Returns a torch CUDAGraph whose replay() reruns the decode on the same
+        buffers: q, out and m's table, lengths and workspace, read as they are
+        at replay time (the decode allocates nothing and issues no memset or
+        copy, so every replay is a pure kernel sequence).  Call attend() once
+        before capturing (one-time host set-up).  The batch must stay within
+        the sizing given to prepare(); replay() does not check it, call
+        check_graph_sizing(m) when lengths grow.
+        """
+        import torch
+        self.check_graph_sizing(m)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.attend(m, q, out, scale, stream=torch.cuda.current_stream())
+        return g
+
+    def check_graph_sizing(self, m):
+        if m.max_len > m.ws_max_len or m.total > m.ws_total:
+            raise ValueError("batch outgrew the workspace sized in prepare()")
+
     def extend(self, m, n_new, k_new, v_new, q, out, scale=None, stream=None):
         """Append n_new[i] tokens to m.seqs[i] and attend causally from each of them.
 
