@@ -1336,7 +1336,7 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   if (n_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
       num_blocks <= 0 || max_blocks_per_seq < 0 || max_context_len < 0)
     return fail(PKV_ERR_INVALID_ARG, "bad sizes");
-  if (num_q_heads % num_kv_heads) return fail(PKV_ERR_INVALID_ARG, "num_q_heads % num_kv_heads != 0");
+  if (num_q_heads % num_kv_heads) return fail(PKV_ERR_INVALID_ARG, "num_q_heads is not a multiple of num_kv_heads");
   if (num_q_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "more than 65535 query heads");
   if (!pkv::dtype_valid(dtype)) return fail(PKV_ERR_INVALID_ARG, "bad dtype");
   if (!pkv::layout_valid(k_layout)) return fail(PKV_ERR_INVALID_ARG, "bad key layout");

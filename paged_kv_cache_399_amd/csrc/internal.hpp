@@ -10,7 +10,8 @@
 namespace pkv {
 
 // Record a message for pkv_last_error() on this thread and return `code`.
-int fail(int code, const char* fmt, ...);
+// `fmt` is a printf format (checked by the compiler): a literal percent sign is "%%".
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 
 // Clear nothing; successful calls leave the last message as it was.
 inline int ok() { return PKV_OK; }

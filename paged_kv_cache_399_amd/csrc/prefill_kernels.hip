@@ -422,7 +422,7 @@ extern "C" int pkv_paged_attention_prefill(void* out, const void* q, const void*
   if (n_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
       num_blocks <= 0 || max_blocks_per_seq < 0 || max_query_len < 0)
     return fail(PKV_ERR_INVALID_ARG, "bad sizes");
-  if (num_q_heads % num_kv_heads) return fail(PKV_ERR_INVALID_ARG, "num_q_heads % num_kv_heads != 0");
+  if (num_q_heads % num_kv_heads) return fail(PKV_ERR_INVALID_ARG, "num_q_heads is not a multiple of num_kv_heads");
   if (!pkv::dtype_valid(dtype)) return fail(PKV_ERR_INVALID_ARG, "bad dtype");
   if (!pkv::layout_valid(k_layout)) return fail(PKV_ERR_INVALID_ARG, "bad key layout");
   if (!std::isfinite(scale) || !(scale > 0.f))
