@@ -275,56 +275,63 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
         }
       }
     }
-    bf16x8 pb[2][NH];
-    float alpha[2];
-    bool rescale[2];
+    float s[2][NH][8];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      float s[NH][8];
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int h = 0; h < NH; ++h)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          s[h][e] = sx[t][h][e];
-          s[h][e + 4] = sy[t][h][e];
+          s[t][h][e] = sx[t][h][e];
+          s[t][h][e + 4] = sy[t][h][e];
         }
-      if (c0 + CH - 1 > base + tok0[t]) {  // uniform: the chunk reaches past some query's position
+    // Rare cases first, each one uniform branch, so that the common path
+    // below (exponentials and both tiles' products) is one straight block.
+    if (c0 + CH - 1 > base + min(tok0[0], tok0[1])) {  // the chunk reaches past some query's position
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int h = 0; h < NH; ++h)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) s[h][e] = c0 + 32 * h + 8 * r + e <= qpos[t] ? s[h][e] : -INFINITY;
-      }
-      float cm = s[0][0];
+          for (int e = 0; e < 8; ++e) s[t][h][e] = c0 + 32 * h + 8 * r + e <= qpos[t] ? s[t][h][e] : -INFINITY;
+    }
+    float cm[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float x = s[t][0][0];
 #pragma unroll
       for (int h = 0; h < NH; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) cm = fmaxf(cm, s[h][e]);
-      cm = pair_max16(pair_max32(cm));
-      // The reference maximum m_run moves only when a chunk's maximum exceeds
-      // it by more than 2^8 (in probability): until then probabilities are
-      // at most 256, and accumulator and sum share the stale reference, so
-      // nothing needs rescaling.  Finite after the first chunk (key 0 lies in
-      // the first chunk of every query), which always moves it.
-      rescale[t] = __builtin_amdgcn_ballot_w64((cm - m_run[t]) * c > kRefSlack) != 0;  // uniform
-      alpha[t] = 1.f;
-      if (rescale[t]) {
-        const float m_new = fmaxf(m_run[t], cm);
-        alpha[t] = fast_exp2((m_run[t] - m_new) * c);
-        m_run[t] = m_new;
+        for (int e = 0; e < 8; ++e) x = fmaxf(x, s[t][h][e]);
+      cm[t] = pair_max16(pair_max32(x));
+    }
+    // The reference maximum m_run moves only when a chunk's maximum exceeds
+    // it by more than 2^8 (in probability): until then probabilities are at
+    // most 256, and accumulator and sum share the stale reference, so nothing
+    // needs rescaling.  Finite after the first chunk (key 0 lies in the first
+    // chunk of every query), which always moves it.
+    if (__builtin_amdgcn_ballot_w64((cm[0] - m_run[0]) * c > kRefSlack ||
+                                    (cm[1] - m_run[1]) * c > kRefSlack) != 0) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        if (__builtin_amdgcn_ballot_w64((cm[t] - m_run[t]) * c > kRefSlack) != 0) {  // uniform
+          const float m_new = fmaxf(m_run[t], cm[t]);
+          const float alpha = fast_exp2((m_run[t] - m_new) * c);
+          m_run[t] = m_new;
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) acc[t][j] *= alpha;
+          lsum[t] *= alpha;
+        }
       }
+    }
+    bf16x8 pb[2][NH];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
       const float mc = m_run[t] * c;
 #pragma unroll
       for (int h = 0; h < NH; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[t][h][e] = (__bf16)fast_exp2(fmaf(s[h][e], c, -mc));
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if (rescale[t]) {  // rare, one uniform branch
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[t][j] *= alpha[t];
-        lsum[t] *= alpha[t];
-      }
+        for (int e = 0; e < 8; ++e) pb[t][h][e] = (__bf16)fast_exp2(fmaf(s[t][h][e], c, -mc));
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
