@@ -73,3 +73,21 @@ def copy_block(k_cache: np.ndarray, v_cache: np.ndarray, src: int, dst: int) -> 
     """Copy-on-write: every slot of block ``src`` (all heads, K and V) to ``dst``."""
     k_cache[dst] = k_cache[src]
     v_cache[dst] = v_cache[src]
+
+
+def shared_prefix_tokens(table_a: Sequence[int], len_a: int, table_b: Sequence[int], len_b: int,
+                         block_size: int) -> int:
+    """How many leading tokens two sequences hold in the very same slots.
+
+    Source: "pagedattention" topic page, fourth paragraph, and "PagedAttention
+    Internals", "Sharing And Dynamic Growth": forked sequences point at the
+    same physical blocks until one of them writes.  Read here as the largest
+    n <= min(len_a, len_b) such that every logical token t < n has the same
+    slot in both sequences, found token by token; tokens in the same slot are
+    the same bytes, so attention may read them once for both.
+    """
+    n = 0
+    while n < min(len_a, len_b) and \
+            slot_of(table_a, block_size, n) == slot_of(table_b, block_size, n):
+        n += 1
+    return n
