@@ -37,6 +37,9 @@ def parse():
                     help="key cache order inside a block: [Hkv, P, D] or [P, Hkv, D]")
     ap.add_argument("--sweep-block-sizes", default="",
                     help="comma-separated block sizes: one decode JSON line per size (block-size study)")
+    ap.add_argument("--no-share", action="store_true",
+                    help="decode without the shared-block array (sequences that share blocks "
+                         "read them once per sequence instead of once per pack)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the CPU oracle baseline (0 = skip)")
@@ -95,7 +98,8 @@ def run_beam(args):
     w = make_beam_workload(cfg, args.seed, dev, steps=nsteps)
     b, hq, hkv, d, p = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
     s = 2 if cfg.dtype == "bf16" else 4
-    kv = PagedKVCache(w.num_blocks, p, hkv, d, w.torch_dtype, dev, w.free_order, fill=0.0)
+    kv = PagedKVCache(w.num_blocks, p, hkv, d, w.torch_dtype, dev, w.free_order, fill=0.0,
+                      share_blocks=not args.no_share)
     roots = kv.new_sequences(cfg.groups)
     slots, _ = kv.pool.append_slots(roots, w.prompt_lengths)
     kv.write_slots(torch.from_numpy(slots).to(dev), w.prompt_k, w.prompt_v)
@@ -115,7 +119,8 @@ def run_beam(args):
     copy_blocks(kv.k_cache, kv.v_cache, cow, stream)
     c1.record(stream)
     meta.max_len, meta.total = kv.pool.block_table_upload(meta.seqs, meta.max_blocks, meta.table,
-                                                          meta.lens, step_slots, meta.slots, stream)
+                                                          meta.lens, step_slots, meta.slots, stream,
+                                                          d_shared_prev=meta.shared)
     meta.uploaded = True
     from paged_kv_cache_399_amd import cache_append
     cache_append(kv.k_cache, kv.v_cache, w.step_k[0], w.step_v[0], meta.slots, stream)
@@ -163,7 +168,8 @@ def run_beam(args):
         "config": {"workload": f"{cfg.name}_decode", "groups": cfg.groups, "fanout": cfg.fanout,
                    "batch": b, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d,
                    "block_size": p, "prompt_lengths": f"uniform [{cfg.length_lo},{cfg.length_hi}]",
-                   "seed": args.seed, "parallelism": "single GPU"},
+                   "seed": args.seed, "shared_blocks_read_once_per_pack": not args.no_share,
+                   "parallelism": "single GPU"},
         "decode_tokens_per_s": round(b / (ms_step * 1e-3), 1),
         "decode_ms": round(dec_ms, 4),
         "decode_bytes_per_step": int(dbytes), "decode_unique_bytes": int(ubytes),
@@ -369,7 +375,7 @@ def run_decode(args, cfg, cpu):
     b, hq, hkv, d, p = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
     s = 2 if cfg.dtype == "bf16" else 4
     kv = PagedKVCache(w.num_blocks, p, hkv, d, w.torch_dtype, dev, w.free_order, fill=0.0,
-                      layout=args.layout)
+                      layout=args.layout, share_blocks=not args.no_share)
     if cfg.prefix_len:
         root = kv.new_sequences(1)[0]
         kv.write([root], [cfg.prefix_len], w.prefix_k, w.prefix_v)
@@ -516,7 +522,8 @@ def run_decode(args, cfg, cpu):
             "head_dim": d, "block_size": p, "context_tokens": int(base.sum()),
             "max_context": int(base.max()), "seed": args.seed,
             "lengths": cfg.length_rule + (f" [{cfg.length_lo},{cfg.length_hi}]" if cfg.length_hi else ""),
-            "prefix_len": cfg.prefix_len, "k_layout": args.layout, "parallelism": "single GPU",
+            "prefix_len": cfg.prefix_len, "k_layout": args.layout,
+            "shared_blocks_read_once_per_pack": not args.no_share, "parallelism": "single GPU",
         },
         "decode_tokens_per_s": round(b / (ms_step * 1e-3), 1),
         "decode_tokens_per_s_stream": round(b / (gpu_ms_step * 1e-3), 1),

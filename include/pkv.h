@@ -162,12 +162,33 @@ int pkv_pool_stats(pkv_pool* pool, pkv_stats* out);
 int pkv_pool_export(pkv_pool* pool, int32_t* free_order_out, int32_t* refcount_out,
                     int32_t* n_free_out);
 
+/* Tokens each sequence holds in the same physical blocks as the one before it
+ * in `seqs` (forks share blocks: "pagedattention" topic page, fourth
+ * paragraph; "Sharing And Dynamic Growth"): for i >= 1, the leading table
+ * entries seqs[i-1] and seqs[i] have in common times block_size, limited to
+ * both lengths; entry 0 is 0.  The same counts pkv_block_table_upload writes
+ * to d_shared_prev.
+ *   shared_out            host int32[n_seqs], or NULL
+ *   unshared_tokens_out   host, or NULL: sum over i of length_i - shared_i,
+ *                         the tokens a decode that reads shared blocks once
+ *                         per pack still streams (a sizing hint for
+ *                         pkv_paged_attention_decode)
+ * Host only.  Errors: INVALID_ARG, BAD_SEQ (nothing written then). */
+int pkv_seq_shared_prefix(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs, int32_t* shared_out,
+                          int64_t* unshared_tokens_out);
+
 /* Bring a device block table, its context lengths and (optionally) a slot
  * mapping up to date with the pool ("The Block Table Map": the table records
  * each new block as the sequence grows):
  *   d_block_table   device int32[n_seqs * max_blocks_per_seq]; row i belongs
  *                   to seqs[i], entries beyond the sequence's blocks are -1
  *   d_context_lens  device int32[n_seqs]
+ *   d_shared_prev   optional device int32[n_seqs] (NULL to skip): entry i >= 1
+ *                   receives the number of leading tokens seqs[i] holds in
+ *                   the same physical blocks as seqs[i-1] (forked sequences,
+ *                   "Sharing And Dynamic Growth"): the common leading table
+ *                   entries times block_size, limited to both lengths.  Entry
+ *                   0 is 0.  pkv_paged_attention_decode reads it.
  *   slot_mapping / d_slot_mapping / n_slots: optional (host int32[n_slots] ->
  *                   device int32[n_slots]) copy of a slot mapping in the same
  *                   round; pass NULL/NULL/0 to skip.
@@ -177,11 +198,13 @@ int pkv_pool_export(pkv_pool* pool, int32_t* free_order_out, int32_t* refcount_o
  *             reused only after the copy that last read it has completed).
  *          PKV_UPLOAD_INCREMENTAL: the caller asserts that d_block_table
  *             still holds what this pool last uploaded to that address (with
- *             the same max_blocks_per_seq).  Rows that hold the same sequence
- *             as then, with no copy-on-write since, receive only their new
- *             entries; other rows are rewritten.  Lengths, slots and entries
- *             travel in the arguments of small patch kernels: no staging and
- *             no host-to-device copy.  Falls back to a full upload when the
+ *             the same max_blocks_per_seq), and that d_shared_prev, if it is
+ *             the array passed last time, was not written since.  Rows that
+ *             hold the same sequence as then, with no copy-on-write since,
+ *             receive only their new entries; other rows are rewritten.
+ *             Lengths, slots, entries and changed shared-token counts travel
+ *             in the arguments of small patch kernels: no staging and no
+ *             host-to-device copy.  Falls back to a full upload when the
  *             patch would be large (or nothing was uploaded there before).
  * The pool records, per device table address and row, what it wrote.  All
  * device work is enqueued on `stream`; the host may return before it runs.
@@ -190,8 +213,8 @@ int pkv_pool_export(pkv_pool* pool, int32_t* free_order_out, int32_t* refcount_o
 #define PKV_UPLOAD_INCREMENTAL 1
 int pkv_block_table_upload(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs,
                            int32_t max_blocks_per_seq, int32_t* d_block_table,
-                           int32_t* d_context_lens, const int32_t* slot_mapping,
-                           int32_t* d_slot_mapping, int32_t n_slots,
+                           int32_t* d_context_lens, int32_t* d_shared_prev,
+                           const int32_t* slot_mapping, int32_t* d_slot_mapping, int32_t n_slots,
                            int32_t* max_context_len_out, int64_t* total_tokens_out,
                            int32_t flags, void* stream);
 
@@ -226,7 +249,8 @@ int pkv_cache_append(void* k_cache, void* v_cache, const void* k_new, const void
 int pkv_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                int32_t head_dim, int32_t block_size,
                                int32_t max_context_len, int64_t total_context_tokens,
-                               pkv_dtype dtype, size_t* bytes_out);
+                               int64_t unshared_context_tokens, pkv_dtype dtype,
+                               size_t* bytes_out);
 
 /* Paged decode attention ("The Block Table Map": attention follows each
  * sequence's table to its keys and values).  For sequence b, query head h,
@@ -238,8 +262,31 @@ int pkv_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_
  *   k_cache, v_cache device, layout above, dtype
  *   d_block_table    device int32[n_seqs * max_blocks_per_seq]
  *   d_context_lens   device int32[n_seqs], 0 <= L <= max_blocks_per_seq * P
+ *   d_shared_prev    NULL, or device int32[n_seqs]: entry b >= 1 is a number
+ *                    of leading tokens that sequence b holds in the same
+ *                    physical blocks as sequence b-1, as pkv_block_table_upload
+ *                    writes it (entry 0 is ignored; values are clamped to
+ *                    [0, min(L_b, L_{b-1})]).  The matrix-core kernel then
+ *                    packs up to 16 / G consecutive sharing sequences and
+ *                    reads the 32-token chunks they all share once for the
+ *                    pack ("pagedattention" topic page, fourth paragraph:
+ *                    forks share blocks): one unit per whole shared partition
+ *                    plus one for a shared piece of the next.  With shared
+ *                    lengths that are whole partitions the result is
+ *                    bit-identical to a call with NULL and the same sizing
+ *                    arguments (which fix T); otherwise the partition split by
+ *                    the end of the shared tokens is summed as two partials.
+ *                    The tables are not
+ *                    compared: a count larger than the true shared prefix makes
+ *                    that sequence read its predecessor's tokens (in bounds).
+ *                    PKV_DECODE_SHARE=off ignores the array.
  *   max_context_len  >= every L (host knowledge, used for sizing)
  *   total_context_tokens  sum of L, or -1 if unknown (sizing only)
+ *   unshared_context_tokens  sum of L minus the shared counts (as
+ *                    pkv_seq_shared_prefix gives it), or -1 if unknown
+ *                    (sizing only).  A value equal to total_context_tokens
+ *                    (nothing shared) sizes the workspace without room for
+ *                    packs, and the call then ignores d_shared_prev.
  *   workspace        device, >= pkv_decode_workspace_bytes(...) bytes,
  *                    caller-owned scratch for one call at a time: calls that
  *                    share a workspace must be ordered (same stream)
@@ -251,8 +298,8 @@ int pkv_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_
  * several partitions are combined by a merge kernel.  The summation order
  * depends only on logical positions, T and the wave split, so results do not
  * depend on where the blocks sit.  Arithmetic is fp32.  Kernel per shape:
- *   - bf16, head_dim 64/128, block_size 8/16/32, 2 <= G <= 16: matrix cores
- *     (score and value products as 16x16x32 bf16 MFMA, head group as N);
+ *   - bf16, head_dim 64/128, block_size 1, 2, 4, ..., 64, 2 <= G <= 16: matrix
+ *     cores (score and value products as 16x16x32 bf16 MFMA, head group as N);
  *   - G <= 4 (including multi-head, G = 1) or fp32, head_dim 64/128,
  *     block_size * element size a multiple of 16 bytes: vector ALU with DPP
  *     row reductions;
@@ -268,11 +315,13 @@ int pkv_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_
  * lengths are clamped in-bounds and flagged. */
 int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
                                const void* v_cache, const int32_t* d_block_table,
-                               const int32_t* d_context_lens, int32_t n_seqs,
+                               const int32_t* d_context_lens, const int32_t* d_shared_prev,
+                               int32_t n_seqs,
                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                int32_t block_size, int32_t num_blocks,
                                int32_t max_blocks_per_seq, int32_t max_context_len,
-                               int64_t total_context_tokens, float scale, pkv_dtype dtype,
+                               int64_t total_context_tokens, int64_t unshared_context_tokens,
+                               float scale, pkv_dtype dtype,
                                pkv_layout k_layout, void* workspace, size_t workspace_bytes,
                                void* stream);
 
@@ -290,7 +339,7 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
  *   d_query_start     device int32[n_seqs + 1], nondecreasing, starting at 0
  *   d_context_lens    device int32[n_seqs], n_b <= L_b <= max_blocks_per_seq * P
  *   max_query_len     >= every n_b (host knowledge, sizes the grid)
- * Both products run on matrix cores; key/value chunks of 32 tokens are staged
+ * Both products run on matrix cores; key/value chunks of 64 tokens are staged
  * once per workgroup in LDS and shared by a tile of queries.  Supported: bf16,
  * head_dim 64 / 128, block_size a power of two from 8 to 256, G in {1, 2, 4, 8, 16},
  * fewer than 2^24 workgroups (n_seqs x Hkv x query tiles of 128 / G tokens),

@@ -170,13 +170,24 @@ class BlockPool:
         _check(lib.pkv_pool_export(self._h, _p32(free), _p32(ref), C.byref(nf)))
         return free[:nf.value].copy(), ref
 
+    def shared_prefix(self, seqs: Sequence[int]) -> Tuple[np.ndarray, int]:
+        """(tokens each sequence holds in the previous one's blocks, unshared total)."""
+        s = _i64_array(seqs)
+        sh = np.empty(max(len(s), 1), dtype=np.int32)
+        un = C.c_int64()
+        _check(lib.pkv_seq_shared_prefix(self._h, _p64(s), len(s), _p32(sh), C.byref(un)))
+        return sh[:len(s)].copy(), un.value
+
     def block_table_upload(self, seqs: Sequence[int], max_blocks: int, d_block_table,
                            d_context_lens, slot_mapping=None, d_slot_mapping=None,
-                           stream=None, incremental: bool = False) -> Tuple[int, int]:
+                           stream=None, incremental: bool = False,
+                           d_shared_prev=None) -> Tuple[int, int]:
         """Upload the padded block table and lengths; returns (max length, total tokens).
 
         ``incremental=True`` sends only what changed since this pool's last upload
         to the same device table (see PKV_UPLOAD_INCREMENTAL in pkv.h).
+        ``d_shared_prev`` (device int32 [n_seqs], optional) receives, per
+        sequence, the leading tokens it holds in the previous sequence's blocks.
         """
         import torch
         s = _i64_array(seqs)
@@ -184,6 +195,9 @@ class BlockPool:
             raise TypeError("block table and lengths must be int32")
         if d_block_table.numel() < len(s) * max_blocks or d_context_lens.numel() < len(s):
             raise ValueError("device buffers too small")
+        if d_shared_prev is not None and (d_shared_prev.dtype != torch.int32 or
+                                          d_shared_prev.numel() < len(s)):
+            raise ValueError("d_shared_prev must be an int32 device tensor of n_seqs entries")
         n_slots = 0
         hs = None
         if slot_mapping is not None:
@@ -196,7 +210,9 @@ class BlockPool:
         tot = C.c_int64()
         _check(lib.pkv_block_table_upload(
             self._h, _p64(s), len(s), int(max_blocks), _dev(d_block_table, "block table"),
-            _dev(d_context_lens, "context lengths"), None if hs is None else _p32(hs),
+            _dev(d_context_lens, "context lengths"),
+            None if d_shared_prev is None else _dev(d_shared_prev, "shared tokens"),
+            None if hs is None else _p32(hs),
             None if hs is None else _dev(d_slot_mapping, "slot mapping"), n_slots,
             C.byref(mx), C.byref(tot), _lib.UPLOAD_INCREMENTAL if incremental else 0,
             _stream_ptr(stream)))
@@ -253,23 +269,27 @@ def cache_append(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None,
 
 def decode_workspace_bytes(n_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                            block_size: int, max_context_len: int, total_context_tokens: int = -1,
-                           dtype=None) -> int:
+                           dtype=None, unshared_context_tokens: int = -1) -> int:
     import torch
     dt = _lib.BF16 if dtype in (None, torch.bfloat16) else _lib.F32
     out = C.c_size_t()
     _check(lib.pkv_decode_workspace_bytes(n_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                                          max_context_len, total_context_tokens, dt, C.byref(out)))
+                                          max_context_len, total_context_tokens,
+                                          unshared_context_tokens, dt, C.byref(out)))
     return out.value
 
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens,
                            max_context_len: int, total_context_tokens: int = -1,
                            scale: Optional[float] = None, workspace=None, stream=None,
-                           layout="head_major"):
+                           layout="head_major", shared_prev=None,
+                           unshared_context_tokens: int = -1):
     """Decode attention over the paged cache; writes ``out`` [B, Hq, D] and returns it.
 
     ``workspace`` is a uint8 device tensor of at least decode_workspace_bytes(...)
-    bytes; if None one is allocated with torch (plumbing only).
+    bytes; if None one is allocated with torch (plumbing only).  ``shared_prev``
+    (device int32 [B], as block_table_upload writes it) lets sequences that
+    share blocks read them once per pack; the output is the same.
     """
     import torch
     nb, hkv, bs, d, lay = _cache_shape(k_cache, v_cache, layout)
@@ -282,19 +302,23 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens,
         raise ValueError("block_table must be int32 [n_seqs, max_blocks_per_seq]")
     if context_lens.dtype != torch.int32 or context_lens.numel() != b:
         raise ValueError("context_lens must be int32 [n_seqs]")
+    if shared_prev is not None and (shared_prev.dtype != torch.int32 or shared_prev.numel() != b):
+        raise ValueError("shared_prev must be int32 [n_seqs]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dt = _dtype_code(q)
     need = decode_workspace_bytes(b, hq, hkv, d, bs, max_context_len, total_context_tokens,
-                                  q.dtype)
+                                  q.dtype, unshared_context_tokens)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if workspace.numel() < need:
         raise ValueError(f"workspace has {workspace.numel()} bytes, {need} needed")
     _check(lib.pkv_paged_attention_decode(
         _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-        _dev(block_table, "block_table"), _dev(context_lens, "context_lens"), b, hq, hkv, d, bs,
-        nb, block_table.shape[1], int(max_context_len), int(total_context_tokens), float(scale),
+        _dev(block_table, "block_table"), _dev(context_lens, "context_lens"),
+        None if shared_prev is None else _dev(shared_prev, "shared_prev"), b, hq, hkv, d, bs,
+        nb, block_table.shape[1], int(max_context_len), int(total_context_tokens),
+        int(unshared_context_tokens), float(scale),
         dt, lay, _dev(workspace, "workspace"), workspace.numel(), _stream_ptr(stream)))
     return out
 

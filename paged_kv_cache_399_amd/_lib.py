@@ -52,15 +52,16 @@ SIGNATURES = {
     "pkv_seq_get_table": (C.c_int, [_vp, _i64, _pi32, _i32, _pi32, _pi64]),
     "pkv_pool_stats": (C.c_int, [_vp, C.POINTER(Stats)]),
     "pkv_pool_export": (C.c_int, [_vp, _pi32, _pi32, _pi32]),
-    "pkv_block_table_upload": (C.c_int, [_vp, _pi64, _i32, _i32, _vp, _vp, _pi32, _vp, _i32,
+    "pkv_seq_shared_prefix": (C.c_int, [_vp, _pi64, _i32, _pi32, _pi64]),
+    "pkv_block_table_upload": (C.c_int, [_vp, _pi64, _i32, _i32, _vp, _vp, _vp, _pi32, _vp, _i32,
                                          _pi32, _pi64, _i32, _vp]),
     "pkv_copy_blocks": (C.c_int, [_vp, _vp, _pi32, _i32, _i32, _i32, _i32, _i32, C.c_int, _vp]),
     "pkv_cache_append": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                    C.c_int, C.c_int, _vp]),
-    "pkv_decode_workspace_bytes": (C.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i64, C.c_int,
-                                             C.POINTER(C.c_size_t)]),
-    "pkv_paged_attention_decode": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
-                                             _i32, _i32, _i32, _i32, _i64, C.c_float, C.c_int,
+    "pkv_decode_workspace_bytes": (C.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i64, _i64,
+                                             C.c_int, C.POINTER(C.c_size_t)]),
+    "pkv_paged_attention_decode": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                             _i32, _i32, _i32, _i32, _i64, _i64, C.c_float, C.c_int,
                                              C.c_int, _vp, C.c_size_t, _vp]),
     "pkv_paged_attention_prefill": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                               _i32, _i32, _i32, _i32, _i32, C.c_float, C.c_int,

@@ -49,6 +49,8 @@ struct pkv_pool {
   struct TableRecord {
     int32_t max_blocks = 0;
     std::vector<RowRecord> rows;
+    const int32_t* shared_dev = nullptr;  // shared-token array written with this table
+    std::vector<int32_t> shared_sent;     // what it holds
   };
   pkv::BlockPool pool;
   Stage stage[2];
@@ -187,16 +189,59 @@ int pkv_pool_export(pkv_pool* pool, int32_t* free_order_out, int32_t* refcount_o
   PKV_TRY_END
 }
 
+}  // extern "C"
+
 namespace {
 
-// Full upload: the padded table, the lengths and the slot mapping through one
-// pinned staging round (double-buffered, reused after its copies finished).
+// Tokens sequence b holds in the same physical blocks as sequence a: the
+// leading table entries they have in common, limited to both lengths (equal
+// block ids mean the same slots, so those tokens are the same bytes).
+int32_t shared_tokens(const pkv::BlockPool& bp, int64_t a, int64_t b) {
+  const std::vector<int32_t>& ta = bp.table(a);
+  const std::vector<int32_t>& tb = bp.table(b);
+  const size_t n = std::min(ta.size(), tb.size());
+  const size_t k = (size_t)(std::mismatch(ta.begin(), ta.begin() + n, tb.begin()).first - ta.begin());
+  return (int32_t)std::min<int64_t>({(int64_t)k * bp.block_size(), bp.length(a), bp.length(b)});
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_seq_shared_prefix(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs, int32_t* shared_out,
+                          int64_t* unshared_tokens_out) {
+  PKV_TRY_BEGIN
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "NULL pool");
+  if (n_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "negative size");
+  if (n_seqs > 0 && !seqs) return fail(PKV_ERR_INVALID_ARG, "NULL sequence list");
+  const pkv::BlockPool& bp = pool->pool;
+  for (int32_t i = 0; i < n_seqs; ++i)
+    if (!bp.live(seqs[i])) return fail(PKV_ERR_BAD_SEQ, "sequence %lld is not live", (long long)seqs[i]);
+  int64_t unshared = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const int32_t sh = i ? shared_tokens(bp, seqs[i - 1], seqs[i]) : 0;
+    if (shared_out) shared_out[i] = sh;
+    unshared += bp.length(seqs[i]) - sh;
+  }
+  if (unshared_tokens_out) *unshared_tokens_out = unshared;
+  return PKV_OK;
+  PKV_TRY_END
+}
+
+}  // extern "C"
+
+namespace {
+
+// Full upload: the padded table, the lengths, the shared-token counts and the
+// slot mapping through one pinned staging round (double-buffered, reused after
+// its copies finished).
 int upload_full(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs, int32_t max_blocks,
-                int32_t* d_table, int32_t* d_lens, const int32_t* slot_mapping, int32_t* d_slots,
-                int32_t n_slots, hipStream_t st) {
+                int32_t* d_table, int32_t* d_lens, int32_t* d_shared, const int32_t* shared,
+                const int32_t* slot_mapping, int32_t* d_slots, int32_t n_slots, hipStream_t st) {
   const pkv::BlockPool& bp = pool->pool;
   const size_t table_words = (size_t)n_seqs * max_blocks;
-  const size_t need = (table_words + n_seqs + n_slots) * sizeof(int32_t);
+  const size_t n_sh = d_shared ? (size_t)n_seqs : 0;
+  const size_t need = (table_words + n_seqs + n_sh + n_slots) * sizeof(int32_t);
   if (need == 0) return PKV_OK;
   pkv_pool::Stage& sg = pool->stage[pool->next];
   if (sg.pending) {
@@ -228,13 +273,16 @@ int upload_full(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs, int32_t max
   }
   int32_t* tab = (int32_t*)sg.host;
   int32_t* lens = tab + table_words;
-  int32_t* slots = lens + n_seqs;
+  int32_t* sh = lens + n_seqs;
+  int32_t* slots = sh + n_sh;
   std::memcpy(tab, b.data(), (table_words + n_seqs) * sizeof(int32_t));
+  if (n_sh) std::memcpy(sh, shared, n_sh * sizeof(int32_t));
   if (n_slots) std::memcpy(slots, slot_mapping, (size_t)n_slots * sizeof(int32_t));
   hipError_t e = hipSuccess;
   if (table_words) e = hipMemcpyAsync(d_table, tab, table_words * 4, hipMemcpyHostToDevice, st);
   if (e == hipSuccess && n_seqs)
     e = hipMemcpyAsync(d_lens, lens, (size_t)n_seqs * 4, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess && n_sh) e = hipMemcpyAsync(d_shared, sh, n_sh * 4, hipMemcpyHostToDevice, st);
   if (e == hipSuccess && n_slots)
     e = hipMemcpyAsync(d_slots, slots, (size_t)n_slots * 4, hipMemcpyHostToDevice, st);
   if (e == hipSuccess) e = hipEventRecord(sg.done, st);
@@ -250,9 +298,12 @@ constexpr size_t kMaxPatchLaunches = 16;
 
 }  // namespace
 
+extern "C" {
+
 int pkv_block_table_upload(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs,
                            int32_t max_blocks_per_seq, int32_t* d_block_table,
-                           int32_t* d_context_lens, const int32_t* slot_mapping,
+                           int32_t* d_context_lens, int32_t* d_shared_prev,
+                           const int32_t* slot_mapping,
                            int32_t* d_slot_mapping, int32_t n_slots,
                            int32_t* max_context_len_out, int64_t* total_tokens_out,
                            int32_t flags, void* stream) {
@@ -279,19 +330,29 @@ int pkv_block_table_upload(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs,
     longest = std::max<int32_t>(longest, (int32_t)L);
   }
   hipStream_t st = (hipStream_t)stream;
+  std::vector<int32_t> shared;
+  if (d_shared_prev) {
+    shared.assign(n_seqs, 0);
+    for (int32_t i = 1; i < n_seqs; ++i) shared[i] = shared_tokens(bp, seqs[i - 1], seqs[i]);
+  }
 
   // Incremental: rows whose record names the same sequence at the same
   // copy-on-write epoch get only their new entries; other rows are rewritten
-  // (entries plus -1 padding).  Lengths and slots are always sent.
+  // (entries plus -1 padding).  Lengths and slots are always sent, the
+  // shared-token counts when they differ from what this array last received.
   bool full = !(flags & PKV_UPLOAD_INCREMENTAL) || n_seqs == 0;
   std::vector<int32_t> ent, rst;
   auto rec_it = pool->tables.find(d_block_table);
   if (!full && (rec_it == pool->tables.end() || rec_it->second.max_blocks != max_blocks_per_seq))
     full = true;
+  bool send_shared = d_shared_prev != nullptr;
+  if (!full && send_shared && rec_it->second.shared_dev == d_shared_prev &&
+      rec_it->second.shared_sent == shared)
+    send_shared = false;
   if (!full) {
     const std::vector<pkv_pool::RowRecord>& rows = rec_it->second.rows;
     const size_t budget = kMaxPatchLaunches * pkv::kPatchWords;
-    size_t words = (size_t)n_seqs + n_slots;
+    size_t words = (size_t)n_seqs + n_slots + (send_shared ? n_seqs : 0);
     for (int32_t i = 0; i < n_seqs && !full; ++i) {
       const std::vector<int32_t>& t = bp.table(seqs[i]);
       const int32_t n = (int32_t)t.size();
@@ -315,18 +376,20 @@ int pkv_block_table_upload(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs,
   }
   if (full) {
     int rc = upload_full(pool, seqs, n_seqs, max_blocks_per_seq, d_block_table, d_context_lens,
-                         slot_mapping, d_slot_mapping, n_slots, st);
+                         d_shared_prev, shared.data(), slot_mapping, d_slot_mapping, n_slots, st);
     if (rc) return rc;
   } else {
     // pack lengths, slots, entries and resets into kernel-argument patches
     pkv::TablePatchArgs a;
     const int32_t n_ent = (int32_t)(ent.size() / 3), n_rst = (int32_t)(rst.size() / 2);
-    int32_t li = 0, si = 0, ei = 0, ri = 0;
-    while (li < n_seqs || si < n_slots || ei < n_ent || ri < n_rst) {
+    const int32_t n_sh = send_shared ? n_seqs : 0;
+    int32_t li = 0, hi = 0, si = 0, ei = 0, ri = 0;
+    while (li < n_seqs || hi < n_sh || si < n_slots || ei < n_ent || ri < n_rst) {
       std::memset(&a, 0, offsetof(pkv::TablePatchArgs, w));
       a.table = d_block_table;
       a.lens = d_context_lens;
       a.slots = d_slot_mapping;
+      a.shared = d_shared_prev;
       a.max_blocks = max_blocks_per_seq;
       int32_t room = pkv::kPatchWords;
       a.len0 = li;
@@ -334,12 +397,17 @@ int pkv_block_table_upload(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs,
       for (int32_t k = 0; k < a.n_len; ++k) a.w[k] = (int32_t)bp.length(seqs[li + k]);
       li += a.n_len;
       room -= a.n_len;
+      a.sh0 = hi;
+      a.n_sh = std::min(room, n_sh - hi);
+      if (a.n_sh) std::memcpy(a.w + a.n_len, shared.data() + hi, (size_t)a.n_sh * 4);
+      hi += a.n_sh;
+      room -= a.n_sh;
       a.slot0 = si;
       a.n_slot = std::min(room, n_slots - si);
-      if (a.n_slot) std::memcpy(a.w + a.n_len, slot_mapping + si, (size_t)a.n_slot * 4);
+      if (a.n_slot) std::memcpy(a.w + a.n_len + a.n_sh, slot_mapping + si, (size_t)a.n_slot * 4);
       si += a.n_slot;
       room -= a.n_slot;
-      int32_t* e = a.w + a.n_len + a.n_slot;
+      int32_t* e = a.w + a.n_len + a.n_sh + a.n_slot;
       a.n_ent = std::min(room / 3, n_ent - ei);
       if (a.n_ent) std::memcpy(e, ent.data() + 3 * (size_t)ei, (size_t)a.n_ent * 12);
       ei += a.n_ent;
@@ -360,6 +428,10 @@ int pkv_block_table_upload(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs,
       tr.rows[i].seq = seqs[i];
       tr.rows[i].blocks = (int32_t)bp.table(seqs[i]).size();
       tr.rows[i].epoch = bp.epoch(seqs[i]);
+    }
+    if (d_shared_prev) {
+      tr.shared_dev = d_shared_prev;
+      tr.shared_sent = shared;
     }
   }
   if (max_context_len_out) *max_context_len_out = longest;

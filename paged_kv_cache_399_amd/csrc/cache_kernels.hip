@@ -237,8 +237,9 @@ __global__ __launch_bounds__(256) void table_patch_kernel(TablePatchArgs p) {
   const int32_t tid = threadIdx.x, nth = blockDim.x;
   const int32_t* w = p.w;
   for (int32_t i = tid; i < p.n_len; i += nth) p.lens[p.len0 + i] = w[i];
-  for (int32_t i = tid; i < p.n_slot; i += nth) p.slots[p.slot0 + i] = w[p.n_len + i];
-  const int32_t* e = w + p.n_len + p.n_slot;
+  for (int32_t i = tid; i < p.n_sh; i += nth) p.shared[p.sh0 + i] = w[p.n_len + i];
+  for (int32_t i = tid; i < p.n_slot; i += nth) p.slots[p.slot0 + i] = w[p.n_len + p.n_sh + i];
+  const int32_t* e = w + p.n_len + p.n_sh + p.n_slot;
   for (int32_t i = tid; i < p.n_ent; i += nth)
     p.table[(int64_t)e[3 * i] * p.max_blocks + e[3 * i + 1]] = e[3 * i + 2];
   const int32_t* r = e + 3 * p.n_ent;

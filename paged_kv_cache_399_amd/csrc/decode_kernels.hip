@@ -9,30 +9,42 @@
 //      V[t,g] = v_cache[table[b][t/P], g, :, t%P].
 //
 // Work decomposition.  A sequence's tokens are cut into partitions of T
-// tokens (T a power of two, chosen on the host from the batch's size).  One
-// wavefront handles one (partition, KV head) unit and all G query heads that
-// share that KV head, so each key/value byte is read from HBM exactly once.
-// A small plan kernel lays the units out: full partitions first, the shorter
-// last partitions of every sequence at the end of the grid, so the tail of
-// the launch is made of short units.  A sequence with one partition writes its
-// output directly; otherwise each partition writes (max, sum, normalised
-// output) in fp32 and the merge kernel combines them.  Summation order depends
-// only on logical token positions and T, never on where the blocks sit.
+// tokens (T a power of two, chosen on the host from the batch's size).  A
+// workgroup of W waves handles one (partition, KV head) unit and all G query
+// heads that share that KV head, so each key/value byte is read from HBM
+// once per unit.  A small plan kernel lays the units out: full partitions
+// first, the shorter last partitions of every sequence at the end of the
+// grid, longest first.  A sequence with one partition writes its output
+// directly; otherwise each partition writes (max, sum, normalised output) in
+// fp32 to the sequence's partition slot and the merge kernel combines them.
+// Summation order depends only on logical token positions, T and W, never on
+// where the blocks sit.
 //
-// Two partition kernels:
-//  * decode_mfma_kernel (bf16, head_dim 64/128, block size 8/16/32, G <= 16):
+// Shared blocks ("pagedattention" topic page, fourth paragraph; "PagedAttention
+// Internals", "Sharing And Dynamic Growth": forked sequences point at the same
+// physical blocks).  When the caller says how many leading tokens each
+// sequence holds in the same blocks as the one before it, the plan packs up
+// to 16 / G consecutive sharing sequences into one unit for each whole
+// partition they share: the matrix-core kernel then gives each packed
+// sequence's query heads their own MFMA columns and reads the shared keys and
+// values once for the pack.  Each column's arithmetic is what its own unit
+// would do, so results are bit-identical with or without packing.
+//
+// Partition kernels:
+//  * decode_mfma_kernel (bf16, head_dim 64/128, block size 1..64, G <= 16):
 //    scores and the value product run on v_mfma_f32_16x16x32_bf16 with the
-//    head group as the 16-wide N dimension (padded with zero queries).  Each
-//    lane loads exactly the 16-byte operand fragments it feeds to the matrix
-//    core straight from HBM (keys token-major, values token-minor), with the
-//    next 32-token chunk's loads in flight while the current one is computed.
-//    The score fragment a lane receives is already the probability fragment
-//    it must feed to the value product, so no data moves between lanes except
-//    for the two-step max / sum reductions across the four 16-lane rows.
-//  * decode_valu_kernel (any dtype / shape within limits): one token per lane
-//    for scores, one head_dim element per lane for the value product, wave
-//    reductions for max and sum.  Used for fp32, for single-head groups and
-//    for shapes the matrix-core kernel does not cover.
+//    head group (or a pack's head groups) as the 16-wide N dimension, padded
+//    with zero queries.  Each lane loads exactly the 16-byte operand fragments
+//    it feeds to the matrix core straight from HBM (keys token-major, values
+//    token-minor), with the next 32-token chunk's loads in flight while the
+//    current one is computed.  The score fragment a lane receives is already
+//    the probability fragment it must feed to the value product, so no data
+//    moves between lanes except for the max / sum reductions across the four
+//    16-lane rows.
+//  * decode_dpp_kernel (G <= 4, bf16 or fp32, head_dim 64/128): vector ALU,
+//    DPP row reductions; multi-head attention and fp32 data.
+//  * decode_valu_kernel (any other shape within limits): one token per lane
+//    for scores, one head_dim element per lane for the value product.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -53,11 +65,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct Plan {
-  int32_t* counts;     // [0] units to run (0 if the plan overflowed), [1] full units
-  int32_t* seq_info;   // [3 * n_seqs]: first full row, number of full rows, ragged row or -1
-  int4* work;          // [max_units]: (sequence, first token, end token, partitions of the sequence)
-  float* part_ml;      // [max_units * Hq * 2]: running max (log2 units), sum
-  float* part_o;       // [max_units * Hq * D]: normalised partial output
+  int32_t* counts;     // [0] units to run (0 if the plan overflowed), [1] full-length units
+  int4* seq_info;      // [n_seqs]: (first slot, partials, partitions, unused); slots are contiguous
+  int2* seq_pack;      // [n_seqs]: (tokens its pack shares or 0, pack size if it leads a pack else 0)
+  int4* work;          // [max_units]: (sequence, first token, end token, sequences in the pack)
+  int2* work_out;      // [max_units]: (partial slot, partials) of the unit's first sequence
+  float* part_ml;      // [max_units * Hq * 2] per slot: running max (log2 units), sum
+  float* part_o;       // [max_units * Hq * D] per slot: normalised partial output
 };
 
 struct DecodeArgs {
@@ -67,7 +81,9 @@ struct DecodeArgs {
   const void* vc;
   const int32_t* table;
   const int32_t* ctx;
+  const int32_t* shared;  // tokens each sequence holds in its predecessor's blocks, or null
   int32_t n_seqs, hq, hkv, d, p, num_blocks, max_blocks, part_tokens, max_units;
+  int32_t pack_max;  // sequences one unit may take (1: no packing)
   KStrides ks;       // key cache: elements between KV heads, between tokens
   int64_t len_cap;   // min(max_blocks * p, max_context_len): longer contexts are clamped
   float scale_log2;  // scale * log2(e): scores are kept in log2 units
@@ -132,9 +148,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Unit bookkeeping common to both partition kernels: one 16-byte record.
+// Unit bookkeeping common to the partition kernels.  A unit covers tokens
+// [t0, t1) of sequences b .. b + pack - 1 (pack > 1 only for whole shared
+// partitions); slot and nparts belong to sequence b.
 struct Unit {
-  int32_t b, t0, t1, nparts, valid;
+  int32_t b, t0, t1, pack, slot, nparts, valid;
 };
 
 __device__ __forceinline__ Unit decode_unit(const DecodeArgs& a, int32_t unit) {
@@ -142,24 +160,74 @@ __device__ __forceinline__ Unit decode_unit(const DecodeArgs& a, int32_t unit) {
   u.valid = unit < a.plan.counts[0];
   if (!u.valid) return u;
   const int4 w = a.plan.work[unit];
+  const int2 o = a.plan.work_out[unit];
   u.b = w.x;
   u.t0 = w.y;
   u.t1 = w.z;
-  u.nparts = w.w;
+  u.pack = w.w;
+  u.slot = o.x;
+  u.nparts = o.y;
   return u;
 }
 
 // ---------------------------------------------------------------------------
-// Plan: per sequence, floor(L/T) full partitions and (L % T != 0 or L == 0)
-// one ragged partition.  Full units take rows [0, F) in sequence order, then
-// the ragged units follow longest first (bucketed by length), so the hardware
-// dispatcher, which starts workgroups in grid order as slots free up, runs a
-// longest-processing-time-first schedule and the launch ends on short units.
-// Row placement never changes results: partials are merged by partition
-// index.  One workgroup of kPlanThreads threads.
+// Plan.  Sequence b of length L has partitions j = 0 .. np - 1 of T tokens
+// (np = floor(L/T), plus one ragged partition if L % T != 0 or L == 0).  Its
+// partial results occupy slots [first_b, first_b + count_b), contiguous and
+// in sequence order: slot first_b + j for partition j, and one extra slot
+// when a shared partition is split (below).  Work rows: the full-length
+// units first in sequence order, then the shorter units longest first
+// (bucketed by length), so the hardware dispatcher, which starts workgroups
+// in grid order as slots free up, runs a longest-processing-time-first
+// schedule and the launch ends on short units.  Row placement never changes
+// results: partials are merged by slot, in partition order.
+//
+// Packs (pack_max > 1 and a shared-token array given).  Sequence m "joins"
+// its predecessor with j_m = floor(min(shared[m], L_m, L_{m-1}) / 32) shared
+// 32-token chunks; a run is a maximal stretch of consecutive sequences that
+// each join the one before.  A run is cut into packs of pack_max sequences
+// from its start; a pack of k >= 2 sequences shares Ls = 32 min j_m over its
+// members after the first (equal block ids are transitive, so every member
+// holds tokens [0, Ls) in the same blocks as the first).  The first sequence
+// runs one pack unit per whole partition below Ls and, if Ls % T != 0, one
+// "tail" pack unit over [floor(Ls/T) T, Ls).  A member's split partition
+// j0 = floor(Ls/T) then has two pieces: the tail (its extra slot) and its own
+// remainder [Ls, min((j0+1) T, L)) (slot first + j0); a member with no
+// remainder takes the tail in slot first + j0.  Everything from partition
+// j0 + 1 on (from j0 if Ls % T == 0) is the member's own.
+// One workgroup of kPlanThreads threads.
 // ---------------------------------------------------------------------------
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanBuckets = 1024;  // one bucket per plan thread
+constexpr int kPackMax = 16;        // MFMA columns
+constexpr int kShareChunk = 32;     // granularity of a pack's shared tokens (the decode chunk)
+
+// Exclusive scans of two non-negative counts at once (packed in 64 bits; each
+// total stays below 2^31).
+__device__ int2 block_exclusive_scan2(int32_t v0, int32_t v1, int32_t* smem64, int2* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int nw = blockDim.x >> 6;
+  const int64_t v = ((int64_t)v0 << 32) | (uint32_t)v1;
+  int64_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  int64_t* sm = reinterpret_cast<int64_t*>(smem64);
+  if (lane == 63) sm[wid] = x;
+  __syncthreads();
+  int64_t before = 0, tot = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int64_t t = sm[w];
+    before += w < wid ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  *total = make_int2((int32_t)(tot >> 32), (int32_t)(tot & 0xffffffff));
+  const int64_t ex = before + x - v;
+  return make_int2((int32_t)(ex >> 32), (int32_t)(ex & 0xffffffff));
+}
 
 __device__ int32_t block_exclusive_scan(int32_t v, int32_t* smem, int32_t* total) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -183,13 +251,58 @@ __device__ int32_t block_exclusive_scan(int32_t v, int32_t* smem, int32_t* total
   return before + x - v;
 }
 
+__device__ int32_t block_inclusive_max(int32_t v, int32_t* smem, int32_t* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int nw = blockDim.x >> 6;
+  int32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x = max(x, y);
+  }
+  if (lane == 63) smem[wid] = x;
+  __syncthreads();
+  int32_t before = INT32_MIN, tot = INT32_MIN;
+  for (int w = 0; w < nw; ++w) {
+    const int32_t t = smem[w];
+    if (w < wid) before = max(before, t);
+    tot = max(tot, t);
+  }
+  __syncthreads();
+  *total = tot;
+  return max(before, x);
+}
+
+// The shorter units of sequence b (at most three): a pack's tail (its first
+// sequence only), the remainder of a split partition, the ragged partition.
+// f(t0, t1, pack, slot) is called for each.
+template <typename F>
+__device__ __forceinline__ void short_units(int32_t T, int64_t L, int32_t Ls, int32_t k_lead, int32_t first,
+                                            F&& f) {
+  const int32_t nfull = (int32_t)(L / T);
+  const int32_t nshf = Ls / T, tail = Ls - nshf * T;
+  if (Ls > 0 && tail > 0) {
+    if (k_lead > 0) f(nshf * T, Ls, k_lead, first + nshf);
+    const int32_t end = (int32_t)min((int64_t)(nshf + 1) * T, L);
+    if (end > Ls) f(Ls, end, 1, first + nshf);
+    if (nfull > nshf && L % T != 0) f(nfull * T, (int32_t)L, 1, first + nfull);
+  } else if (L % T != 0 || L == 0) {
+    f(nfull * T, (int32_t)L, 1, first + nfull);
+  }
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
   __shared__ int32_t smem[16];
-  __shared__ int32_t bucket[kPlanBuckets];  // counts, then the next free row of each bucket
+  __shared__ __align__(8) int32_t smem64[32];
+  __shared__ int32_t bucket[kPlanBuckets];  // counts, then the next free offset of each bucket
+  // j_m for m in [base - kPackMax, base + kPlanThreads + kPackMax)
+  __shared__ int32_t jt[kPackMax + kPlanThreads + kPackMax];
   const int32_t T = a.part_tokens;
   const int64_t cap = a.len_cap;
+  const int32_t S = a.pack_max;
   const int tid = threadIdx.x;
   bucket[tid] = 0;
+  if (tid < kPackMax) jt[tid] = 0;  // no sequence before the first
   __syncthreads();
   auto length_of = [&](int32_t b, bool flag) -> int64_t {
     int64_t L = a.ctx[b];
@@ -199,54 +312,113 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
     }
     return L;
   };
-  // bucket 0 holds the longest ragged partitions (T - 1 tokens)
-  auto bucket_of = [&](int64_t L) -> int32_t {
-    return (int32_t)(((int64_t)(T - 1 - (int32_t)(L % T)) * kPlanBuckets) / T);
+  // shared 32-token chunks of sequence m with sequence m - 1 (0: none, or no packing)
+  auto joins = [&](int32_t m) -> int32_t {
+    if (S < 2 || m <= 0 || m >= a.n_seqs) return 0;
+    const int64_t lim = min(length_of(m, false), length_of(m - 1, false));
+    int64_t sh = a.shared[m];
+    sh = sh < 0 ? 0 : (sh > lim ? lim : sh);
+    return (int32_t)(sh / kShareChunk);
+  };
+  // a unit of c < T tokens: bucket 0 holds the longest (T - 1 tokens)
+  auto bucket_of = [&](int32_t c) -> int32_t {
+    return (int32_t)(((int64_t)(T - 1 - c) * kPlanBuckets) / T);
   };
 
-  // pass 1: full rows in sequence order; ragged partitions counted per bucket
-  int32_t full_base = 0;
+  // pass 1: slots and full-length rows in sequence order; shorter units counted per bucket
+  int32_t row_base = 0, slot_base = 0, run_carry = 0;
   for (int32_t base = 0; base < a.n_seqs; base += kPlanThreads) {
     const int32_t b = base + tid;
+    const bool in = b < a.n_seqs;
     int64_t L = 0;
-    int32_t nfull = 0, rag = 0;
-    if (b < a.n_seqs) {
+    int32_t nfull = 0, np = 0;
+    if (in) {
       L = length_of(b, true);
       nfull = (int32_t)(L / T);
-      rag = (L % T != 0 || L == 0) ? 1 : 0;
+      np = nfull + ((L % T != 0 || L == 0) ? 1 : 0);
     }
-    int32_t ftot;
-    const int32_t fo = full_base + block_exclusive_scan(nfull, smem, &ftot);
-    if (b < a.n_seqs) {
-      a.plan.seq_info[3 * b + 0] = fo;
-      a.plan.seq_info[3 * b + 1] = nfull;
-      for (int32_t j = 0; j < nfull; ++j)
-        if (fo + j < a.max_units) a.plan.work[fo + j] = make_int4(b, j * T, (j + 1) * T, nfull + rag);
-      if (rag) atomicAdd(&bucket[bucket_of(L)], 1);
+    int32_t k = 1, Ls = 0, lead = b;
+    if (S >= 2) {  // uniform
+      const int32_t jb = in ? joins(b) : 0;
+      jt[kPackMax + tid] = jb;
+      if (tid < kPackMax) jt[kPackMax + kPlanThreads + tid] = joins(base + kPlanThreads + tid);
+      // start of the run holding b: the last sequence at or before b that joins nothing
+      int32_t cmax;
+      const int32_t st = max(run_carry, block_inclusive_max(in && jb == 0 ? b : -1, smem, &cmax));
+      run_carry = max(run_carry, cmax);
+      // jt is complete: block_inclusive_max synchronised after the writes above
+      lead = st + (b - st) / S * S;  // first sequence of b's pack
+      if (in) {
+        int32_t mn = INT32_MAX;
+        for (int32_t i = 1; i < S; ++i) {
+          const int32_t jm = jt[kPackMax + lead + i - base];  // lead + i - base in [-15, 1039)
+          if (jm == 0) break;
+          mn = min(mn, jm);
+          ++k;
+        }
+        if (k >= 2) Ls = mn * kShareChunk;
+      }
     }
-    full_base += ftot;
+    const int32_t nshf = Ls / T, tail = Ls - nshf * T;
+    const int32_t extra = (tail > 0 && L > Ls) ? 1 : 0;
+    const bool leader = in && b == lead && k >= 2;
+    const int32_t own_start = nshf + (tail > 0 ? 1 : 0);
+    const int32_t nrows = in ? (leader ? nshf : 0) + max(nfull - own_start, 0) : 0;
+    const int32_t count = in ? np + extra : 0;
+    int2 tot;
+    const int2 ex = block_exclusive_scan2(nrows, count, smem64, &tot);
+    const int32_t r0 = row_base + ex.x, f0 = slot_base + ex.y;
+    if (in) {
+      a.plan.seq_info[b] = make_int4(f0, count, np, 0);
+      a.plan.seq_pack[b] = make_int2(Ls, leader ? k : 0);
+      int32_t row = r0;
+      if (leader)
+        for (int32_t j = 0; j < nshf; ++j, ++row)
+          if (row < a.max_units) {
+            a.plan.work[row] = make_int4(b, j * T, (j + 1) * T, k);
+            a.plan.work_out[row] = make_int2(f0 + j, count);
+          }
+      for (int32_t j = own_start; j < nfull; ++j, ++row)
+        if (row < a.max_units) {
+          a.plan.work[row] = make_int4(b, j * T, (j + 1) * T, 1);
+          a.plan.work_out[row] = make_int2(f0 + j, count);
+        }
+      short_units(T, L, Ls, leader ? k : 0, f0, [&](int32_t t0, int32_t t1, int32_t, int32_t) {
+        atomicAdd(&bucket[bucket_of(t1 - t0)], 1);
+      });
+    }
+    row_base += tot.x;
+    slot_base += tot.y;
+    if (S >= 2) {
+      // carry the last kPackMax entries over as the next chunk's look-behind
+      __syncthreads();
+      if (tid < kPackMax) jt[tid] = jt[kPlanThreads + tid];
+      __syncthreads();
+    }
   }
-  __syncthreads();
-  const int32_t F = full_base;
+  __syncthreads();  // every short-unit count is in before the bucket totals are read
+  const int32_t F = row_base, FS = slot_base;
   int32_t R;
   const int32_t cnt = bucket[tid];
   const int32_t off = block_exclusive_scan(cnt, smem, &R);
-  bucket[tid] = F + off;
+  bucket[tid] = off;
   __syncthreads();
-  const bool overflow = (int64_t)F + R > a.max_units;
+  const bool overflow = (int64_t)F + R > a.max_units || FS > a.max_units;
 
-  // pass 2: ragged rows, longest bucket first (order inside a bucket is free)
+  // pass 2: shorter units, longest bucket first (order inside a bucket is free)
   for (int32_t base = 0; base < a.n_seqs; base += kPlanThreads) {
     const int32_t b = base + tid;
     if (b < a.n_seqs) {
       const int64_t L = length_of(b, false);
-      const int32_t nfull = (int32_t)(L / T);
-      int32_t row = -1;
-      if (L % T != 0 || L == 0) {
-        row = atomicAdd(&bucket[bucket_of(L)], 1);
-        if (!overflow) a.plan.work[row] = make_int4(b, nfull * T, (int32_t)L, nfull + 1);
-      }
-      a.plan.seq_info[3 * b + 2] = row;
+      const int4 si = a.plan.seq_info[b];   // written by this thread in pass 1
+      const int2 sp = a.plan.seq_pack[b];
+      short_units(T, L, sp.x, sp.y, si.x, [&](int32_t t0, int32_t t1, int32_t k, int32_t slot) {
+        const int32_t row = F + atomicAdd(&bucket[bucket_of(t1 - t0)], 1);
+        if (!overflow) {
+          a.plan.work[row] = make_int4(b, t0, t1, k);
+          a.plan.work_out[row] = make_int2(slot, si.y);
+        }
+      });
     }
   }
   if (tid == 0) {
@@ -295,6 +467,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ float red_o[W][16][DP];
   __shared__ float red_m[W][16], red_l[W][16];
   __shared__ int32_t tab_lds[W][P < 8 ? 512 : 1];
+  __shared__ int32_t col_slot[16], col_np[16];  // per column of a pack: partial slot, partitions
 
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
@@ -305,8 +478,21 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
   if (!u.valid) return;             // uniform over the workgroup
   const int32_t G = a.hq / a.hkv;
   const int n = lane & 15, r = lane >> 4;
-  const int32_t head = g * G + n;
-  const bool head_ok = n < G;
+  // MFMA column n: query head n % G of pack member n / G (the unit's own
+  // sequence when the pack is one sequence); columns >= pack * G are padding
+  const int32_t NC = u.pack * G;
+  const int32_t mem = n / G;
+  const int32_t head = g * G + (n - mem * G);
+  const bool head_ok = n < NC;
+  if (u.pack > 1 && threadIdx.x < NC) {
+    // a shared piece of partition j = t0 / T of every member: slot first + j,
+    // except a tail (t1 % T != 0) of a member that continues past it, which
+    // goes to its extra slot first + partitions
+    const int4 si = a.plan.seq_info[u.b + (int32_t)threadIdx.x / G];
+    const bool tail = (u.t1 & (a.part_tokens - 1)) != 0;
+    col_slot[threadIdx.x] = si.x + (tail && si.y > si.z ? si.z : u.t0 / a.part_tokens);
+    col_np[threadIdx.x] = si.y;
+  }
 
   const uint16_t* kc = (const uint16_t*)a.kc;
   const uint16_t* vc = (const uint16_t*)a.vc;
@@ -328,7 +514,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
     // query fragments (B operand of the score MFMA): head n, dims 32 i + 8 r
     bf16x8 qf[KI];
     {
-      const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)u.b * a.hq + head) * D + 8 * r;
+      const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)(u.b + mem) * a.hq + head) * D + 8 * r;
 #pragma unroll
       for (int i = 0; i < KI; ++i) {
         uint4 x = head_ok ? *reinterpret_cast<const uint4*>(qrow + 32 * i) : uint4{0, 0, 0, 0};
@@ -553,7 +739,7 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
   __syncthreads();
 
   // combine the W waves: out = sum_v 2^((m_v - M) c) o_v / sum_v 2^((m_v - M) c) l_v
-  for (int32_t e = threadIdx.x; e < G * D; e += 64 * W) {
+  for (int32_t e = threadIdx.x; e < NC * D; e += 64 * W) {
     const int32_t h = e / D, dd = e - h * D;
     float M = -INFINITY;
 #pragma unroll
@@ -570,13 +756,17 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
       }
     }
     const float inv = sum > 0.f ? 1.f / sum : 0.f;
-    const int32_t qh = g * G + h;
-    if (u.nparts == 1) {
-      store_f32((uint16_t*)a.out + ((int64_t)u.b * a.hq + qh) * D + dd, o * inv);
+    const int32_t hm = h / G;
+    const int32_t qh = g * G + (h - hm * G);
+    const int32_t seq = u.b + hm;
+    const int32_t slot = u.pack > 1 ? col_slot[h] : u.slot;
+    const int32_t np = u.pack > 1 ? col_np[h] : u.nparts;
+    if (np == 1) {
+      store_f32((uint16_t*)a.out + ((int64_t)seq * a.hq + qh) * D + dd, o * inv);
     } else {
-      __builtin_nontemporal_store(o * inv, a.plan.part_o + ((int64_t)unit * a.hq + qh) * D + dd);
+      __builtin_nontemporal_store(o * inv, a.plan.part_o + ((int64_t)slot * a.hq + qh) * D + dd);
       if (dd == 0) {
-        float* ml = a.plan.part_ml + ((int64_t)unit * a.hq + qh) * 2;
+        float* ml = a.plan.part_ml + ((int64_t)slot * a.hq + qh) * 2;
         ml[0] = M * c;
         ml[1] = sum;
       }
@@ -874,9 +1064,9 @@ __global__ __launch_bounds__(256) void decode_dpp_kernel(DecodeArgs a) {
     if (u.nparts == 1) {
       store_f32((T*)a.out + ((int64_t)u.b * a.hq + qh) * D + dd, o * inv);
     } else {
-      __builtin_nontemporal_store(o * inv, a.plan.part_o + ((int64_t)unit * a.hq + qh) * D + dd);
+      __builtin_nontemporal_store(o * inv, a.plan.part_o + ((int64_t)u.slot * a.hq + qh) * D + dd);
       if (dd == 0) {
-        float* ml = a.plan.part_ml + ((int64_t)unit * a.hq + qh) * 2;
+        float* ml = a.plan.part_ml + ((int64_t)u.slot * a.hq + qh) * 2;
         ml[0] = M * c;
         ml[1] = sum;
       }
@@ -985,14 +1175,14 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
         if (dd < D) store_f32(orow + dd, acc[h][k] * inv);
       }
     } else {
-      float* prow = a.plan.part_o + ((int64_t)unit * a.hq + head) * D;
+      float* prow = a.plan.part_o + ((int64_t)u.slot * a.hq + head) * D;
 #pragma unroll
       for (int k = 0; k < DK; ++k) {
         const int32_t dd = lane + 64 * k;
         if (dd < D) prow[dd] = acc[h][k] * inv;
       }
       if (lane == 0) {
-        float* ml = a.plan.part_ml + ((int64_t)unit * a.hq + head) * 2;
+        float* ml = a.plan.part_ml + ((int64_t)u.slot * a.hq + head) * 2;
         ml[0] = m[h];
         ml[1] = l[h];
       }
@@ -1013,9 +1203,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   __shared__ float red_m[W], red_s[W];
   __shared__ float red_o[W][DK * 64];
   const int32_t b = blockIdx.x, head = blockIdx.y;
-  const int32_t* si = a.plan.seq_info + 3 * b;
-  const int32_t f0 = si[0], nf = si[1], rr = si[2];
-  const int32_t n = nf + (rr >= 0 ? 1 : 0);
+  const int4 si = a.plan.seq_info[b];
+  const int32_t f0 = si.x, n = si.y;  // slots f0 .. f0 + n - 1, in partition order
   if (n <= 1) return;
   if (a.plan.counts[0] == 0) return;  // plan overflowed
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -1033,7 +1222,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
 #pragma unroll
       for (int k = 0; k < DK; ++k) op[u][k] = 0.f;
       if (i < n) {
-        const int64_t row = (i < nf ? f0 + i : rr) * (int64_t)a.hq + head;
+        const int64_t row = (int64_t)(f0 + i) * a.hq + head;
         mp[u] = a.plan.part_ml[row * 2];
         lp[u] = a.plan.part_ml[row * 2 + 1];
 #pragma unroll
@@ -1120,6 +1309,7 @@ struct Choice {
   int32_t part_tokens;
   int64_t max_units;
   bool need_partials;
+  bool may_pack;  // sized for packs of sharing sequences (one extra slot per sequence)
 };
 
 enum { kMathAuto, kMathValu, kMathMfma, kMathDpp, kMathGeneric };
@@ -1149,7 +1339,7 @@ bool dpp_shape_ok(int32_t hq, int32_t hkv, int32_t d, int32_t p, pkv_dtype dt) {
 bool generic_shape_ok(int32_t hq, int32_t hkv, int32_t d) { return d <= 256 && hq / hkv <= 16; }
 
 int choose(int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t p, int32_t max_len,
-           int64_t total, pkv_dtype dt, Choice* out) {
+           int64_t total, int64_t unshared, pkv_dtype dt, Choice* out) {
   const int mode = math_mode();
   const bool mshape = mfma_shape_ok(hq, hkv, d, p, dt);
   const bool dshape = dpp_shape_ok(hq, hkv, d, p, dt);
@@ -1172,6 +1362,8 @@ int choose(int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t p, int32_
   if (kind == kKindGeneric && !generic_shape_ok(hq, hkv, d))
     return fail(PKV_ERR_UNSUPPORTED, "decode supports head_dim <= 256 and Hq/Hkv <= 16");
   const int64_t L = std::max<int32_t>(max_len, 1);
+  // packs need the matrix-core kernel and a batch not known to share nothing
+  const bool may_pack = kind == kKindMfma && !(unshared >= 0 && total >= 0 && unshared >= total);
   if (total < 0) total = (int64_t)n_seqs * L;
   // W waves share a partition of T tokens; each wave's share is whole chunks
   int32_t W = 1, tmin = 64, tmax = 512;
@@ -1205,15 +1397,17 @@ int choose(int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t p, int32_
   out->kind = kind;
   out->waves_per_group = W;
   out->part_tokens = T;
-  out->max_units = std::max<int64_t>(1, std::min(by_len, by_total));
-  out->need_partials = T < L;
+  // a split shared partition adds one slot (and one unit) per sequence
+  out->max_units = std::max<int64_t>(1, std::min(by_len, by_total)) + (may_pack ? n_seqs : 0);
+  out->need_partials = T < L || may_pack;
+  out->may_pack = may_pack;
   return PKV_OK;
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t counts, seq_info, work, part_ml, part_o, total;
+  size_t counts, seq_info, seq_pack, work, work_out, part_ml, part_o, total;
 };
 
 Layout layout_of(int32_t n_seqs, int32_t hq, int32_t d, const Choice& c) {
@@ -1222,9 +1416,13 @@ Layout layout_of(int32_t n_seqs, int32_t hq, int32_t d, const Choice& c) {
   l.counts = off;
   off = align256(off + 2 * sizeof(int32_t));
   l.seq_info = off;
-  off = align256(off + (size_t)3 * n_seqs * sizeof(int32_t));
+  off = align256(off + (size_t)n_seqs * sizeof(int4));
+  l.seq_pack = off;
+  off = align256(off + (size_t)n_seqs * sizeof(int2));
   l.work = off;
   off = align256(off + (size_t)c.max_units * sizeof(int4));
+  l.work_out = off;
+  off = align256(off + (size_t)c.max_units * sizeof(int2));
   l.part_ml = off;
   if (c.need_partials) off = align256(off + (size_t)c.max_units * hq * 2 * sizeof(float));
   l.part_o = off;
@@ -1307,7 +1505,8 @@ using pkv::fail;
 extern "C" int pkv_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                           int32_t head_dim, int32_t block_size,
                                           int32_t max_context_len, int64_t total_context_tokens,
-                                          pkv_dtype dtype, size_t* bytes_out) {
+                                          int64_t unshared_context_tokens, pkv_dtype dtype,
+                                          size_t* bytes_out) {
   PKV_TRY_BEGIN
   if (!bytes_out) return fail(PKV_ERR_INVALID_ARG, "bytes_out is NULL");
   if (n_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
@@ -1316,7 +1515,7 @@ extern "C" int pkv_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, i
   if (!pkv::dtype_valid(dtype)) return fail(PKV_ERR_INVALID_ARG, "bad dtype");
   pkv::Choice c;
   int rc = pkv::choose(n_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
-                       total_context_tokens, dtype, &c);
+                       total_context_tokens, unshared_context_tokens, dtype, &c);
   if (rc) return rc;
   *bytes_out = pkv::layout_of(n_seqs, num_q_heads, head_dim, c).total;
   return PKV_OK;
@@ -1325,11 +1524,13 @@ extern "C" int pkv_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, i
 
 extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
                                           const void* v_cache, const int32_t* d_block_table,
-                                          const int32_t* d_context_lens, int32_t n_seqs,
+                                          const int32_t* d_context_lens,
+                                          const int32_t* d_shared_prev, int32_t n_seqs,
                                           int32_t num_q_heads, int32_t num_kv_heads,
                                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                           int32_t max_blocks_per_seq, int32_t max_context_len,
-                                          int64_t total_context_tokens, float scale,
+                                          int64_t total_context_tokens,
+                                          int64_t unshared_context_tokens, float scale,
                                           pkv_dtype dtype, pkv_layout k_layout, void* workspace,
                                           size_t workspace_bytes, void* stream) {
   PKV_TRY_BEGIN
@@ -1349,7 +1550,7 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
     return fail(PKV_ERR_INVALID_ARG, "max_context_len exceeds the block-table capacity");
   pkv::Choice c;
   int rc = pkv::choose(n_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
-                       total_context_tokens, dtype, &c);
+                       total_context_tokens, unshared_context_tokens, dtype, &c);
   if (rc) return rc;
   if (c.kind != pkv::kKindGeneric) {
     const uintptr_t mis = (uintptr_t)out | (uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache;
@@ -1378,6 +1579,7 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   a.vc = v_cache;
   a.table = d_block_table;
   a.ctx = d_context_lens;
+  a.shared = d_shared_prev;
   a.n_seqs = n_seqs;
   a.hq = num_q_heads;
   a.hkv = num_kv_heads;
@@ -1388,11 +1590,19 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   a.max_blocks = max_blocks_per_seq;
   a.part_tokens = c.part_tokens;
   a.max_units = (int32_t)c.max_units;
+  // packs of sequences that share blocks: matrix-core kernel only (its 16
+  // columns take 16 / G sequences' head groups).  A hint that nothing is
+  // shared (unshared == total) skips the array and the plan's pack pass.
+  a.pack_max = 1;
+  if (d_shared_prev && c.may_pack && c.kind == pkv::kKindMfma && !pkv::env_is("PKV_DECODE_SHARE", "off"))
+    a.pack_max = std::max(1, std::min(pkv::kPackMax, 16 / (num_q_heads / num_kv_heads)));
   a.len_cap = std::min<int64_t>((int64_t)max_blocks_per_seq * block_size, max_context_len);
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.plan.counts = (int32_t*)(ws + lay.counts);
-  a.plan.seq_info = (int32_t*)(ws + lay.seq_info);
+  a.plan.seq_info = (int4*)(ws + lay.seq_info);
+  a.plan.seq_pack = (int2*)(ws + lay.seq_pack);
   a.plan.work = (int4*)(ws + lay.work);
+  a.plan.work_out = (int2*)(ws + lay.work_out);
   a.plan.part_ml = c.need_partials ? (float*)(ws + lay.part_ml) : nullptr;
   a.plan.part_o = c.need_partials ? (float*)(ws + lay.part_o) : nullptr;
   a.err = err;
@@ -1412,7 +1622,8 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   } else {
     pkv::launch_valu<float>(a, waves, st);
   }
-  if (c.need_partials) {
+  // some sequence has several partials: a partition split, or a split shared partition
+  if (c.need_partials && (c.part_tokens < std::max<int32_t>(max_context_len, 1) || a.pack_max > 1)) {
     const dim3 grid((unsigned)n_seqs, (unsigned)num_q_heads);
     if (dtype == PKV_BF16) pkv::launch_merge<uint16_t>(a, grid, st);
     else pkv::launch_merge<float>(a, grid, st);

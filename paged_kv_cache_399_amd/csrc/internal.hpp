@@ -35,15 +35,17 @@ inline KStrides k_strides(int layout, int32_t hkv, int32_t p, int32_t d) {
 }
 
 // Block-table patch carried entirely in kernel arguments (no staging copy):
-// lens[len0 + i] = w[i] (i < n_len); slots[slot0 + i] = w[n_len + i]
-// (i < n_slot); then n_ent (row, col, value) triples; then n_reset (row, from)
-// pairs whose row entries [from, max_blocks) become -1.
+// lens[len0 + i] = w[i] (i < n_len); shared[sh0 + i] = w[n_len + i]
+// (i < n_sh); slots[slot0 + i] = w[n_len + n_sh + i] (i < n_slot); then
+// n_ent (row, col, value) triples; then n_reset (row, from) pairs whose row
+// entries [from, max_blocks) become -1.
 constexpr int kPatchWords = 896;
 struct TablePatchArgs {
   int32_t* table;
   int32_t* lens;
   int32_t* slots;
-  int32_t max_blocks, n_len, len0, n_slot, slot0, n_ent, n_reset, unused;
+  int32_t* shared;
+  int32_t max_blocks, n_len, len0, n_slot, slot0, n_ent, n_reset, n_sh, sh0, unused;
   int32_t w[kPatchWords];
 };
 

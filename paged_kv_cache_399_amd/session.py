@@ -6,7 +6,9 @@ library calls together in the order a decode step needs them:
 
     append_slots (host) -> copy_blocks (copy-on-write) -> block_table_upload
     (a full upload into a new table, then incremental patches of the new
-    entries, lengths and slot mapping) -> cache_append -> paged_attention_decode
+    entries, lengths and slot mapping; also how many leading tokens each
+    sequence holds in the previous one's blocks) -> cache_append ->
+    paged_attention_decode (sequences that share blocks read them once per pack)
 
 Everything that computes runs in libpkv.so; this class only keeps buffers and
 calls the binding.
@@ -29,13 +31,14 @@ def _poison_value(dtype):
 class PagedKVCache:
     def __init__(self, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
                  dtype, device="cuda", free_order=None, fill: Optional[float] = None,
-                 layout: str = "head_major"):
+                 layout: str = "head_major", share_blocks: bool = True):
         import torch
         self.pool = BlockPool(num_blocks, block_size, free_order)
         self.num_blocks, self.block_size = num_blocks, block_size
         self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
         self.dtype, self.device = dtype, torch.device(device)
         self.layout = layout
+        self.share_blocks = share_blocks
         if layout == "token_major":
             shape_k = (num_blocks, block_size, num_kv_heads, head_dim)
         elif layout == "head_major":
@@ -102,11 +105,20 @@ class PagedKVCache:
         m.table = torch.empty((b, m.max_blocks), dtype=torch.int32, device=self.device)
         m.lens = torch.empty(b, dtype=torch.int32, device=self.device)
         m.slots = torch.empty(max(b, 1), dtype=torch.int32, device=self.device)
+        m.shared = (torch.zeros(b, dtype=torch.int32, device=self.device)
+                    if self.share_blocks else None)
         m.num_q_heads = num_q_heads
         m.ws_max_len = int(max_context_len)
         m.ws_total = int(total_tokens)
+        # with sharing, the partition length follows the tokens left once the
+        # blocks shared now are read once per pack (fixed for the batch's life)
+        m.ws_unshared = -1
+        if self.share_blocks and b:
+            sh, _ = self.pool.shared_prefix(m.seqs)
+            m.ws_unshared = max(m.ws_total - int(sh.sum()), 0)
         need = decode_workspace_bytes(b, num_q_heads, self.num_kv_heads, self.head_dim,
-                                      self.block_size, m.ws_max_len, m.ws_total, self.dtype)
+                                      self.block_size, m.ws_max_len, m.ws_total, self.dtype,
+                                      m.ws_unshared)
         m.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=self.device)
         m.max_len = 0
         m.total = 0
@@ -122,7 +134,8 @@ class PagedKVCache:
             copy_blocks(self.k_cache, self.v_cache, cow, stream, self.layout)
         m.max_len, m.total = self.pool.block_table_upload(m.seqs, m.max_blocks, m.table, m.lens,
                                                           slots, m.slots, stream,
-                                                          incremental=m.uploaded)
+                                                          incremental=m.uploaded,
+                                                          d_shared_prev=m.shared)
         m.uploaded = True
         cache_append(self.k_cache, self.v_cache, k_new, v_new, m.slots, stream, self.layout)
         return slots
@@ -130,7 +143,8 @@ class PagedKVCache:
     def upload(self, m, stream=None):
         """Upload table and lengths without appending (e.g. after a prefill)."""
         m.max_len, m.total = self.pool.block_table_upload(m.seqs, m.max_blocks, m.table, m.lens,
-                                                          stream=stream, incremental=m.uploaded)
+                                                          stream=stream, incremental=m.uploaded,
+                                                          d_shared_prev=m.shared)
         m.uploaded = True
 
     def attend(self, m, q, out, scale=None, stream=None):
@@ -140,7 +154,8 @@ class PagedKVCache:
         # with it the summation order) is fixed for the life of the batch
         return paged_attention_decode(out, q, self.k_cache, self.v_cache, m.table, m.lens,
                                       m.ws_max_len, m.ws_total, scale, m.workspace, stream,
-                                      self.layout)
+                                      self.layout, shared_prev=m.shared,
+                                      unshared_context_tokens=m.ws_unshared)
 
     def capture_attend(self, m, q, out, scale=None):
         """Record one decode call (plan, partition, merge kernels) into a HIP graph.
@@ -180,7 +195,8 @@ class PagedKVCache:
             m.slots = torch.empty(len(slots), dtype=torch.int32, device=self.device)
         m.max_len, m.total = self.pool.block_table_upload(m.seqs, m.max_blocks, m.table, m.lens,
                                                           slots, m.slots, stream,
-                                                          incremental=m.uploaded)
+                                                          incremental=m.uploaded,
+                                                          d_shared_prev=m.shared)
         m.uploaded = True
         if len(slots):
             cache_append(self.k_cache, self.v_cache, k_new, v_new, m.slots, stream, self.layout)

@@ -1,0 +1,265 @@
+"""Decode over sequences that share blocks (forks), read once per pack.
+
+Sequences are built as a forest: each root receives a prompt, is forked, and
+every member appends a private suffix (copy-on-write copies a shared partial
+block first), then one decode step appends a token to each.  The library's
+upload writes, per sequence, the tokens it holds in the previous sequence's
+blocks; that array is checked bit for bit against the oracle's slot-by-slot
+definition.  Decode with and without the array must both match float64
+attention over each sequence's tokens in logical order; where every shared
+length is a whole number of partitions the two are bit-identical (each MFMA
+column computes what its own unit would), otherwise a partition split by the
+end of a shared prefix is summed as two partials.
+"""
+import numpy as np
+import pytest
+
+from oracle import attention as oatt
+from oracle import layout as olayout
+from tests.paged_case import BF16_TOL, host_bits, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu_guard(request):
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    say(f"\n[gpu] {request.node.name}")
+    yield
+    torch.cuda.synchronize()
+    import paged_kv_cache_399_amd as pkv
+    assert pkv.check_device_errors() == 0
+
+
+def _randn(rng, shape):
+    import torch
+    return torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(torch.bfloat16)
+
+
+def _forest(groups, hkv, d, p, seed, layout="head_major", shuffle=False):
+    """groups: (prompt length, [suffix length per member]); returns kv, batch, keys, values."""
+    import torch
+    from paged_kv_cache_399_amd.session import PagedKVCache
+    rng = np.random.default_rng(seed)
+    tokens = sum(pl + sum(sf) for pl, sf in groups)
+    members = sum(len(sf) for _, sf in groups)
+    nb = 2 * (tokens // p + 3 * members) + 16
+    kv = PagedKVCache(nb, p, hkv, d, torch.bfloat16, "cuda", rng.permutation(nb).astype(np.int32),
+                      fill=float("nan"), layout=layout)
+    seqs, keys, vals = [], [], []
+    for plen, sfx in groups:
+        root = kv.new_sequences(1)[0]
+        pk, pv = _randn(rng, (plen, hkv, d)), _randn(rng, (plen, hkv, d))
+        if plen:
+            kv.write([root], [plen], pk.cuda(), pv.cuda())
+        mem = [root] + [kv.fork(root) for _ in range(len(sfx) - 1)]
+        for m, s in zip(mem, sfx):
+            sk, sv = _randn(rng, (s, hkv, d)), _randn(rng, (s, hkv, d))
+            if s:
+                kv.write([m], [s], sk.cuda(), sv.cuda())
+            seqs.append(m)
+            keys.append(torch.cat([pk, sk]))
+            vals.append(torch.cat([pv, sv]))
+    order = rng.permutation(len(seqs)) if shuffle else np.arange(len(seqs))
+    return kv, [seqs[i] for i in order], [keys[i] for i in order], [vals[i] for i in order]
+
+
+def _expected_shared(kv, batch):
+    want = [0]
+    for a, b in zip(batch[:-1], batch[1:]):
+        ta, la = kv.pool.get_table(a)
+        tb, lb = kv.pool.get_table(b)
+        want.append(olayout.shared_prefix_tokens(ta.tolist(), int(la), tb.tolist(), int(lb),
+                                                 kv.block_size))
+    return np.array(want, np.int32)
+
+
+def _step_and_check(kv, batch, keys, vals, hq, seed, steps=1, t=None):
+    """Decode steps with and without the shared array; both against float64.
+    With a forced partition length t, shared lengths that are all multiples
+    of t must give bit-identical outputs."""
+    import torch
+    from paged_kv_cache_399_amd import paged_attention_decode
+    rng = np.random.default_rng(seed + 1000)
+    b, hkv, d, p = len(batch), kv.num_kv_heads, kv.head_dim, kv.block_size
+    lens = np.array([len(k) for k in keys])
+    max_len = int(lens.max()) + steps
+    m = kv.prepare(batch, -(-max_len // p), hq, max_len, int(lens.sum()) + b * steps)
+    worst = 0.0
+    for step in range(steps):
+        sk, sv = _randn(rng, (b, hkv, d)), _randn(rng, (b, hkv, d))
+        kv.append_decode_tokens(m, sk.cuda(), sv.cuda())
+        for i in range(b):
+            keys[i] = torch.cat([keys[i], sk[i:i + 1]])
+            vals[i] = torch.cat([vals[i], sv[i:i + 1]])
+        torch.cuda.synchronize()
+        got_sh = m.shared.cpu().numpy()
+        want_sh = _expected_shared(kv, batch)
+        assert np.array_equal(got_sh, want_sh), (got_sh, want_sh)
+        q = _randn(rng, (b, hq, d)).cuda()
+        out_sh = torch.full_like(q, float("nan"))
+        out_no = torch.full_like(q, float("nan"))
+        kv.attend(m, q, out_sh)
+        # same sizing arguments (so the same partition length), no shared array
+        paged_attention_decode(out_no, q, kv.k_cache, kv.v_cache, m.table, m.lens, m.ws_max_len,
+                               m.ws_total, None, m.workspace, None, kv.layout, shared_prev=None,
+                               unshared_context_tokens=m.ws_unshared)
+        torch.cuda.synchronize()
+        if t and all(x % t == 0 for x in want_sh):
+            assert torch.equal(out_sh, out_no), "packing whole partitions changed the result"
+        qb = host_bits(q)
+        for i in range(b):
+            ref = oatt.decode(qb[i], host_bits(keys[i]), host_bits(vals[i]))
+            for name, o in (("shared", out_sh), ("unshared", out_no)):
+                err = float(np.abs(o[i].double().cpu().numpy() - ref).max())
+                assert err <= BF16_TOL, f"{name}: sequence {i} (length {len(keys[i])}): max abs err {err}"
+                worst = max(worst, err)
+    return worst, int(want_sh.max()) if b else 0
+
+
+CASES = [
+    # (Hq, Hkv, D, P, layout, forced T, groups, shuffle)
+    (8, 2, 128, 16, "head_major", 128, [(600, [3, 0, 50, 200]), (0, [40]), (300, [1, 1, 1, 1, 1, 1, 1])], False),
+    (16, 4, 128, 16, "head_major", 256, [(2048, [5, 60, 300, 2, 0, 17, 9, 100, 31])], False),
+    (32, 8, 128, 16, "head_major", None, [(2048, [int(x) for x in np.arange(1, 130, 8)])], False),
+    (16, 2, 64, 8, "head_major", 128, [(1000, [0, 0, 0, 0, 0, 0]), (999, [3, 3])], False),
+    (16, 1, 128, 16, "head_major", 128, [(700, [10, 20, 30])], False),
+    (16, 16, 128, 16, "head_major", 128, [(700, [10, 20, 30])], False),
+    (8, 2, 128, 1, "head_major", 128, [(300, [1, 2, 3, 4, 5])], False),
+    (8, 2, 128, 4, "token_major", 128, [(513, [0, 7, 260])], False),
+    (16, 4, 128, 64, "head_major", 256, [(1100, [64, 0, 1, 65, 128])], False),
+    (16, 4, 128, 32, "token_major", 256, [(777, [5, 5, 5, 5, 5]), (512, [0, 0])], False),
+    (16, 4, 128, 16, "head_major", 128, [(500, [3, 4, 5]), (400, [6, 7]), (0, [9]), (260, [1, 2, 3])], True),
+    (24, 8, 128, 16, "head_major", 128, [(384, [0, 1, 2, 3, 4, 5, 6])], False),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_shared_blocks_decode(monkeypatch, case):
+    hq, hkv, d, p, layout, t, groups, shuffle = CASES[case]
+    if t:
+        monkeypatch.setenv("PKV_PARTITION_TOKENS", str(t))
+    say(f"  case {case}: Hq={hq} Hkv={hkv} D={d} P={p} {layout} T={t} groups={[(g[0], len(g[1])) for g in groups]}"
+        f" shuffle={shuffle}")
+    kv, batch, keys, vals = _forest(groups, hkv, d, p, seed=case, layout=layout, shuffle=shuffle)
+    worst, most = _step_and_check(kv, batch, keys, vals, hq, seed=case, steps=2, t=t)
+    say(f"  case {case}: max shared {most}, max err {worst:.3e}")
+    kv.close()
+
+
+@pytest.mark.parametrize("t", [128, 256])
+def test_whole_context_shared(monkeypatch, t):
+    """Every token of every member is shared: the pack units alone produce the
+    output (one partition: written directly; two: merged from pack partials)."""
+    import torch
+    from paged_kv_cache_399_amd import paged_attention_decode
+    monkeypatch.setenv("PKV_PARTITION_TOKENS", str(t))
+    hq, hkv, d, p = 16, 4, 128, 16
+    kv, batch, keys, vals = _forest([(256, [0, 0, 0, 0, 0]), (256, [0, 0, 0])], hkv, d, p, seed=5)
+    m = kv.prepare(batch, 16, hq, 256, 256 * len(batch))
+    kv.upload(m)
+    torch.cuda.synchronize()
+    assert np.array_equal(m.shared.cpu().numpy(), _expected_shared(kv, batch))
+    assert m.shared.cpu().numpy().tolist() == [0, 256, 256, 256, 256, 0, 256, 256]
+    rng = np.random.default_rng(6)
+    q = _randn(rng, (len(batch), hq, d)).cuda()
+    out_sh = torch.full_like(q, float("nan"))
+    out_no = torch.full_like(q, float("nan"))
+    kv.attend(m, q, out_sh)
+    paged_attention_decode(out_no, q, kv.k_cache, kv.v_cache, m.table, m.lens, m.ws_max_len, m.ws_total,
+                           None, m.workspace, unshared_context_tokens=m.ws_unshared)
+    torch.cuda.synchronize()
+    assert torch.equal(out_sh, out_no)
+    qb = host_bits(q)
+    for i in range(len(batch)):
+        ref = oatt.decode(qb[i], host_bits(keys[i]), host_bits(vals[i]))
+        assert float(np.abs(out_sh[i].double().cpu().numpy() - ref).max()) <= BF16_TOL
+    kv.close()
+
+
+def test_shared_prefix_ending_inside_a_partition(monkeypatch):
+    """Shared lengths that are not whole partitions: a tail pack unit covers the
+    shared 32-token chunks of the last partition.  A member that continues
+    past them gets the tail as an extra partial; a member that ends exactly
+    there (224 tokens, one partition) takes it as its only partial, written
+    as the output directly."""
+    import torch
+    monkeypatch.setenv("PKV_PARTITION_TOKENS", "256")
+    hq, hkv, d, p = 16, 4, 128, 16
+    kv, batch, keys, vals = _forest([(200, [0, 0, 0]), (224, [0, 0]), (600, [0, 37, 250, 3]),
+                                     (40, [0, 1])], hkv, d, p, seed=8)
+    lens = np.array([len(k) for k in keys])
+    m = kv.prepare(batch, -(-int(lens.max()) // p), hq, int(lens.max()), int(lens.sum()))
+    kv.upload(m)
+    rng = np.random.default_rng(9)
+    q = _randn(rng, (len(batch), hq, d)).cuda()
+    out = torch.full_like(q, float("nan"))
+    kv.attend(m, q, out)
+    torch.cuda.synchronize()
+    assert m.shared.cpu().numpy().tolist() == _expected_shared(kv, batch).tolist()
+    qb = host_bits(q)
+    for i in range(len(batch)):
+        ref = oatt.decode(qb[i], host_bits(keys[i]), host_bits(vals[i]))
+        err = float(np.abs(out[i].double().cpu().numpy() - ref).max())
+        assert err <= BF16_TOL, f"sequence {i} (length {len(keys[i])}): max abs err {err}"
+    kv.close()
+
+
+def test_incremental_upload_sends_changed_shared_counts():
+    """Row reuse in a new order through incremental uploads: the shared-token
+    array follows the new neighbours; unchanged counts are not resent and stay."""
+    import torch
+    kv, batch, _, _ = _forest([(100, [0, 4, 9]), (50, [3, 0])], 2, 64, 8, seed=9)
+    dev = torch.device("cuda")
+    table = torch.empty((5, 32), dtype=torch.int32, device=dev)
+    lens = torch.empty(5, dtype=torch.int32, device=dev)
+    shared = torch.full((5,), -7, dtype=torch.int32, device=dev)
+    orders = [batch, batch, [batch[i] for i in (3, 0, 4, 1, 2)], [batch[i] for i in (3, 0, 4, 1, 2)], batch]
+    for k, order in enumerate(orders):
+        kv.pool.block_table_upload(order, 32, table, lens, incremental=k > 0, d_shared_prev=shared)
+        torch.cuda.synchronize()
+        assert np.array_equal(shared.cpu().numpy(), _expected_shared(kv, order)), k
+    kv.close()
+
+
+def test_out_of_range_counts_are_clamped():
+    """Negative counts act as no sharing (bit-identical to none); counts past
+    both lengths are clamped, so decode stays in bounds and raises no error."""
+    import torch
+    from paged_kv_cache_399_amd import paged_attention_decode
+    hq, hkv, d, p = 16, 4, 128, 16
+    kv, batch, keys, vals = _forest([(300, [0, 5]), (0, [70]), (10, [0, 0])], hkv, d, p, seed=3)
+    lens = np.array([len(k) for k in keys])
+    m = kv.prepare(batch, -(-int(lens.max()) // p), hq, int(lens.max()), int(lens.sum()))
+    kv.upload(m)
+    rng = np.random.default_rng(4)
+    q = _randn(rng, (len(batch), hq, d)).cuda()
+    base = torch.full_like(q, float("nan"))
+    paged_attention_decode(base, q, kv.k_cache, kv.v_cache, m.table, m.lens, m.ws_max_len, m.ws_total,
+                           None, m.workspace, unshared_context_tokens=m.ws_unshared)
+    neg = torch.full((len(batch),), -1000, dtype=torch.int32, device="cuda")
+    out = torch.full_like(q, float("nan"))
+    paged_attention_decode(out, q, kv.k_cache, kv.v_cache, m.table, m.lens, m.ws_max_len, m.ws_total,
+                           None, m.workspace, shared_prev=neg, unshared_context_tokens=m.ws_unshared)
+    torch.cuda.synchronize()
+    assert torch.equal(out, base)
+    big = torch.full((len(batch),), 1 << 30, dtype=torch.int32, device="cuda")
+    paged_attention_decode(out, q, kv.k_cache, kv.v_cache, m.table, m.lens, m.ws_max_len, m.ws_total,
+                           None, m.workspace, shared_prev=big, unshared_context_tokens=m.ws_unshared)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    kv.close()
+
+
+def test_more_sequences_than_one_plan_pass(monkeypatch):
+    """1101 sequences in fork groups of three: packs and runs cross the plan's
+    1024-sequence passes (its look-behind and run carry)."""
+    monkeypatch.setenv("PKV_PARTITION_TOKENS", "128")
+    groups = [(130 + (i % 7) * 20, [i % 3, 2, 5]) for i in range(367)]
+    kv, batch, keys, vals = _forest(groups, 2, 64, 16, seed=21)
+    assert len(batch) == 1101
+    worst, most = _step_and_check(kv, batch, keys, vals, 8, seed=21, steps=1, t=128)
+    say(f"  1101 sequences: max shared {most}, max err {worst:.3e}")
+    kv.close()
