@@ -67,7 +67,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 struct Plan {
   int32_t* counts;     // [0] units to run (0 if the plan overflowed), [1] full-length units
   int4* seq_info;      // [n_seqs]: (first slot, partials, partitions, unused); slots are contiguous
-  int2* seq_pack;      // [n_seqs]: (tokens its pack shares or 0, pack size if it leads a pack else 0)
+  int2* seq_pack;      // [n_seqs]: (tokens its pack shares or 0, pack size if it leads a pack
+                       // else 0), kept between plan passes when one pass does not cover the batch
   int4* work;          // [max_units]: (sequence, first token, end token, sequences in the pack)
   int2* work_out;      // [max_units]: (partial slot, partials) of the unit's first sequence
   float* part_ml;      // [max_units * Hq * 2] per slot: running max (log2 units), sum
@@ -327,6 +328,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
 
   // pass 1: slots and full-length rows in sequence order; shorter units counted per bucket
   int32_t row_base = 0, slot_base = 0, run_carry = 0;
+  // this thread's last sequence, kept for pass 2 when one pass covers the batch
+  int64_t keep_L = 0;
+  int32_t keep_first = 0, keep_count = 0, keep_Ls = 0, keep_k = 0;
   for (int32_t base = 0; base < a.n_seqs; base += kPlanThreads) {
     const int32_t b = base + tid;
     const bool in = b < a.n_seqs;
@@ -370,7 +374,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
     const int32_t r0 = row_base + ex.x, f0 = slot_base + ex.y;
     if (in) {
       a.plan.seq_info[b] = make_int4(f0, count, np, 0);
-      a.plan.seq_pack[b] = make_int2(Ls, leader ? k : 0);
+      if (a.n_seqs > kPlanThreads) a.plan.seq_pack[b] = make_int2(Ls, leader ? k : 0);  // for pass 2
       int32_t row = r0;
       if (leader)
         for (int32_t j = 0; j < nshf; ++j, ++row)
@@ -386,6 +390,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
       short_units(T, L, Ls, leader ? k : 0, f0, [&](int32_t t0, int32_t t1, int32_t, int32_t) {
         atomicAdd(&bucket[bucket_of(t1 - t0)], 1);
       });
+      keep_L = L;
+      keep_first = f0;
+      keep_count = count;
+      keep_Ls = Ls;
+      keep_k = leader ? k : 0;
     }
     row_base += tot.x;
     slot_base += tot.y;
@@ -409,14 +418,22 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
   for (int32_t base = 0; base < a.n_seqs; base += kPlanThreads) {
     const int32_t b = base + tid;
     if (b < a.n_seqs) {
-      const int64_t L = length_of(b, false);
-      const int4 si = a.plan.seq_info[b];   // written by this thread in pass 1
-      const int2 sp = a.plan.seq_pack[b];
-      short_units(T, L, sp.x, sp.y, si.x, [&](int32_t t0, int32_t t1, int32_t k, int32_t slot) {
+      int64_t L = keep_L;
+      int32_t first = keep_first, count = keep_count, Ls = keep_Ls, kl = keep_k;
+      if (a.n_seqs > kPlanThreads) {  // uniform: read back what this thread wrote in pass 1
+        L = length_of(b, false);
+        const int4 si = a.plan.seq_info[b];
+        const int2 sp = a.plan.seq_pack[b];
+        first = si.x;
+        count = si.y;
+        Ls = sp.x;
+        kl = sp.y;
+      }
+      short_units(T, L, Ls, kl, first, [&](int32_t t0, int32_t t1, int32_t k, int32_t slot) {
         const int32_t row = F + atomicAdd(&bucket[bucket_of(t1 - t0)], 1);
         if (!overflow) {
           a.plan.work[row] = make_int4(b, t0, t1, k);
-          a.plan.work_out[row] = make_int2(slot, si.y);
+          a.plan.work_out[row] = make_int2(slot, count);
         }
       });
     }
