@@ -91,6 +91,31 @@ __device__ __forceinline__ float pair_max16(float v) {
   return fmaxf(__builtin_bit_cast(float, (uint32_t)x[0]), __builtin_bit_cast(float, (uint32_t)x[1]));
 }
 
+// LDS layout of the staged chunk.
+//
+// Key rows sit in LDS unpadded, with the 16-byte piece c of key row k stored
+// at piece c ^ kswz(k).  One score-fragment read covers key rows
+// {8a + b (+4) : a, b < 4} (the MFMA row order that gives each lane eight
+// consecutive keys) at one piece index.  With rows padded by one piece
+// (a uniform stride) those rows shared banks: on gfx950 the bank-conflict
+// counter (SQ_LDS_BANK_CONFLICT) showed 4 extra cycles per such read, and 0
+// with this swizzle (probe kernels of the exact address patterns).  The XOR
+// uses row bits 0, 1, 3 and 4; bits 2 and 5 (chain Y, second half) are not
+// used, so all rows a lane reads share one swizzle.
+template <int D>
+__device__ __forceinline__ int kswz(int k) {
+  if constexpr (D == 128) return (k & 3) | (((k >> 3) & 3) << 2);
+  return ((k & 3) | (((k >> 3) & 1) << 2)) ^ (((k >> 4) & 1) * 3);
+}
+
+// Value rows (one head_dim row of a chunk's 64 keys, token-minor) sit
+// unpadded too, piece c of row d at c ^ vswz(d).  The value-fragment reads
+// (rows 16 j + 0..15 at one piece index) still show 4 extra cycles per read
+// on the counter, as they did with padded rows; the swizzle is kept for the
+// smaller footprint (the staging writes are conflict-free either way).  Only
+// the row's low four bits are used, so a lane's rows share one swizzle.
+__device__ __forceinline__ int vswz(int d) { return (d & 7) ^ (((d >> 3) & 1) * 3); }
+
 template <int D, int GW>
 __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int NT = 256;             // threads: four waves
@@ -99,8 +124,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int CH = 32 * NH;         // keys per chunk
   constexpr int KI = D / 32;          // score MFMA steps over head_dim
   constexpr int NJ = D / 16;          // value MFMA output tiles over head_dim
-  constexpr int KS = D + 8;           // padded LDS key row (elements)
-  constexpr int VS = CH + 8;          // padded LDS value row (elements)
+  constexpr int KS = D;               // LDS key row (elements); 16-byte pieces swizzled, see kswz
+  constexpr int VS = CH;              // LDS value row (elements); 16-byte pieces swizzled, see vswz
   constexpr int KU = CH * D / 8 / NT; // 16-byte key pieces per thread per chunk
   constexpr int VU = D * CH / 8 / NT; // 16-byte value pieces per thread per chunk
   constexpr int TW = 1024;            // block-table window (entries)
@@ -229,13 +254,13 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     for (int u = 0; u < KU; ++u) {
       const int p = tid + u * NT;
       const int key = p / (D / 8), dc = p % (D / 8);
-      *reinterpret_cast<uint4*>(&k_lds[buf][key * KS + dc * 8]) = kst[u];
+      *reinterpret_cast<uint4*>(&k_lds[buf][key * KS + (dc ^ kswz<D>(key)) * 8]) = kst[u];
     }
 #pragma unroll
     for (int u = 0; u < VU; ++u) {
       const int p = tid + u * NT;
       const int dim = p / (CH / 8), qq = p % (CH / 8);
-      *reinterpret_cast<uint4*>(&v_lds[buf][dim * VS + qq * 8]) = vst[u];
+      *reinterpret_cast<uint4*>(&v_lds[buf][dim * VS + (qq ^ vswz(dim)) * 8]) = vst[u];
     }
   };
 
@@ -253,6 +278,9 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
   const int krow_x = 8 * (nq >> 2) + (nq & 3);  // key of chain-X row nq within the chunk
+  // the swizzle of every key row this lane reads (chains X and Y, both halves)
+  const int kx = kswz<D>(krow_x);
+  const int vx = vswz(nq);  // the swizzle of value rows 16 j + nq
 
   auto compute = [&](int buf, int32_t c0) {
     const uint16_t* kl = k_lds[buf];
@@ -266,8 +294,9 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     for (int h = 0; h < NH; ++h) {
 #pragma unroll
       for (int i = 0; i < KI; ++i) {
-        const bf16x8 ax = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x) * KS + 32 * i + 8 * r]);
-        const bf16x8 ay = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x + 4) * KS + 32 * i + 8 * r]);
+        const int cb = ((4 * i + r) ^ kx) * 8;
+        const bf16x8 ax = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x) * KS + cb]);
+        const bf16x8 ay = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x + 4) * KS + cb]);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           sx[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, qf[t][i], sx[t][h], 0, 0, 0);
@@ -342,7 +371,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     for (int j = 0; j < NJ; ++j) {
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&vl[(16 * j + nq) * VS + 32 * h + 8 * r]);
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&vl[(16 * j + nq) * VS + ((4 * h + r) ^ vx) * 8]);
 #pragma unroll
         for (int t = 0; t < 2; ++t)
           acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[t][h], acc[t][j], 0, 0, 0);

@@ -263,3 +263,42 @@ def test_more_sequences_than_one_plan_pass(monkeypatch):
     worst, most = _step_and_check(kv, batch, keys, vals, 8, seed=21, steps=1, t=128)
     say(f"  1101 sequences: max shared {most}, max err {worst:.3e}")
     kv.close()
+
+
+def test_graph_replay_with_packs(monkeypatch):
+    """A captured decode (plan with packs, partition, merge) replays bit for bit
+    like the eager decode on the same state, while decode steps in between
+    append tokens (and copy-on-write changes nothing the packs rely on)."""
+    import torch
+    monkeypatch.setenv("PKV_PARTITION_TOKENS", "256")
+    hq, hkv, d, p = 16, 4, 128, 16
+    kv, batch, keys, vals = _forest([(700, [0, 3, 40, 0, 9]), (300, [0, 0, 2])], hkv, d, p, seed=12)
+    b, steps = len(batch), 3
+    lens = np.array([len(k) for k in keys])
+    max_len = int(lens.max()) + steps
+    m = kv.prepare(batch, -(-max_len // p), hq, max_len, int(lens.sum()) + b * steps)
+    kv.upload(m)
+    rng = np.random.default_rng(13)
+    q = _randn(rng, (b, hq, d)).cuda()
+    out_e = torch.full_like(q, float("nan"))
+    out_g = torch.full_like(q, float("nan"))
+    kv.attend(m, q, out_e)  # one-time host set-up outside the capture
+    graph = kv.capture_attend(m, q, out_g)
+    for s in range(steps):
+        sk, sv = _randn(rng, (b, hkv, d)), _randn(rng, (b, hkv, d))
+        kv.append_decode_tokens(m, sk.cuda(), sv.cuda())
+        for i in range(b):
+            keys[i] = torch.cat([keys[i], sk[i:i + 1]])
+            vals[i] = torch.cat([vals[i], sv[i:i + 1]])
+        kv.attend(m, q, out_e)
+        kv.check_graph_sizing(m)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), f"replay {s} differs from the eager decode"
+        out_g.fill_(float("nan"))
+    assert int(m.shared.cpu().max()) > 0
+    qb = host_bits(q)
+    for i in range(b):
+        ref = oatt.decode(qb[i], host_bits(keys[i]), host_bits(vals[i]))
+        assert float(np.abs(out_e[i].double().cpu().numpy() - ref).max()) <= BF16_TOL
+    kv.close()
