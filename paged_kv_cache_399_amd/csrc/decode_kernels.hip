@@ -1208,80 +1208,112 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge: out = sum_p w_p o_p / sum_p w_p with w_p = l_p * 2^(m_p - M), M the
-// largest m_p.  One workgroup of four waves per (sequence, query head); wave w
-// folds partitions w, w + 4, ... with a running maximum (four partitions'
-// loads in flight per step), then the four waves are combined through LDS.
-// The fold order depends only on the partition indices.  grid (n_seqs, Hq).
+// Merge.  For query head h of a sequence with n > 1 partial results in slots
+// f0 .. f0 + n - 1 (partition order), over the slots with l_i > 0:
+//   M = max_i m_i,  w_i = l_i 2^(m_i - M),  out = sum_i w_i o_i / sum_i w_i.
+// One workgroup per (sequence, KV head) takes the G query heads of that KV
+// head, kMergeElems output elements per thread (G D / kMergeElems threads,
+// rounded up to whole waves), so the grid is n_seqs * Hkv workgroups; those
+// of a sequence with one partition return at once (it wrote its output
+// directly).  Wave w finds M, the weights (to LDS, the first kMergeSlots
+// slots) and their total for heads w, w + W, ...; meanwhile every thread has
+// issued the loads of its elements' first kMergePre partial outputs, so a
+// merge of up to kMergePre partitions costs one round trip to memory.  Each
+// output element sums its slots in order, so the result does not depend on
+// the launch.
 // ---------------------------------------------------------------------------
-template <typename T, int DK>
-__global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
-  constexpr int W = 4, U = 4;
-  __shared__ float red_m[W], red_s[W];
-  __shared__ float red_o[W][DK * 64];
-  const int32_t b = blockIdx.x, head = blockIdx.y;
+constexpr int kMergeSlots = 128;  // weights kept in LDS per head; later ones are recomputed
+constexpr int kMergePre = 4;      // partial outputs loaded before the weights are known
+constexpr int kMergeElems = 4;    // output elements per thread
+
+// threads of a merge workgroup: G * D <= 16 * 256 elements
+inline int merge_threads(int32_t hq, int32_t hkv, int32_t d) {
+  const int32_t per = (hq / hkv) * d;
+  const int32_t t = (per + kMergeElems - 1) / kMergeElems;
+  return std::min(1024, std::max(64, (t + 63) / 64 * 64));
+}
+
+template <typename T>
+__global__ __launch_bounds__(1024) void merge_kernel(DecodeArgs a) {
+  constexpr int EPT = kMergeElems;
+  __shared__ float wts[16][kMergeSlots];
+  __shared__ float m_head[16], tot_head[16];
+  const int32_t b = blockIdx.x / a.hkv;
+  const int32_t g = blockIdx.x - b * a.hkv;
   const int4 si = a.plan.seq_info[b];
-  const int32_t f0 = si.x, n = si.y;  // slots f0 .. f0 + n - 1, in partition order
-  if (n <= 1) return;
+  const int32_t f0 = si.x, n = si.y;
+  if (n <= 1) return;                 // uniform
   if (a.plan.counts[0] == 0) return;  // plan overflowed
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int32_t D = a.d;
-  float m_run = -INFINITY, s_run = 0.f, acc[DK];
+  const int W = blockDim.x >> 6;
+  const int32_t D = a.d, G = a.hq / a.hkv, GD = G * D;
+  const int64_t slot_stride = (int64_t)a.hq;  // (slot, head) rows per slot
+  const int64_t row0 = (int64_t)f0 * slot_stride + (int64_t)g * G;  // (slot f0, head g G)
+
+  // partial outputs of the first slots, loaded before anything waits
+  float pre[EPT][kMergePre];
 #pragma unroll
-  for (int k = 0; k < DK; ++k) acc[k] = 0.f;
-  for (int32_t i0 = w; i0 < n; i0 += W * U) {
-    float mp[U], lp[U], op[U][DK];
+  for (int k = 0; k < EPT; ++k) {
+    const int32_t e = threadIdx.x + k * blockDim.x;
+    const int32_t hh = e / D, dd = e - hh * D;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int32_t i = i0 + W * u;
-      mp[u] = -INFINITY;
-      lp[u] = 0.f;
-#pragma unroll
-      for (int k = 0; k < DK; ++k) op[u][k] = 0.f;
-      if (i < n) {
-        const int64_t row = (int64_t)(f0 + i) * a.hq + head;
-        mp[u] = a.plan.part_ml[row * 2];
-        lp[u] = a.plan.part_ml[row * 2 + 1];
-#pragma unroll
-        for (int k = 0; k < DK; ++k) {
-          const int32_t dd = lane + 64 * k;
-          if (dd < D) op[u][k] = a.plan.part_o[row * D + dd];
-        }
+    for (int j = 0; j < kMergePre; ++j)
+      pre[k][j] = (e < GD && j < n) ? a.plan.part_o[(row0 + j * slot_stride + hh) * D + dd] : 0.f;
+  }
+
+  for (int32_t hh = w; hh < G; hh += W) {  // uniform per wave
+    const float* ml = a.plan.part_ml + (row0 + hh) * 2;
+    float m0 = 0.f, l0 = 0.f;
+    if (lane < n) {
+      m0 = ml[lane * slot_stride * 2];
+      l0 = ml[lane * slot_stride * 2 + 1];
+    }
+    float mx = l0 > 0.f ? m0 : -INFINITY;
+    for (int32_t i = lane + 64; i < n; i += 64) {
+      const float mi = ml[i * slot_stride * 2], li = ml[i * slot_stride * 2 + 1];
+      if (li > 0.f) mx = fmaxf(mx, mi);
+    }
+    mx = wave_max(mx);
+    float tot = 0.f;
+    for (int32_t i = lane; i < n; i += 64) {
+      float mi = m0, li = l0;
+      if (i >= 64) {
+        mi = ml[i * slot_stride * 2];
+        li = ml[i * slot_stride * 2 + 1];
       }
+      const float wi = li > 0.f ? li * fast_exp2(mi - mx) : 0.f;
+      if (i < kMergeSlots) wts[hh][i] = wi;
+      tot += wi;
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (!(lp[u] > 0.f)) continue;  // empty partition or padding
-      const float m_new = fmaxf(m_run, mp[u]);
-      const float al = fast_exp2(m_run - m_new), wt = lp[u] * fast_exp2(mp[u] - m_new);
-      s_run = fmaf(s_run, al, wt);
-#pragma unroll
-      for (int k = 0; k < DK; ++k) acc[k] = fmaf(acc[k], al, wt * op[u][k]);
-      m_run = m_new;
+    tot = wave_sum(tot);
+    if (lane == 0) {
+      m_head[hh] = mx;
+      tot_head[hh] = tot;
     }
   }
-  if (lane == 0) {
-    red_m[w] = m_run;
-    red_s[w] = s_run;
-  }
-#pragma unroll
-  for (int k = 0; k < DK; ++k) red_o[w][lane + 64 * k] = acc[k];
   __syncthreads();
-  float mx = -INFINITY;
+
 #pragma unroll
-  for (int v = 0; v < W; ++v) mx = fmaxf(mx, red_m[v]);
-  float sc[W], tot = 0.f;
+  for (int k = 0; k < EPT; ++k) {
+    const int32_t e = threadIdx.x + k * blockDim.x;
+    if (e >= GD) continue;
+    const int32_t hh = e / D, dd = e - hh * D;
+    float acc = 0.f;
 #pragma unroll
-  for (int v = 0; v < W; ++v) {
-    sc[v] = red_s[v] > 0.f ? fast_exp2(red_m[v] - mx) : 0.f;
-    tot = fmaf(red_s[v], sc[v], tot);
-  }
-  const float inv = tot > 0.f ? 1.f / tot : 0.f;
-  for (int32_t dd = threadIdx.x; dd < D; dd += blockDim.x) {
-    float o = 0.f;
-#pragma unroll
-    for (int v = 0; v < W; ++v) o = fmaf(sc[v], red_o[v][dd], o);
-    store_f32((T*)a.out + ((int64_t)b * a.hq + head) * D + dd, o * inv);
+    for (int j = 0; j < kMergePre; ++j)
+      if (j < n) acc = fmaf(wts[hh][j], pre[k][j], acc);
+    for (int32_t j = kMergePre; j < n; ++j) {
+      float wj;
+      if (j < kMergeSlots) {
+        wj = wts[hh][j];
+      } else {
+        const float* ml = a.plan.part_ml + (row0 + j * slot_stride + hh) * 2;
+        wj = ml[1] > 0.f ? ml[1] * fast_exp2(ml[0] - m_head[hh]) : 0.f;
+      }
+      acc = fmaf(wj, a.plan.part_o[(row0 + j * slot_stride + hh) * D + dd], acc);
+    }
+    const float tot = tot_head[hh];
+    store_f32((T*)a.out + ((int64_t)b * a.hq + g * G + hh) * D + dd, tot > 0.f ? acc / tot : 0.f);
   }
 }
 
@@ -1505,13 +1537,8 @@ void launch_valu(const DecodeArgs& a, int64_t waves, hipStream_t st) {
 }
 
 template <typename T>
-void launch_merge(const DecodeArgs& a, dim3 grid, hipStream_t st) {
-  switch ((a.d + 63) / 64) {
-    case 1: hipLaunchKernelGGL((merge_kernel<T, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((merge_kernel<T, 2>), grid, dim3(256), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((merge_kernel<T, 3>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((merge_kernel<T, 4>), grid, dim3(256), 0, st, a); break;
-  }
+void launch_merge(const DecodeArgs& a, unsigned grid, hipStream_t st) {
+  hipLaunchKernelGGL((merge_kernel<T>), grid, dim3(merge_threads(a.hq, a.hkv, a.d)), 0, st, a);
 }
 
 }  // namespace
@@ -1641,7 +1668,7 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   }
   // some sequence has several partials: a partition split, or a split shared partition
   if (c.need_partials && (c.part_tokens < std::max<int32_t>(max_context_len, 1) || a.pack_max > 1)) {
-    const dim3 grid((unsigned)n_seqs, (unsigned)num_q_heads);
+    const unsigned grid = (unsigned)((int64_t)n_seqs * num_kv_heads);
     if (dtype == PKV_BF16) pkv::launch_merge<uint16_t>(a, grid, st);
     else pkv::launch_merge<float>(a, grid, st);
   }
