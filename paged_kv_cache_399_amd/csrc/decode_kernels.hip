@@ -1212,30 +1212,31 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
 // f0 .. f0 + n - 1 (partition order), over the slots with l_i > 0:
 //   M = max_i m_i,  w_i = l_i 2^(m_i - M),  out = sum_i w_i o_i / sum_i w_i.
 // One workgroup per (sequence, KV head) takes the G query heads of that KV
-// head, kMergeElems output elements per thread (G D / kMergeElems threads,
-// rounded up to whole waves), so the grid is n_seqs * Hkv workgroups; those
+// head, EPT output elements per thread (G D / EPT threads, rounded up to
+// whole waves), so the grid is n_seqs * Hkv workgroups; those
 // of a sequence with one partition return at once (it wrote its output
 // directly).  Wave w finds M, the weights (to LDS, the first kMergeSlots
-// slots) and their total for heads w, w + W, ...; meanwhile every thread has
-// issued the loads of its elements' first kMergePre partial outputs, so a
-// merge of up to kMergePre partitions costs one round trip to memory.  Each
-// output element sums its slots in order, so the result does not depend on
-// the launch.
+// slots) and their total for heads w, w + W, ...; before any of that waits,
+// every thread has issued the loads of its elements' first kMergePre partial
+// outputs and of the first 64 slots' (m, l) of its wave's first kMergeHeads
+// heads, so a merge of up to kMergePre partitions costs one round trip to
+// memory (later slots: one more per kMergePre).  Each output element sums its
+// slots in order, so the result does not depend on the launch.
 // ---------------------------------------------------------------------------
 constexpr int kMergeSlots = 128;  // weights kept in LDS per head; later ones are recomputed
 constexpr int kMergePre = 4;      // partial outputs loaded before the weights are known
-constexpr int kMergeElems = 4;    // output elements per thread
+constexpr int kMergeElems = 4;    // most output elements per thread (G D up to 4096)
+constexpr int kMergeHeads = 4;    // heads per wave whose first slots' (m, l) are loaded up front
 
-// threads of a merge workgroup: G * D <= 16 * 256 elements
-inline int merge_threads(int32_t hq, int32_t hkv, int32_t d) {
+// threads of a merge workgroup for `ept` elements per thread (G * D <= 4096)
+inline int merge_threads(int32_t hq, int32_t hkv, int32_t d, int ept) {
   const int32_t per = (hq / hkv) * d;
-  const int32_t t = (per + kMergeElems - 1) / kMergeElems;
+  const int32_t t = (per + ept - 1) / ept;
   return std::min(1024, std::max(64, (t + 63) / 64 * 64));
 }
 
-template <typename T>
+template <typename T, int EPT>
 __global__ __launch_bounds__(1024) void merge_kernel(DecodeArgs a) {
-  constexpr int EPT = kMergeElems;
   __shared__ float wts[16][kMergeSlots];
   __shared__ float m_head[16], tot_head[16];
   const int32_t b = blockIdx.x / a.hkv;
@@ -1250,36 +1251,57 @@ __global__ __launch_bounds__(1024) void merge_kernel(DecodeArgs a) {
   const int64_t slot_stride = (int64_t)a.hq;  // (slot, head) rows per slot
   const int64_t row0 = (int64_t)f0 * slot_stride + (int64_t)g * G;  // (slot f0, head g G)
 
-  // partial outputs of the first slots, loaded before anything waits
-  float pre[EPT][kMergePre];
+  // this thread's output elements: head hk[k], element dk[k] (ok[k]: in range)
+  int32_t hk[EPT], dk[EPT];
+  bool ok[EPT];
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
     const int32_t e = threadIdx.x + k * blockDim.x;
-    const int32_t hh = e / D, dd = e - hh * D;
+    ok[k] = e < GD;
+    hk[k] = ok[k] ? e / D : 0;
+    dk[k] = ok[k] ? e - hk[k] * D : 0;
+  }
+  auto o_ptr = [&](int32_t j, int k) -> const float* {
+    return a.plan.part_o + (row0 + j * slot_stride + hk[k]) * D + dk[k];
+  };
+  auto ml_ptr = [&](int32_t i, int32_t hh) -> const float* {
+    return a.plan.part_ml + (row0 + i * slot_stride + hh) * 2;
+  };
+
+  // Loads issued before anything waits: the first kMergePre partial outputs
+  // of this thread's elements, and (m, l) of slot `lane` for the wave's first
+  // kMergeHeads heads.
+  float pre[EPT][kMergePre];
 #pragma unroll
-    for (int j = 0; j < kMergePre; ++j)
-      pre[k][j] = (e < GD && j < n) ? a.plan.part_o[(row0 + j * slot_stride + hh) * D + dd] : 0.f;
+  for (int k = 0; k < EPT; ++k)
+#pragma unroll
+    for (int j = 0; j < kMergePre; ++j) pre[k][j] = (ok[k] && j < n) ? *o_ptr(j, k) : 0.f;
+  float m0[kMergeHeads], l0[kMergeHeads];
+#pragma unroll
+  for (int r = 0; r < kMergeHeads; ++r) {
+    const int32_t hh = w + r * W;
+    m0[r] = 0.f;
+    l0[r] = 0.f;
+    if (hh < G && lane < n) {
+      m0[r] = ml_ptr(lane, hh)[0];
+      l0[r] = ml_ptr(lane, hh)[1];
+    }
   }
 
-  for (int32_t hh = w; hh < G; hh += W) {  // uniform per wave
-    const float* ml = a.plan.part_ml + (row0 + hh) * 2;
-    float m0 = 0.f, l0 = 0.f;
-    if (lane < n) {
-      m0 = ml[lane * slot_stride * 2];
-      l0 = ml[lane * slot_stride * 2 + 1];
-    }
-    float mx = l0 > 0.f ? m0 : -INFINITY;
+  // maximum, weights and total of head hh (uniform per wave); mf, lf: slot `lane`
+  auto head_stats = [&](int32_t hh, float mf, float lf) {
+    float mx = lf > 0.f ? mf : -INFINITY;
     for (int32_t i = lane + 64; i < n; i += 64) {
-      const float mi = ml[i * slot_stride * 2], li = ml[i * slot_stride * 2 + 1];
+      const float mi = ml_ptr(i, hh)[0], li = ml_ptr(i, hh)[1];
       if (li > 0.f) mx = fmaxf(mx, mi);
     }
     mx = wave_max(mx);
     float tot = 0.f;
     for (int32_t i = lane; i < n; i += 64) {
-      float mi = m0, li = l0;
+      float mi = mf, li = lf;
       if (i >= 64) {
-        mi = ml[i * slot_stride * 2];
-        li = ml[i * slot_stride * 2 + 1];
+        mi = ml_ptr(i, hh)[0];
+        li = ml_ptr(i, hh)[1];
       }
       const float wi = li > 0.f ? li * fast_exp2(mi - mx) : 0.f;
       if (i < kMergeSlots) wts[hh][i] = wi;
@@ -1290,30 +1312,56 @@ __global__ __launch_bounds__(1024) void merge_kernel(DecodeArgs a) {
       m_head[hh] = mx;
       tot_head[hh] = tot;
     }
+  };
+#pragma unroll
+  for (int r = 0; r < kMergeHeads; ++r)
+    if (w + r * W < G) head_stats(w + r * W, m0[r], l0[r]);
+  for (int32_t hh = w + kMergeHeads * W; hh < G; hh += W) {
+    float mf = 0.f, lf = 0.f;
+    if (lane < n) {
+      mf = ml_ptr(lane, hh)[0];
+      lf = ml_ptr(lane, hh)[1];
+    }
+    head_stats(hh, mf, lf);
   }
   __syncthreads();
 
+  float acc[EPT];
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
-    const int32_t e = threadIdx.x + k * blockDim.x;
-    if (e >= GD) continue;
-    const int32_t hh = e / D, dd = e - hh * D;
-    float acc = 0.f;
+    acc[k] = 0.f;
 #pragma unroll
     for (int j = 0; j < kMergePre; ++j)
-      if (j < n) acc = fmaf(wts[hh][j], pre[k][j], acc);
-    for (int32_t j = kMergePre; j < n; ++j) {
-      float wj;
-      if (j < kMergeSlots) {
-        wj = wts[hh][j];
-      } else {
-        const float* ml = a.plan.part_ml + (row0 + j * slot_stride + hh) * 2;
-        wj = ml[1] > 0.f ? ml[1] * fast_exp2(ml[0] - m_head[hh]) : 0.f;
+      if (ok[k] && j < n) acc[k] = fmaf(wts[hk[k]][j], pre[k][j], acc[k]);
+  }
+  // later slots, kMergePre at a time with all their loads issued together
+  for (int32_t j0 = kMergePre; j0 < n; j0 += kMergePre) {
+    float ov[EPT][kMergePre];
+#pragma unroll
+    for (int k = 0; k < EPT; ++k)
+#pragma unroll
+      for (int u = 0; u < kMergePre; ++u) ov[k][u] = (ok[k] && j0 + u < n) ? *o_ptr(j0 + u, k) : 0.f;
+#pragma unroll
+    for (int k = 0; k < EPT; ++k)
+#pragma unroll
+      for (int u = 0; u < kMergePre; ++u) {
+        const int32_t j = j0 + u;
+        if (!ok[k] || j >= n) continue;
+        float wj;
+        if (j < kMergeSlots) {
+          wj = wts[hk[k]][j];
+        } else {
+          const float* ml = ml_ptr(j, hk[k]);
+          wj = ml[1] > 0.f ? ml[1] * fast_exp2(ml[0] - m_head[hk[k]]) : 0.f;
+        }
+        acc[k] = fmaf(wj, ov[k][u], acc[k]);
       }
-      acc = fmaf(wj, a.plan.part_o[(row0 + j * slot_stride + hh) * D + dd], acc);
-    }
-    const float tot = tot_head[hh];
-    store_f32((T*)a.out + ((int64_t)b * a.hq + g * G + hh) * D + dd, tot > 0.f ? acc / tot : 0.f);
+  }
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    if (!ok[k]) continue;
+    const float tot = tot_head[hk[k]];
+    store_f32((T*)a.out + ((int64_t)b * a.hq + g * G + hk[k]) * D + dk[k], tot > 0.f ? acc[k] / tot : 0.f);
   }
 }
 
@@ -1538,7 +1586,19 @@ void launch_valu(const DecodeArgs& a, int64_t waves, hipStream_t st) {
 
 template <typename T>
 void launch_merge(const DecodeArgs& a, unsigned grid, hipStream_t st) {
-  hipLaunchKernelGGL((merge_kernel<T>), grid, dim3(merge_threads(a.hq, a.hkv, a.d)), 0, st, a);
+  // Elements per thread: measured best is one for small batches (more waves
+  // hide the latency of a short launch) and two for large ones (fewer waves
+  // to dispatch); raised until G * D fits 1024 threads.
+  const int32_t gd = (a.hq / a.hkv) * a.d;
+  const int64_t elems = (int64_t)a.n_seqs * a.hkv * gd;
+  const int dflt = elems <= (int64_t)1 << 19 ? 1 : 2;
+  int ept = std::max(1, std::min<int>(kMergeElems, env_int("PKV_MERGE_ELEMS", dflt)));
+  while (ept < kMergeElems && gd > 1024 * ept) ept *= 2;
+  ept = ept >= 4 ? 4 : (ept >= 2 ? 2 : 1);
+  const dim3 block(merge_threads(a.hq, a.hkv, a.d, ept));
+  if (ept == 1) hipLaunchKernelGGL((merge_kernel<T, 1>), grid, block, 0, st, a);
+  else if (ept == 2) hipLaunchKernelGGL((merge_kernel<T, 2>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((merge_kernel<T, 4>), grid, block, 0, st, a);
 }
 
 }  // namespace

@@ -369,3 +369,27 @@ def test_token_major_key_layout(monkeypatch, math, dtype, hq, hkv, d, p):
     head = build_case(cfg, seed=13, fill=7.0)
     assert torch.equal(case.out, head.out)
     say(f"  {cfg.name}: max err {err:.3e}")
+
+
+@pytest.mark.parametrize("math,dtype,hq,hkv,d,p,part", [
+    ("mfma", "bf16", 32, 8, 128, 16, "128"),   # matrix cores, G = 4
+    ("mfma", "bf16", 16, 1, 64, 16, "128"),    # G = 16: one wave per two heads in the merge
+    ("dpp", "f32", 8, 2, 128, 16, "64"),
+    ("generic", "bf16", 6, 2, 96, 8, "64"),
+])
+@pytest.mark.parametrize("ept", ["1", "2", "4"])
+def test_many_partitions_merge(monkeypatch, math, dtype, hq, hkv, d, p, part, ept):
+    """Sequences of up to 21,000 tokens cut into up to 330 partitions: the merge
+    takes slots past the first 64 (second pass for the maximum) and past the
+    first 128 (weights recomputed instead of kept in LDS), plus sequences of
+    one partition and of exactly one partition boundary; with 1, 2 and 4
+    output elements per merge thread."""
+    monkeypatch.setenv("PKV_DECODE_MATH", math)
+    monkeypatch.setenv("PKV_PARTITION_TOKENS", part)
+    monkeypatch.setenv("PKV_MERGE_ELEMS", ept)
+    lengths = (21000, 9000, 1, 8193, 128, 129, 4100)
+    cfg = DecodeConfig(f"many_{math}_{dtype}_{hq}_{hkv}_{d}_{p}", len(lengths), hq, hkv, d, p, dtype,
+                       "fixed", fixed_lengths=lengths)
+    case = build_case(cfg, seed=6)
+    err = check_attention(case)
+    say(f"  {cfg.name} T={part} merge elements {ept}: max err {err:.3e}")
