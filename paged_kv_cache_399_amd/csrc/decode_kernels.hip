@@ -136,6 +136,32 @@ __device__ __forceinline__ uint32_t load_stream4(const uint16_t* p) {
 
 __device__ __forceinline__ uint16_t load_stream2(const uint16_t* p) { return __builtin_nontemporal_load(p); }
 
+// Key/value loads: nontemporal (streaming) by default.  In a batch of
+// sequences that share blocks, the shared blocks are read once per pack of
+// sharers, and every pack over the same blocks runs on the same XCD (same KV
+// head); there cached loads (KEEP) let the next pack find them in L2, and
+// they also measured faster for the short private units of such batches.
+template <bool KEEP>
+__device__ __forceinline__ uint4 load_kv16(const uint16_t* p) {
+  if constexpr (KEEP) return *reinterpret_cast<const uint4*>(p);
+  else return load_stream16(p);
+}
+template <bool KEEP>
+__device__ __forceinline__ uint2 load_kv8(const uint16_t* p) {
+  if constexpr (KEEP) return *reinterpret_cast<const uint2*>(p);
+  else return load_stream8(p);
+}
+template <bool KEEP>
+__device__ __forceinline__ uint32_t load_kv4(const uint16_t* p) {
+  if constexpr (KEEP) return *reinterpret_cast<const uint32_t*>(p);
+  else return load_stream4(p);
+}
+template <bool KEEP>
+__device__ __forceinline__ uint16_t load_kv2(const uint16_t* p) {
+  if constexpr (KEEP) return *p;
+  else return load_stream2(p);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -474,7 +500,7 @@ struct MfmaChunk {
 // LDS at the end.  So a partial result goes to HBM once per workgroup, not
 // once per wave: partial-result writes interleaved with the key/value read
 // stream cost far more than their byte count.
-template <int D, int P, int W>
+template <int D, int P, int W, bool KEEP>
 __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
   using Chunk = MfmaChunk<D, P>;
   constexpr int KI = Chunk::KI, NJ = Chunk::NJ;
@@ -599,8 +625,8 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
         const uint16_t* kyp = kb + (ty % P) * ktok;
 #pragma unroll
         for (int i = 0; i < KI; ++i) {
-          f.kx[i] = load_stream16(kxp + 32 * i);
-          f.ky[i] = load_stream16(kyp + 32 * i);
+          f.kx[i] = load_kv16<KEEP>(kxp + 32 * i);
+          f.ky[i] = load_kv16<KEEP>(kyp + 32 * i);
         }
         // values: tokens c0 + 8 r .. +7 of head_dim rows 16 j + n
         const int32_t tv = min(c0 + 8 * r, wlast);
@@ -615,11 +641,11 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
             for (int j = 0; j < NJ; ++j) f.v[j] = *reinterpret_cast<const uint4*>(vb + 16 * j * P);
           } else {
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) f.v[j] = load_stream16(vb + 16 * j * P);
+            for (int j = 0; j < NJ; ++j) f.v[j] = load_kv16<KEEP>(vb + 16 * j * P);
           }
         } else {
 #pragma unroll
-          for (int j = 0; j < NJ; ++j) f.v[j] = load_stream16(vb + 16 * j * P);
+          for (int j = 0; j < NJ; ++j) f.v[j] = load_kv16<KEEP>(vb + 16 * j * P);
         }
       } else {
         // Blocks of fewer than 8 tokens: each lane reads its entries from the
@@ -629,8 +655,8 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
         const uint16_t* kyp = kc + (int64_t)pick(ty) * blk_stride + khead_off + 8 * r + (ty % P) * ktok;
 #pragma unroll
         for (int i = 0; i < KI; ++i) {
-          f.kx[i] = load_stream16(kxp + 32 * i);
-          f.ky[i] = load_stream16(kyp + 32 * i);
+          f.kx[i] = load_kv16<KEEP>(kxp + 32 * i);
+          f.ky[i] = load_kv16<KEEP>(kyp + 32 * i);
         }
         // values: tokens c0 + 8 r .. +7 of head_dim rows 16 j + n, as 8 / P
         // runs of P tokens (2 P bytes) from as many blocks; each run starts a
@@ -649,18 +675,18 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
           if constexpr (P == 4) {
 #pragma unroll
             for (int pi = 0; pi < 2; ++pi) {
-              const uint2 x = load_stream8(vp[pi] + 16 * j * P);
+              const uint2 x = load_kv8<KEEP>(vp[pi] + 16 * j * P);
               wv[2 * pi] = x.x;
               wv[2 * pi + 1] = x.y;
             }
           } else if constexpr (P == 2) {
 #pragma unroll
-            for (int pi = 0; pi < 4; ++pi) wv[pi] = load_stream4(vp[pi] + 16 * j * P);
+            for (int pi = 0; pi < 4; ++pi) wv[pi] = load_kv4<KEEP>(vp[pi] + 16 * j * P);
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              wv[e] = (uint32_t)load_stream2(vp[2 * e] + 16 * j) |
-                      ((uint32_t)load_stream2(vp[2 * e + 1] + 16 * j) << 16);
+              wv[e] = (uint32_t)load_kv2<KEEP>(vp[2 * e] + 16 * j) |
+                      ((uint32_t)load_kv2<KEEP>(vp[2 * e + 1] + 16 * j) << 16);
           }
           f.v[j] = uint4{wv[0], wv[1], wv[2], wv[3]};
         }
@@ -1530,10 +1556,15 @@ Layout layout_of(int32_t n_seqs, int32_t hq, int32_t d, const Choice& c) {
 
 template <int D, int P>
 void launch_mfma(const DecodeArgs& a, int32_t waves_per_group, int64_t groups, hipStream_t st) {
-  if (waves_per_group == 8)
-    hipLaunchKernelGGL((decode_mfma_kernel<D, P, 8>), dim3((unsigned)groups), dim3(512), 0, st, a);
-  else
-    hipLaunchKernelGGL((decode_mfma_kernel<D, P, 4>), dim3((unsigned)groups), dim3(256), 0, st, a);
+  // cached key/value loads when the batch packs sequences that share blocks
+  const bool keep = a.pack_max > 1;
+  if (waves_per_group == 8) {
+    if (keep) hipLaunchKernelGGL((decode_mfma_kernel<D, P, 8, true>), dim3((unsigned)groups), dim3(512), 0, st, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<D, P, 8, false>), dim3((unsigned)groups), dim3(512), 0, st, a);
+  } else {
+    if (keep) hipLaunchKernelGGL((decode_mfma_kernel<D, P, 4, true>), dim3((unsigned)groups), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<D, P, 4, false>), dim3((unsigned)groups), dim3(256), 0, st, a);
+  }
 }
 
 template <int D>
