@@ -276,9 +276,9 @@ int pkv_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_
  *                    bit-identical to a call with NULL and the same sizing
  *                    arguments (which fix T); otherwise the partition split by
  *                    the end of the shared tokens is summed as two partials.
- *                    Such a call reads keys and values with cached loads
- *                    (so packs over one prefix find it in L2); a call with
- *                    NULL streams them with nontemporal loads.
+ *                    A pack reads its shared tokens with cached loads (the
+ *                    next pack over the same prefix finds them in L2); all
+ *                    other keys and values stream with nontemporal loads.
  *                    The tables are not
  *                    compared: a count larger than the true shared prefix makes
  *                    that sequence read its predecessor's tokens (in bounds).

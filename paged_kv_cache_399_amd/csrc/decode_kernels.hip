@@ -52,6 +52,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "internal.hpp"
@@ -136,11 +137,10 @@ __device__ __forceinline__ uint32_t load_stream4(const uint16_t* p) {
 
 __device__ __forceinline__ uint16_t load_stream2(const uint16_t* p) { return __builtin_nontemporal_load(p); }
 
-// Key/value loads: nontemporal (streaming) by default.  In a batch of
-// sequences that share blocks, the shared blocks are read once per pack of
-// sharers, and every pack over the same blocks runs on the same XCD (same KV
-// head); there cached loads (KEEP) let the next pack find them in L2, and
-// they also measured faster for the short private units of such batches.
+// Key/value loads: nontemporal (streaming) for data read once.  Blocks that
+// several sequences share are read once per pack of sharers, and every pack
+// over the same blocks runs on the same XCD (same KV head); for those, cached
+// loads (KEEP) let the next pack find them in that XCD's L2.
 template <bool KEEP>
 __device__ __forceinline__ uint4 load_kv16(const uint16_t* p) {
   if constexpr (KEEP) return *reinterpret_cast<const uint4*>(p);
@@ -500,7 +500,7 @@ struct MfmaChunk {
 // LDS at the end.  So a partial result goes to HBM once per workgroup, not
 // once per wave: partial-result writes interleaved with the key/value read
 // stream cost far more than their byte count.
-template <int D, int P, int W, bool KEEP>
+template <int D, int P, int W, bool MIXED>
 __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
   using Chunk = MfmaChunk<D, P>;
   constexpr int KI = Chunk::KI, NJ = Chunk::NJ;
@@ -596,7 +596,8 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
     // A chunk spans at most NBC blocks; their ids are read from the window
     // with uniform lane reads and each lane picks its own.
     constexpr int NBC = CH / P > 1 ? CH / P : 1;
-    auto issue = [&](Chunk& f, int32_t c0) {
+    auto issue = [&](Chunk& f, int32_t c0, auto keep_tag) {
+      constexpr bool KEEP = decltype(keep_tag)::value;
       const int32_t tx = min(c0 + krow_x, wlast);
       const int32_t ty = min(c0 + krow_x + 4, wlast);
       if constexpr (P >= 8) {
@@ -747,25 +748,36 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
     // length), so chunks never straddle two windows.  Within a window the
     // next chunk's loads are in flight while the current one is computed;
     // the prefetch past the window end reads clamped, in-bounds addresses.
-    for (int32_t ws = s0; ws < s1;) {
-      wb = uniform(ws / P);
-      const int32_t we = min(s1, (wb + 64 * KW) * P);
-      wlast = we - 1;
-      load_window(wb);
-      Chunk f0, f1;
-      int32_t c0 = ws;
-      issue(f0, c0);
-      while (true) {
-        issue(f1, c0 + CH);
-        compute(f0, c0);
-        c0 += CH;
-        if (c0 >= we) break;
-        issue(f0, c0 + CH);
-        compute(f1, c0);
-        c0 += CH;
-        if (c0 >= we) break;
+    auto stream = [&](auto keep_tag) {
+      for (int32_t ws = s0; ws < s1;) {
+        wb = uniform(ws / P);
+        const int32_t we = min(s1, (wb + 64 * KW) * P);
+        wlast = we - 1;
+        load_window(wb);
+        Chunk f0, f1;
+        int32_t c0 = ws;
+        issue(f0, c0, keep_tag);
+        while (true) {
+          issue(f1, c0 + CH, keep_tag);
+          compute(f0, c0);
+          c0 += CH;
+          if (c0 >= we) break;
+          issue(f0, c0 + CH, keep_tag);
+          compute(f1, c0);
+          c0 += CH;
+          if (c0 >= we) break;
+        }
+        ws = we;
       }
-      ws = we;
+    };
+    // a pack's tokens are shared by all its members and by the packs after
+    // it: cached loads; everything else streams.  Only batches with packs
+    // get the second copy of the loop (MIXED).
+    if constexpr (MIXED) {
+      if (u.pack > 1) stream(std::true_type{});  // uniform
+      else stream(std::false_type{});
+    } else {
+      stream(std::false_type{});
     }
   }
 
@@ -1556,7 +1568,8 @@ Layout layout_of(int32_t n_seqs, int32_t hq, int32_t d, const Choice& c) {
 
 template <int D, int P>
 void launch_mfma(const DecodeArgs& a, int32_t waves_per_group, int64_t groups, hipStream_t st) {
-  // cached key/value loads when the batch packs sequences that share blocks
+  // a batch that packs sequences sharing blocks reads the packs' tokens with
+  // cached loads
   const bool keep = a.pack_max > 1;
   if (waves_per_group == 8) {
     if (keep) hipLaunchKernelGGL((decode_mfma_kernel<D, P, 8, true>), dim3((unsigned)groups), dim3(512), 0, st, a);
