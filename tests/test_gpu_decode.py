@@ -376,6 +376,7 @@ def test_token_major_key_layout(monkeypatch, math, dtype, hq, hkv, d, p):
     ("mfma", "bf16", 16, 1, 64, 16, "128"),    # G = 16: one wave per two heads in the merge
     ("dpp", "f32", 8, 2, 128, 16, "64"),
     ("generic", "bf16", 6, 2, 96, 8, "64"),
+    ("generic", "bf16", 16, 1, 256, 16, "64"),  # G D = 4096: four elements per thread whatever is asked
 ])
 @pytest.mark.parametrize("ept", ["1", "2", "4"])
 def test_many_partitions_merge(monkeypatch, math, dtype, hq, hkv, d, p, part, ept):
