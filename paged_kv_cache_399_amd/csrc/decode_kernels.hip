@@ -222,10 +222,11 @@ __device__ __forceinline__ Unit decode_unit(const DecodeArgs& a, int32_t unit) {
 // remainder [Ls, min((j0+1) T, L)) (slot first + j0); a member with no
 // remainder takes the tail in slot first + j0.  Everything from partition
 // j0 + 1 on (from j0 if Ls % T == 0) is the member's own.
-// One workgroup of kPlanThreads threads.
+// One workgroup of NT threads (256 for batches of up to 256 sequences, else
+// 1024), one length bucket per thread.
 // ---------------------------------------------------------------------------
-constexpr int kPlanThreads = 1024;
-constexpr int kPlanBuckets = 1024;  // one bucket per plan thread
+constexpr int kPlanThreads = 1024;  // the larger plan workgroup
+constexpr int kPlanSmall = 256;     // the plan workgroup for up to this many sequences
 constexpr int kPackMax = 16;        // MFMA columns
 constexpr int kShareChunk = 32;     // granularity of a pack's shared tokens (the decode chunk)
 
@@ -318,12 +319,13 @@ __device__ __forceinline__ void short_units(int32_t T, int64_t L, int32_t Ls, in
   }
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
+template <int NT>
+__global__ __launch_bounds__(NT) void plan_kernel(DecodeArgs a) {
   __shared__ int32_t smem[16];
   __shared__ __align__(8) int32_t smem64[32];
-  __shared__ int32_t bucket[kPlanBuckets];  // counts, then the next free offset of each bucket
-  // j_m for m in [base - kPackMax, base + kPlanThreads + kPackMax)
-  __shared__ int32_t jt[kPackMax + kPlanThreads + kPackMax];
+  __shared__ int32_t bucket[NT];  // counts, then the next free offset of each bucket
+  // j_m for m in [base - kPackMax, base + NT + kPackMax)
+  __shared__ int32_t jt[kPackMax + NT + kPackMax];
   const int32_t T = a.part_tokens;
   const int64_t cap = a.len_cap;
   const int32_t S = a.pack_max;
@@ -348,8 +350,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
     return (int32_t)(sh / kShareChunk);
   };
   // a unit of c < T tokens: bucket 0 holds the longest (T - 1 tokens)
+  const int lg_t = 31 - __builtin_clz((uint32_t)T);  // T is a power of two
   auto bucket_of = [&](int32_t c) -> int32_t {
-    return (int32_t)(((int64_t)(T - 1 - c) * kPlanBuckets) / T);
+    return (int32_t)(((int64_t)(T - 1 - c) * NT) >> lg_t);
   };
 
   // pass 1: slots and full-length rows in sequence order; shorter units counted per bucket
@@ -357,7 +360,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
   // this thread's last sequence, kept for pass 2 when one pass covers the batch
   int64_t keep_L = 0;
   int32_t keep_first = 0, keep_count = 0, keep_Ls = 0, keep_k = 0;
-  for (int32_t base = 0; base < a.n_seqs; base += kPlanThreads) {
+  for (int32_t base = 0; base < a.n_seqs; base += NT) {
     const int32_t b = base + tid;
     const bool in = b < a.n_seqs;
     int64_t L = 0;
@@ -371,7 +374,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
     if (S >= 2) {  // uniform
       const int32_t jb = in ? joins(b) : 0;
       jt[kPackMax + tid] = jb;
-      if (tid < kPackMax) jt[kPackMax + kPlanThreads + tid] = joins(base + kPlanThreads + tid);
+      if (tid < kPackMax) jt[kPackMax + NT + tid] = joins(base + NT + tid);
       // start of the run holding b: the last sequence at or before b that joins nothing
       int32_t cmax;
       const int32_t st = max(run_carry, block_inclusive_max(in && jb == 0 ? b : -1, smem, &cmax));
@@ -381,7 +384,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
       if (in) {
         int32_t mn = INT32_MAX;
         for (int32_t i = 1; i < S; ++i) {
-          const int32_t jm = jt[kPackMax + lead + i - base];  // lead + i - base in [-15, 1039)
+          const int32_t jm = jt[kPackMax + lead + i - base];  // lead + i - base in [-15, NT + 15)
           if (jm == 0) break;
           mn = min(mn, jm);
           ++k;
@@ -400,7 +403,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
     const int32_t r0 = row_base + ex.x, f0 = slot_base + ex.y;
     if (in) {
       a.plan.seq_info[b] = make_int4(f0, count, np, 0);
-      if (a.n_seqs > kPlanThreads) a.plan.seq_pack[b] = make_int2(Ls, leader ? k : 0);  // for pass 2
+      if (a.n_seqs > NT) a.plan.seq_pack[b] = make_int2(Ls, leader ? k : 0);  // for pass 2
       int32_t row = r0;
       if (leader)
         for (int32_t j = 0; j < nshf; ++j, ++row)
@@ -427,7 +430,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
     if (S >= 2) {
       // carry the last kPackMax entries over as the next chunk's look-behind
       __syncthreads();
-      if (tid < kPackMax) jt[tid] = jt[kPlanThreads + tid];
+      if (tid < kPackMax) jt[tid] = jt[NT + tid];
       __syncthreads();
     }
   }
@@ -441,12 +444,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeArgs a) {
   const bool overflow = (int64_t)F + R > a.max_units || FS > a.max_units;
 
   // pass 2: shorter units, longest bucket first (order inside a bucket is free)
-  for (int32_t base = 0; base < a.n_seqs; base += kPlanThreads) {
+  for (int32_t base = 0; base < a.n_seqs; base += NT) {
     const int32_t b = base + tid;
     if (b < a.n_seqs) {
       int64_t L = keep_L;
       int32_t first = keep_first, count = keep_count, Ls = keep_Ls, kl = keep_k;
-      if (a.n_seqs > kPlanThreads) {  // uniform: read back what this thread wrote in pass 1
+      if (a.n_seqs > NT) {  // uniform: read back what this thread wrote in pass 1
         L = length_of(b, false);
         const int4 si = a.plan.seq_info[b];
         const int2 sp = a.plan.seq_pack[b];
@@ -1756,7 +1759,10 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   a.err = err;
 
   hipStream_t st = (hipStream_t)stream;
-  hipLaunchKernelGGL(pkv::plan_kernel, dim3(1), dim3(pkv::kPlanThreads), 0, st, a);
+  if (n_seqs <= pkv::kPlanSmall)
+    hipLaunchKernelGGL(pkv::plan_kernel<pkv::kPlanSmall>, dim3(1), dim3(pkv::kPlanSmall), 0, st, a);
+  else
+    hipLaunchKernelGGL(pkv::plan_kernel<pkv::kPlanThreads>, dim3(1), dim3(pkv::kPlanThreads), 0, st, a);
   const int64_t waves = c.max_units * num_kv_heads;
   if (c.kind == pkv::kKindMfma) {
     const int32_t W = c.waves_per_group;
