@@ -222,11 +222,10 @@ __device__ __forceinline__ Unit decode_unit(const DecodeArgs& a, int32_t unit) {
 // remainder [Ls, min((j0+1) T, L)) (slot first + j0); a member with no
 // remainder takes the tail in slot first + j0.  Everything from partition
 // j0 + 1 on (from j0 if Ls % T == 0) is the member's own.
-// One workgroup of NT threads (256 for batches of up to 256 sequences, else
-// 1024), one length bucket per thread.
+// One workgroup of NT threads (the smallest of 64, 128, 256 that covers the
+// batch, else 1024), one length bucket per thread.
 // ---------------------------------------------------------------------------
-constexpr int kPlanThreads = 1024;  // the larger plan workgroup
-constexpr int kPlanSmall = 256;     // the plan workgroup for up to this many sequences
+constexpr int kPlanThreads = 1024;  // the plan workgroup for batches of more than 256 sequences
 constexpr int kPackMax = 16;        // MFMA columns
 constexpr int kShareChunk = 32;     // granularity of a pack's shared tokens (the decode chunk)
 
@@ -1759,10 +1758,11 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   a.err = err;
 
   hipStream_t st = (hipStream_t)stream;
-  if (n_seqs <= pkv::kPlanSmall)
-    hipLaunchKernelGGL(pkv::plan_kernel<pkv::kPlanSmall>, dim3(1), dim3(pkv::kPlanSmall), 0, st, a);
-  else
-    hipLaunchKernelGGL(pkv::plan_kernel<pkv::kPlanThreads>, dim3(1), dim3(pkv::kPlanThreads), 0, st, a);
+  // fewer plan threads finish sooner (fewer waves per SIMD on one compute unit)
+  if (n_seqs <= 64) hipLaunchKernelGGL(pkv::plan_kernel<64>, dim3(1), dim3(64), 0, st, a);
+  else if (n_seqs <= 128) hipLaunchKernelGGL(pkv::plan_kernel<128>, dim3(1), dim3(128), 0, st, a);
+  else if (n_seqs <= 256) hipLaunchKernelGGL(pkv::plan_kernel<256>, dim3(1), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(pkv::plan_kernel<pkv::kPlanThreads>, dim3(1), dim3(pkv::kPlanThreads), 0, st, a);
   const int64_t waves = c.max_units * num_kv_heads;
   if (c.kind == pkv::kKindMfma) {
     const int32_t W = c.waves_per_group;
