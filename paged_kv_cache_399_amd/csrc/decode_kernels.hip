@@ -1638,9 +1638,9 @@ void launch_merge(const DecodeArgs& a, unsigned grid, hipStream_t st) {
   const int32_t gd = (a.hq / a.hkv) * a.d;
   const int64_t elems = (int64_t)a.n_seqs * a.hkv * gd;
   const int dflt = elems <= (int64_t)1 << 19 ? 1 : 2;
-  int ept = std::max(1, std::min<int>(kMergeElems, env_int("PKV_MERGE_ELEMS", dflt)));
-  while (ept < kMergeElems && gd > 1024 * ept) ept *= 2;
-  ept = ept >= 4 ? 4 : (ept >= 2 ? 2 : 1);
+  const int want = env_int("PKV_MERGE_ELEMS", dflt);
+  int ept = want >= 4 ? 4 : (want >= 2 ? 2 : 1);  // an instantiated width
+  while (ept < kMergeElems && gd > 1024 * ept) ept *= 2;  // G D <= 4096 = 1024 * kMergeElems
   const dim3 block(merge_threads(a.hq, a.hkv, a.d, ept));
   if (ept == 1) hipLaunchKernelGGL((merge_kernel<T, 1>), grid, block, 0, st, a);
   else if (ept == 2) hipLaunchKernelGGL((merge_kernel<T, 2>), grid, block, 0, st, a);

@@ -377,14 +377,16 @@ def test_token_major_key_layout(monkeypatch, math, dtype, hq, hkv, d, p):
     ("dpp", "f32", 8, 2, 128, 16, "64"),
     ("generic", "bf16", 6, 2, 96, 8, "64"),
     ("generic", "bf16", 16, 1, 256, 16, "64"),  # G D = 4096: four elements per thread whatever is asked
+    ("generic", "bf16", 10, 1, 256, 16, "64"),  # G D = 2560: widened to four from one, two or three
 ])
-@pytest.mark.parametrize("ept", ["1", "2", "4"])
+@pytest.mark.parametrize("ept", ["1", "2", "3", "4"])
 def test_many_partitions_merge(monkeypatch, math, dtype, hq, hkv, d, p, part, ept):
     """Sequences of up to 21,000 tokens cut into up to 330 partitions: the merge
     takes slots past the first 64 (second pass for the maximum) and past the
     first 128 (weights recomputed instead of kept in LDS), plus sequences of
     one partition and of exactly one partition boundary; with 1, 2 and 4
-    output elements per merge thread."""
+    output elements per merge thread asked for (3 is taken as 2), widened
+    where G * head_dim needs more than 1024 threads."""
     monkeypatch.setenv("PKV_DECODE_MATH", math)
     monkeypatch.setenv("PKV_PARTITION_TOKENS", part)
     monkeypatch.setenv("PKV_MERGE_ELEMS", ept)
