@@ -313,12 +313,12 @@ int pkv_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_
  * and DPP kernels also need 16-byte aligned q, out and caches (otherwise the
  * generic kernel runs).  PKV_PARTITION_TOKENS forces T (rounded down to a
  * power of two, at least one chunk per wave); PKV_DECODE_SPLIT=off makes
- * every sequence a single partition.  Tuning overrides (measurement only;
- * results stay within tolerance, not bit-identical): PKV_SPLIT_DIV (default
- * 4; T is the largest power of two <= total tokens * Hkv / (CUs * div)),
- * PKV_DECODE_WAVES=8 (matrix-core kernel: eight waves per unit instead of
- * four; T changes with it), PKV_MERGE_ELEMS = 1 | 2 | 4 (merge output
- * elements per thread; 3 counts as 2; widened where G * head_dim needs it).
+ * every sequence a single partition.  Tuning overrides for measurement:
+ * PKV_SPLIT_DIV (default 4; T is the largest power of two <= total tokens *
+ * Hkv / (CUs * div)) and PKV_DECODE_WAVES=8 (matrix-core kernel: eight waves
+ * per unit instead of four) change the summation order (results stay within
+ * tolerance); PKV_MERGE_ELEMS = 1 | 2 | 4 (merge output elements per thread;
+ * 3 counts as 2; widened where G * head_dim needs it) does not.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.  Bad table entries or
  * lengths are clamped in-bounds and flagged. */
 int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
