@@ -396,3 +396,25 @@ def test_many_partitions_merge(monkeypatch, math, dtype, hq, hkv, d, p, part, ep
     case = build_case(cfg, seed=6)
     err = check_attention(case)
     say(f"  {cfg.name} T={part} merge elements {ept}: max err {err:.3e}")
+
+
+def test_merge_width_does_not_change_bits(monkeypatch):
+    """Every merge width sums each output element's slots in the same order
+    with the same weights: outputs are bit-identical across 1, 2 and 4
+    elements per thread."""
+    import torch
+    monkeypatch.setenv("PKV_PARTITION_TOKENS", "128")
+    lengths = (3000, 1, 900, 4097, 128, 2500)
+    cfg = DecodeConfig("merge_width", len(lengths), 32, 8, 128, 16, "bf16", "fixed", fixed_lengths=lengths)
+    case = build_case(cfg, seed=8)  # appends the last token and decodes once
+    outs = []
+    for ept in ("1", "2", "4"):
+        monkeypatch.setenv("PKV_MERGE_ELEMS", ept)
+        out = torch.full_like(case.w.q, float("nan"))
+        case.kv.attend(case.meta, case.w.q, out)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    case.out = outs[0]
+    err = check_attention(case)
+    say(f"  max err {err:.3e}")
