@@ -20,42 +20,64 @@
 namespace pkv {
 namespace {
 
-// One workgroup per token (grid-stride).  Keys: each token row of every head
-// is contiguous in the cache, so threads move 16-byte chunks.  Values: the
-// token's column is strided by P elements; threads move single elements.
+// One workgroup per token (grid-stride).  With 16-byte rows (vec_ok) the
+// token's key row and value row are cut into 16-byte pieces, keys first;
+// thread i loads piece i and stores it: a key piece as one 16-byte write
+// (token rows are contiguous in the cache), a value piece as one element
+// per head_dim row (values are token-minor, P elements apart).  A piece
+// never crosses heads (head_dim is a whole number of pieces).  The first
+// piece's load is issued together with the slot's, so a token costs one
+// round trip to memory before its stores.  Otherwise threads move single
+// elements.
 template <typename E>
 __global__ __launch_bounds__(256) void cache_append_kernel(
     E* __restrict__ kc, E* __restrict__ vc, const E* __restrict__ kn, const E* __restrict__ vn,
     const int32_t* __restrict__ slots, int32_t n_tokens, int64_t num_slots, int32_t hkv,
     int32_t d, int32_t p, KStrides ks, int32_t vec_ok, int32_t* __restrict__ err) {
+  constexpr int V = 16 / sizeof(E);  // elements per 16-byte piece
   const int32_t hd = hkv * d;
+  const int32_t nvec = vec_ok ? hd / V : 0;  // pieces per row
   for (int32_t tok = blockIdx.x; tok < n_tokens; tok += gridDim.x) {
+    const E* ksrc = kn + (int64_t)tok * hd;
+    const E* vsrc = vn + (int64_t)tok * hd;
+    auto piece = [&](int32_t i) -> uint4 {
+      return i < nvec ? *reinterpret_cast<const uint4*>(ksrc + i * V)
+                      : *reinterpret_cast<const uint4*>(vsrc + (i - nvec) * V);
+    };
+    const int32_t i0 = threadIdx.x;
+    uint4 x0 = uint4{0, 0, 0, 0};
+    if (i0 < 2 * nvec) x0 = piece(i0);
     const int32_t s = slots[tok];
+    // an empty statement that takes the piece keeps its load ahead of the
+    // slot test instead of sunk below it
+    asm volatile("" ::"v"(x0.x), "v"(x0.y), "v"(x0.z), "v"(x0.w));
     if (s < 0) continue;
     if ((int64_t)s >= num_slots) {
       if (threadIdx.x == 0) atomicOr(err, PKV_DEVERR_SLOT);
       continue;
     }
     const int64_t blk = s / p, off = s % p;
-    const E* ksrc = kn + (int64_t)tok * hd;
-    const E* vsrc = vn + (int64_t)tok * hd;
     if (vec_ok) {
-      constexpr int V = 16 / sizeof(E);  // elements per 16-byte chunk
-      const int32_t nvec = hd / V;
-      for (int32_t i = threadIdx.x; i < nvec; i += blockDim.x) {
-        const int32_t e = i * V, h = e / d, dd = e % d;
-        const uint4 x = *reinterpret_cast<const uint4*>(ksrc + e);
-        *reinterpret_cast<uint4*>(kc + blk * hd * p + h * ks.head + off * ks.tok + dd) = x;
+      for (int32_t i = i0; i < 2 * nvec; i += blockDim.x) {
+        const uint4 x = i == i0 ? x0 : piece(i);
+        if (i < nvec) {
+          const int32_t e = i * V, h = e / d, dd = e % d;
+          *reinterpret_cast<uint4*>(kc + blk * hd * p + h * ks.head + off * ks.tok + dd) = x;
+        } else {
+          const int32_t e = (i - nvec) * V, h = e / d, dd = e % d;
+          E vals[V];
+          __builtin_memcpy(vals, &x, 16);
+          E* col = vc + ((blk * hkv + h) * d + dd) * p + off;
+#pragma unroll
+          for (int j = 0; j < V; ++j) col[(int64_t)j * p] = vals[j];
+        }
       }
     } else {
       for (int32_t e = threadIdx.x; e < hd; e += blockDim.x) {
         const int32_t h = e / d, dd = e % d;
         kc[blk * hd * p + h * ks.head + off * ks.tok + dd] = ksrc[e];
+        vc[((blk * hkv + h) * d + dd) * p + off] = vsrc[e];
       }
-    }
-    for (int32_t e = threadIdx.x; e < hd; e += blockDim.x) {
-      const int32_t h = e / d, dd = e % d;
-      vc[((blk * hkv + h) * d + dd) * p + off] = vsrc[e];
     }
   }
 }
