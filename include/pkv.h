@@ -314,8 +314,8 @@ int pkv_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_
  * generic kernel runs).  PKV_PARTITION_TOKENS forces T (rounded down to a
  * power of two, at least one chunk per wave); PKV_DECODE_SPLIT=off makes
  * every sequence a single partition.  Tuning overrides for measurement:
- * PKV_SPLIT_DIV (default 4; T is the largest power of two <= total tokens *
- * Hkv / (CUs * div)) and PKV_DECODE_WAVES=8 (matrix-core kernel: eight waves
+ * PKV_SPLIT_DIV (T is the largest power of two <= total tokens * Hkv /
+ * (CUs * div); default 2 when n_seqs * Hkv >= 8 * CUs, else 4) and PKV_DECODE_WAVES=8 (matrix-core kernel: eight waves
  * per unit instead of four) change the summation order (results stay within
  * tolerance); PKV_MERGE_ELEMS = 1 | 2 | 4 (merge output elements per thread;
  * 3 counts as 2; widened where G * head_dim needs it) does not.
