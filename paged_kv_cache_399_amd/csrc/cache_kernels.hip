@@ -20,15 +20,16 @@
 namespace pkv {
 namespace {
 
-// One workgroup per token (grid-stride).  With 16-byte rows (vec_ok) the
-// token's key row and value row are cut into 16-byte pieces, keys first;
-// thread i loads piece i and stores it: a key piece as one 16-byte write
-// (token rows are contiguous in the cache), a value piece as one element
-// per head_dim row (values are token-minor, P elements apart).  A piece
-// never crosses heads (head_dim is a whole number of pieces).  The first
-// piece's load is issued together with the slot's, so a token costs one
-// round trip to memory before its stores.  Otherwise threads move single
-// elements.
+// One workgroup per token (grid-stride).  Keys: each token row of every head
+// is contiguous in the cache, so threads move 16-byte pieces (vec_ok) or
+// single elements.  Values: the token's column is strided by P elements, so
+// threads move single elements, consecutive threads taking consecutive head_dim
+// rows (a store instruction covers one compact run of the value tiles),
+// kAppendBatch elements per thread per batch with the batch's loads issued
+// before its stores.  The first key piece and the first value batch do not
+// depend on the slot and are loaded before it is tested.
+constexpr int kAppendBatch = 4;
+
 template <typename E>
 __global__ __launch_bounds__(256) void cache_append_kernel(
     E* __restrict__ kc, E* __restrict__ vc, const E* __restrict__ kn, const E* __restrict__ vn,
@@ -36,47 +37,49 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
     int32_t d, int32_t p, KStrides ks, int32_t vec_ok, int32_t* __restrict__ err) {
   constexpr int V = 16 / sizeof(E);  // elements per 16-byte piece
   const int32_t hd = hkv * d;
-  const int32_t nvec = vec_ok ? hd / V : 0;  // pieces per row
+  const int32_t nvec = vec_ok ? hd / V : 0;  // key pieces per row
+  const int32_t tid = threadIdx.x, nt = blockDim.x;
   for (int32_t tok = blockIdx.x; tok < n_tokens; tok += gridDim.x) {
     const E* ksrc = kn + (int64_t)tok * hd;
     const E* vsrc = vn + (int64_t)tok * hd;
-    auto piece = [&](int32_t i) -> uint4 {
-      return i < nvec ? *reinterpret_cast<const uint4*>(ksrc + i * V)
-                      : *reinterpret_cast<const uint4*>(vsrc + (i - nvec) * V);
-    };
-    const int32_t i0 = threadIdx.x;
-    uint4 x0 = uint4{0, 0, 0, 0};
-    if (i0 < 2 * nvec) x0 = piece(i0);
+    // loads that do not depend on the slot
+    uint4 kx = uint4{0, 0, 0, 0};
+    if (tid < nvec) kx = *reinterpret_cast<const uint4*>(ksrc + tid * V);
+    uint32_t vb[kAppendBatch];
+#pragma unroll
+    for (int u = 0; u < kAppendBatch; ++u) {
+      const int32_t e = tid + u * nt;
+      vb[u] = e < hd ? (uint32_t)vsrc[e] : 0u;
+    }
     const int32_t s = slots[tok];
-    // an empty statement that takes the piece keeps its load ahead of the
-    // slot test instead of sunk below it
-    asm volatile("" ::"v"(x0.x), "v"(x0.y), "v"(x0.z), "v"(x0.w));
     if (s < 0) continue;
     if ((int64_t)s >= num_slots) {
-      if (threadIdx.x == 0) atomicOr(err, PKV_DEVERR_SLOT);
+      if (tid == 0) atomicOr(err, PKV_DEVERR_SLOT);
       continue;
     }
     const int64_t blk = s / p, off = s % p;
+    E* krow = kc + blk * hd * p + off * ks.tok;  // + h * ks.head + dd
     if (vec_ok) {
-      for (int32_t i = i0; i < 2 * nvec; i += blockDim.x) {
-        const uint4 x = i == i0 ? x0 : piece(i);
-        if (i < nvec) {
-          const int32_t e = i * V, h = e / d, dd = e % d;
-          *reinterpret_cast<uint4*>(kc + blk * hd * p + h * ks.head + off * ks.tok + dd) = x;
-        } else {
-          const int32_t e = (i - nvec) * V, h = e / d, dd = e % d;
-          E vals[V];
-          __builtin_memcpy(vals, &x, 16);
-          E* col = vc + ((blk * hkv + h) * d + dd) * p + off;
-#pragma unroll
-          for (int j = 0; j < V; ++j) col[(int64_t)j * p] = vals[j];
-        }
+      for (int32_t i = tid; i < nvec; i += nt) {
+        const uint4 x = i == tid ? kx : *reinterpret_cast<const uint4*>(ksrc + i * V);
+        const int32_t e = i * V, h = e / d, dd = e % d;
+        *reinterpret_cast<uint4*>(krow + h * ks.head + dd) = x;
       }
     } else {
-      for (int32_t e = threadIdx.x; e < hd; e += blockDim.x) {
-        const int32_t h = e / d, dd = e % d;
-        kc[blk * hd * p + h * ks.head + off * ks.tok + dd] = ksrc[e];
-        vc[((blk * hkv + h) * d + dd) * p + off] = vsrc[e];
+      for (int32_t e = tid; e < hd; e += nt) krow[(e / d) * ks.head + e % d] = ksrc[e];
+    }
+    E* vtile = vc + blk * hkv * d * p + off;  // + ((h d) + dd) p = e p
+    for (int32_t e0 = tid; e0 < hd; e0 += kAppendBatch * nt) {
+      uint32_t w[kAppendBatch];
+#pragma unroll
+      for (int u = 0; u < kAppendBatch; ++u) {
+        const int32_t e = e0 + u * nt;
+        w[u] = e0 == tid ? vb[u] : (e < hd ? (uint32_t)vsrc[e] : 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < kAppendBatch; ++u) {
+        const int32_t e = e0 + u * nt;
+        if (e < hd) vtile[(int64_t)e * p] = (E)w[u];
       }
     }
   }
