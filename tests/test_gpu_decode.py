@@ -418,3 +418,17 @@ def test_merge_width_does_not_change_bits(monkeypatch):
     case.out = outs[0]
     err = check_attention(case)
     say(f"  max err {err:.3e}")
+
+
+@pytest.mark.parametrize("batch", [63, 65, 127, 129, 200, 255, 257, 300])
+def test_plan_sizes_across_batch_sizes(monkeypatch, batch):
+    """The plan runs in a workgroup of 64, 128, 256 or 1024 threads chosen by
+    batch size: batches on both sides of each boundary, with partitions split
+    (T = 128) so that full, ragged and merged units all occur."""
+    monkeypatch.setenv("PKV_PARTITION_TOKENS", "128")
+    rng = np.random.default_rng(batch)
+    lengths = tuple(int(x) for x in rng.integers(1, 400, size=batch))
+    cfg = DecodeConfig(f"plan_b{batch}", batch, 8, 2, 64, 16, "bf16", "fixed", fixed_lengths=lengths)
+    case = build_case(cfg, seed=batch)
+    err = check_attention(case)
+    say(f"  B={batch}: max err {err:.3e}")

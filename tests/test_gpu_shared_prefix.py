@@ -265,6 +265,18 @@ def test_more_sequences_than_one_plan_pass(monkeypatch):
     kv.close()
 
 
+@pytest.mark.parametrize("groups_n", [22, 67, 90])
+def test_packs_across_plan_sizes(monkeypatch, groups_n):
+    """Fork groups of three in batches of 66, 201 and 270 sequences: packs and
+    runs under the 128-, 256- and 1024-thread plans."""
+    monkeypatch.setenv("PKV_PARTITION_TOKENS", "128")
+    groups = [(90 + (i % 5) * 37, [i % 4, 3, 30]) for i in range(groups_n)]
+    kv, batch, keys, vals = _forest(groups, 2, 64, 16, seed=30 + groups_n)
+    worst, most = _step_and_check(kv, batch, keys, vals, 8, seed=30 + groups_n, steps=1, t=128)
+    say(f"  {len(batch)} sequences: max shared {most}, max err {worst:.3e}")
+    kv.close()
+
+
 def test_graph_replay_with_packs(monkeypatch):
     """A captured decode (plan with packs, partition, merge) replays bit for bit
     like the eager decode on the same state, while decode steps in between
