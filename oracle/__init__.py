@@ -34,6 +34,13 @@ routines.  Pins per function:
                           invariants under random operation sequences.
 * layout.*                round trip through the printed block table,
                           disjointness brute force.
+* layout.copy_block       the copy-on-write contract on the pool model's
+                          pairs (prefix of 3 in pages of 2, three sharers:
+                          every sharer reads back its own tokens, blocks
+                          nobody holds keep their fill), which planted
+                          mistakes (swapped source and destination, keys or
+                          values only, one head only) break; element-wise
+                          brute force over a whole cache.
 * attention.decode        brute force, torch scaled_dot_product_attention in
                           float64, closed-form two-token case, L=1 and
                           equal-key special cases, GQA == repeated MHA.
