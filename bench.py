@@ -24,13 +24,15 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+DEFAULT_STEPS = 50    # timed steps
+DEFAULT_WARMUP = 10   # untimed warm-up steps
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=DEFAULT_STEPS)
+    ap.add_argument("--warmup", type=int, default=DEFAULT_WARMUP)
     ap.add_argument("--config", default="long", help="tiny|small_mha|gqa|long|prefix|beam|prefill|prefill_chunk|admission|admission_small")
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--layout", default="head_major", choices=["head_major", "token_major"],

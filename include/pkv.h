@@ -38,9 +38,16 @@
  *   i.e. each block stores its keys as head_dim-contiguous rows and its values
  *   transposed (token-minor), so that the value product of decode attention
  *   reads contiguous runs of tokens of one head; the values keep that order in
- *   both layouts.  A block is one contiguous run of num_kv_heads * block_size
- *   * head_dim elements in each cache either way.  Slot s = block
- *   (s / block_size), offset (s % block_size).
+ *   both layouts.  The transposed value tile departs from the plainest
+ *   reading of a paged cache ([num_blocks, num_kv_heads, block_size,
+ *   head_dim] for values as for keys): the matrix-core value product contracts
+ *   over tokens and takes eight consecutive tokens of one head_dim element per
+ *   lane, which this order turns into one 16-byte load straight from HBM.  Its
+ *   cost: appending one token to a block stores each of its head_dim value
+ *   elements into a different row of the tile.
+ *   A block is one contiguous run of num_kv_heads * block_size * head_dim
+ *   elements in each cache either way.  Slot s = block (s / block_size),
+ *   offset (s % block_size).
  *   q, out:          [n_seqs, num_q_heads, head_dim]
  *   k_new, v_new:    [n_tokens, num_kv_heads, head_dim]
  *   block table:     int32 [n_seqs, max_blocks_per_seq], unused entries -1
@@ -94,7 +101,10 @@ typedef struct {
 
 /* ---- host block pool --------------------------------------------------- */
 
-/* Create a pool of `num_blocks` blocks of `block_size` token slots.
+/* Create a pool of `num_blocks` blocks of `block_size` token slots: the KV
+ * cache cut into equal fixed-size blocks, any of which may hold any
+ * sequence's tokens ("PagedAttention Internals", "Fixed-Size KV Blocks";
+ * "pagedattention" topic page, third paragraph).
  * `free_order` (host, num_blocks entries, may be NULL = 0..num_blocks-1) is
  * the initial free list, a permutation of the block ids; allocation takes its
  * head, release appends to its tail.  *out receives the handle.
@@ -133,8 +143,12 @@ int pkv_seq_append_slots(pkv_pool* pool, const int64_t* seqs, const int32_t* n_n
  * with the parent's length (topic page, fourth paragraph). */
 int pkv_seq_fork(pkv_pool* pool, int64_t parent, int64_t* child_out);
 
-/* Release a sequence: drop one reference to each block in logical order;
- * blocks reaching zero go to the free-list tail in that order. */
+/* Release a sequence: a finished request gives its blocks back ("PagedAttention
+ * Internals", "Sharing And Dynamic Growth"; a block shared with a fork stays
+ * held by the others, "pagedattention" topic page, fourth paragraph).  Drops
+ * one reference to each block in logical order; blocks reaching zero go to the
+ * free-list tail in that order.  Errors: BAD_SEQ (unknown or released id; the
+ * id stays unusable). */
 int pkv_seq_free(pkv_pool* pool, int64_t seq);
 
 /* Place an empty sequence on explicit free blocks `phys` (host int32[n_blocks],
@@ -220,8 +234,13 @@ int pkv_block_table_upload(pkv_pool* pool, const int64_t* seqs, int32_t n_seqs,
 
 /* ---- device kernels ---------------------------------------------------- */
 
-/* Copy-on-write block copies: for each pair, every slot of block src (K and V,
- * all heads) is copied to block dst.  `pairs` is HOST memory, int32[2*n_pairs]
+/* Copy-on-write block copies: a sharer about to write into a block that
+ * others still hold gets a private copy first ("pagedattention" topic page,
+ * fourth paragraph and the comparison table's sharing row: shared blocks are
+ * copied only where the sharers diverge; "PagedAttention Internals",
+ * "Sharing And Dynamic Growth").  For each pair, every slot of block src (K
+ * and V, all heads) is copied to block dst; both caches in the layout above
+ * (any key layout: a block is one contiguous run either way).  `pairs` is HOST memory, int32[2*n_pairs]
  * as returned by pkv_seq_append_slots; the pairs travel in kernel arguments,
  * so no host-to-device copy is needed.  Enqueue before the cache_append that
  * writes into the new blocks.  Pairs outside [0, num_blocks) are skipped and
@@ -284,12 +303,19 @@ int pkv_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_
  *                    that sequence read its predecessor's tokens (in bounds).
  *                    PKV_DECODE_SHARE=off ignores the array.
  *   max_context_len  >= every L (host knowledge, used for sizing)
- *   total_context_tokens  sum of L, or -1 if unknown (sizing only)
+ *   total_context_tokens  >= sum of L, or -1 if unknown (a bound from
+ *                    n_seqs * max_context_len is used then).  It sizes the
+ *                    work list: an underestimate that leaves the list too
+ *                    small makes the plan run nothing, so no output is written
+ *                    and PKV_DEVERR_WORK_OVERFLOW is set (the call itself
+ *                    returns PKV_OK; pkv_check_device_errors reports it).
  *   unshared_context_tokens  sum of L minus the shared counts (as
  *                    pkv_seq_shared_prefix gives it), or -1 if unknown
  *                    (sizing only).  A value equal to total_context_tokens
  *                    (nothing shared) sizes the workspace without room for
  *                    packs, and the call then ignores d_shared_prev.
+ *   scale            0 selects 1 / sqrt(head_dim) (rounded to fp32); otherwise
+ *                    finite and positive
  *   workspace        device, >= pkv_decode_workspace_bytes(...) bytes,
  *                    caller-owned scratch for one call at a time: calls that
  *                    share a workspace must be ordered (same stream)
@@ -346,7 +372,11 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
  *   out, q            device [total new tokens, Hq, D], bf16
  *   d_query_start     device int32[n_seqs + 1], nondecreasing, starting at 0
  *   d_context_lens    device int32[n_seqs], n_b <= L_b <= max_blocks_per_seq * P
- *   max_query_len     >= every n_b (host knowledge, sizes the grid)
+ *   max_query_len     >= every n_b (host knowledge, sizes the grid); a
+ *                     sequence with more new tokens has its rows past
+ *                     max_query_len left unwritten and flags
+ *                     PKV_DEVERR_CONTEXT_LEN
+ *   scale             as in pkv_paged_attention_decode (0 = 1 / sqrt(head_dim))
  * Both products run on matrix cores; key/value chunks of 64 tokens are staged
  * once per workgroup in LDS and shared by a tile of queries.  Supported: bf16,
  * head_dim 64 / 128, block_size a power of two from 8 to 256, G in {1, 2, 4, 8, 16},

@@ -14,7 +14,6 @@ follows the table to its keys and values.
 from __future__ import annotations
 
 import ctypes as C
-import math
 from typing import Optional, Sequence, Tuple
 
 import numpy as np
@@ -305,7 +304,7 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens,
     if shared_prev is not None and (shared_prev.dtype != torch.int32 or shared_prev.numel() != b):
         raise ValueError("shared_prev must be int32 [n_seqs]")
     if scale is None:
-        scale = 1.0 / math.sqrt(d)
+        scale = 0.0   # the library's default, 1 / sqrt(head_dim)
     dt = _dtype_code(q)
     need = decode_workspace_bytes(b, hq, hkv, d, bs, max_context_len, total_context_tokens,
                                   q.dtype, unshared_context_tokens)
@@ -346,7 +345,7 @@ def paged_attention_prefill(out, q, k_cache, v_cache, block_table, context_lens,
             query_start.numel() != b + 1:
         raise ValueError("context_lens int32 [n_seqs], query_start int32 [n_seqs + 1]")
     if scale is None:
-        scale = 1.0 / math.sqrt(d)
+        scale = 0.0   # the library's default, 1 / sqrt(head_dim)
     _check(lib.pkv_paged_attention_prefill(
         _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(block_table, "block_table"), _dev(context_lens, "context_lens"),

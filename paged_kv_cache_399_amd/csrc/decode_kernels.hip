@@ -1696,8 +1696,8 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   if (num_q_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "more than 65535 query heads");
   if (!pkv::dtype_valid(dtype)) return fail(PKV_ERR_INVALID_ARG, "bad dtype");
   if (!pkv::layout_valid(k_layout)) return fail(PKV_ERR_INVALID_ARG, "bad key layout");
-  if (!std::isfinite(scale) || !(scale > 0.f))
-    return fail(PKV_ERR_INVALID_ARG, "scale must be finite and positive");
+  if (!pkv::resolve_scale(&scale, head_dim))
+    return fail(PKV_ERR_INVALID_ARG, "scale must be 0 (1/sqrt(head_dim)) or finite and positive");
   if (n_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !d_context_lens || (max_blocks_per_seq > 0 && !d_block_table))
     return fail(PKV_ERR_INVALID_ARG, "NULL pointer");

@@ -22,6 +22,13 @@ inline size_t dtype_size(pkv_dtype dt) { return dt == PKV_F32 ? 4 : 2; }
 
 inline bool dtype_valid(int dt) { return dt == PKV_F32 || dt == PKV_BF16; }
 
+// Attention scale: 0 selects the usual 1 / sqrt(head_dim), rounded to fp32;
+// anything else must be finite and positive.  Returns false if refused.
+inline bool resolve_scale(float* scale, int32_t head_dim) {
+  if (*scale == 0.f && head_dim > 0) *scale = (float)(1.0 / __builtin_sqrt((double)head_dim));
+  return __builtin_isfinite(*scale) && *scale > 0.f;
+}
+
 inline bool layout_valid(int l) { return l == PKV_LAYOUT_HEAD_MAJOR || l == PKV_LAYOUT_TOKEN_MAJOR; }
 
 // Element strides of the key cache inside a block: between KV heads and

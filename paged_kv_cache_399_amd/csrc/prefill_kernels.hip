@@ -151,6 +151,10 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   const int32_t q0 = a.qstart[b];
   const int32_t n = a.qstart[b + 1] - q0;
   if (n <= 0 || tile * BT >= n) return;  // uniform over the workgroup
+  // more new tokens than the grid's tiles cover (max_query_len too small):
+  // the rows past the last tile stay unwritten, so flag it
+  if (tile == a.n_tiles - 1 && hpart == 0 && threadIdx.x == 0 && (int64_t)a.n_tiles * BT < n)
+    atomicOr(a.err, PKV_DEVERR_CONTEXT_LEN);
   const int32_t P = a.p, lp = a.lp;  // block size, a power of two
   const int32_t L = a.ctx[b];
   if (L < n || (int64_t)L > (int64_t)a.max_blocks * P) {
@@ -461,8 +465,8 @@ extern "C" int pkv_paged_attention_prefill(void* out, const void* q, const void*
   if (num_q_heads % num_kv_heads) return fail(PKV_ERR_INVALID_ARG, "num_q_heads is not a multiple of num_kv_heads");
   if (!pkv::dtype_valid(dtype)) return fail(PKV_ERR_INVALID_ARG, "bad dtype");
   if (!pkv::layout_valid(k_layout)) return fail(PKV_ERR_INVALID_ARG, "bad key layout");
-  if (!std::isfinite(scale) || !(scale > 0.f))
-    return fail(PKV_ERR_INVALID_ARG, "scale must be finite and positive");
+  if (!pkv::resolve_scale(&scale, head_dim))
+    return fail(PKV_ERR_INVALID_ARG, "scale must be 0 (1/sqrt(head_dim)) or finite and positive");
   const int32_t G = num_q_heads / num_kv_heads;
   const bool pow2 = block_size >= 8 && block_size <= 256 && (block_size & (block_size - 1)) == 0;
   if (dtype != PKV_BF16 || (head_dim != 64 && head_dim != 128) || !pow2 ||

@@ -157,8 +157,10 @@ def test_prefill_argument_validation_without_device():
     assert call(d=96) == L.ERR_UNSUPPORTED
     assert call(dtype=L.F32) == L.ERR_UNSUPPORTED
     assert call(hq=30, hkv=8) == L.ERR_INVALID_ARG  # Hq % Hkv != 0
-    assert call(scale=0.0) == L.ERR_INVALID_ARG
+    assert call(scale=-0.5) == L.ERR_INVALID_ARG
     assert call(scale=float("nan")) == L.ERR_INVALID_ARG
+    assert call(scale=float("inf")) == L.ERR_INVALID_ARG
+    assert call(scale=0.0, n_seqs=0) == L.OK        # 0 selects 1 / sqrt(head_dim)
     assert call(layout=5) == L.ERR_INVALID_ARG
     assert call(n_seqs=-1) == L.ERR_INVALID_ARG
     # nothing to do: no launch, no device call

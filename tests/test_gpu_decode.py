@@ -432,3 +432,56 @@ def test_plan_sizes_across_batch_sizes(monkeypatch, batch):
     case = build_case(cfg, seed=batch)
     err = check_attention(case)
     say(f"  B={batch}: max err {err:.3e}")
+
+
+def test_default_scale_is_one_over_sqrt_head_dim():
+    """scale = 0 (the binding's default) selects 1/sqrt(head_dim) inside the
+    library: bit-identical to passing that value explicitly."""
+    import math
+    import torch
+    import paged_kv_cache_399_amd as pkv
+    case = build_case(dataclasses.replace(CONFIGS["gqa"], batch=6, length_hi=900), seed=4)
+    m, kv, w = case.meta, case.kv, case.w
+    d = case.cfg.head_dim
+    outs = []
+    for scale in (None, 1.0 / math.sqrt(d)):
+        o = torch.full_like(w.q, float("nan"))
+        pkv.paged_attention_decode(o, w.q, kv.k_cache, kv.v_cache, m.table, m.lens, m.ws_max_len,
+                                   m.ws_total, scale, m.workspace, shared_prev=m.shared,
+                                   unshared_context_tokens=m.ws_unshared)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], case.out)
+
+
+def test_underestimated_total_flags_work_overflow_and_writes_nothing():
+    """A total_context_tokens below the real sum sizes the work list too small:
+    the plan runs nothing, every output stays as it was, and the device error
+    word says PKV_DEVERR_WORK_OVERFLOW (0x10)."""
+    import torch
+    import paged_kv_cache_399_amd as pkv
+    from paged_kv_cache_399_amd.session import PagedKVCache
+    b, hq, hkv, d, p, L = 4, 32, 8, 128, 16, 1000
+    kv = PagedKVCache(b * (L // p + 1) + 4, p, hkv, d, torch.bfloat16, "cuda", fill=0.5)
+    seqs = kv.new_sequences(b)
+    slots, _ = kv.pool.append_slots(seqs, [L] * b)
+    g = torch.Generator(device="cuda").manual_seed(2)
+    k = torch.randn((b * L, hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    kv.write_slots(torch.from_numpy(slots).cuda(), k, k)
+    m = kv.prepare(seqs, -(-L // p), hq, L, b * L)
+    kv.upload(m)
+    q = torch.randn((b, hq, d), generator=g, device="cuda").to(torch.bfloat16)
+    # claimed total 1 token, nothing shared: room for one unit per sequence
+    need = pkv.decode_workspace_bytes(b, hq, hkv, d, p, L, 1, torch.bfloat16, 1)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = torch.full_like(q, float("nan"))
+    pkv.paged_attention_decode(out, q, kv.k_cache, kv.v_cache, m.table, m.lens, L, 1, None, ws,
+                               unshared_context_tokens=1)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.check_device_errors()
+    assert "0x10" in str(e.value)
+    assert torch.isnan(out.float()).all()
+    # the same call sized with the true total runs normally
+    kv.attend(m, q, out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()

@@ -130,7 +130,7 @@ def test_error_paths():
         assert pool.export()[0].tolist() == before[0].tolist()
 
 
-@pytest.mark.parametrize("name", ["tiny", "small_mha", "gqa"])
+@pytest.mark.parametrize("name", ["tiny", "small_mha", "gqa", "long"])
 def test_config_prefill_and_decode_step_match_model(name):
     cfg = CONFIGS[name]
     lens = context_lengths(cfg, 0)
