@@ -359,6 +359,34 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
                                pkv_layout k_layout, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/* Decode without any device allocation, for callers that cannot allocate
+ * (code under graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): pkv_paged_attention_decode with every argument the same
+ * except that the workspace is the library's own scratch, a static device
+ * array of PKV_DECODE_SCRATCH_BYTES bytes per device (held until the process
+ * ends).  The call allocates nothing.
+ *   Limit: a batch whose pkv_decode_workspace_bytes(...) exceeds
+ *          PKV_DECODE_SCRATCH_BYTES is refused with PKV_ERR_WORKSPACE.
+ *   Sharing: every call on one device uses that device's one scratch; calls
+ *          that may overlap on a device (several streams, several threads)
+ *          race and must be serialised by the caller.  Nothing in the scratch
+ *          needs to start at zero: each call writes what it reads.
+ *   The first call on a device looks up the scratch's device address (a
+ *   runtime symbol query, no allocation).
+ * Errors: as pkv_paged_attention_decode, WORKSPACE as above, HIP if the
+ * scratch address cannot be found. */
+#define PKV_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* d_block_table,
+                                       const int32_t* d_context_lens,
+                                       const int32_t* d_shared_prev, int32_t n_seqs,
+                                       int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                       int32_t max_blocks_per_seq, int32_t max_context_len,
+                                       int64_t total_context_tokens,
+                                       int64_t unshared_context_tokens, float scale,
+                                       pkv_dtype dtype, pkv_layout k_layout, void* stream);
+
 /* Paged prefill attention: causal attention of the newest tokens of each
  * sequence over everything it holds ("Fixed-Size KV Blocks": a prompt's
  * blocks are handed out as its tokens arrive; "The Block Table Map": the

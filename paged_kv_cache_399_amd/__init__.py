@@ -25,8 +25,8 @@ from ._lib import (DEVERR_CONTEXT_LEN, DEVERR_COPY_PAIR, DEVERR_SLOT,  # noqa: F
 lib = _lib.load()
 
 __all__ = ["PkvError", "BlockPool", "cache_append", "copy_blocks", "decode_workspace_bytes",
-           "paged_attention_decode", "paged_attention_prefill", "check_device_errors", "version",
-           "lib"]
+           "paged_attention_decode", "paged_attention_decode_noalloc", "paged_attention_prefill",
+           "check_device_errors", "version", "lib", "DECODE_SCRATCH_BYTES"]
 
 
 class PkvError(RuntimeError):
@@ -278,18 +278,8 @@ def decode_workspace_bytes(n_seqs: int, num_q_heads: int, num_kv_heads: int, hea
     return out.value
 
 
-def paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens,
-                           max_context_len: int, total_context_tokens: int = -1,
-                           scale: Optional[float] = None, workspace=None, stream=None,
-                           layout="head_major", shared_prev=None,
-                           unshared_context_tokens: int = -1):
-    """Decode attention over the paged cache; writes ``out`` [B, Hq, D] and returns it.
-
-    ``workspace`` is a uint8 device tensor of at least decode_workspace_bytes(...)
-    bytes; if None one is allocated with torch (plumbing only).  ``shared_prev``
-    (device int32 [B], as block_table_upload writes it) lets sequences that
-    share blocks read them once per pack; the output is the same.
-    """
+def _decode_common(out, q, k_cache, v_cache, block_table, context_lens, shared_prev, layout):
+    """Checks shared by both decode calls; returns (b, hq, hkv, d, bs, nb, layout code)."""
     import torch
     nb, hkv, bs, d, lay = _cache_shape(k_cache, v_cache, layout)
     b, hq, d2 = q.shape
@@ -303,9 +293,25 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens,
         raise ValueError("context_lens must be int32 [n_seqs]")
     if shared_prev is not None and (shared_prev.dtype != torch.int32 or shared_prev.numel() != b):
         raise ValueError("shared_prev must be int32 [n_seqs]")
-    if scale is None:
-        scale = 0.0   # the library's default, 1 / sqrt(head_dim)
-    dt = _dtype_code(q)
+    return b, hq, hkv, d, bs, nb, lay
+
+
+def paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens,
+                           max_context_len: int, total_context_tokens: int = -1,
+                           scale: Optional[float] = None, workspace=None, stream=None,
+                           layout="head_major", shared_prev=None,
+                           unshared_context_tokens: int = -1):
+    """Decode attention over the paged cache; writes ``out`` [B, Hq, D] and returns it.
+
+    ``workspace`` is a uint8 device tensor of at least decode_workspace_bytes(...)
+    bytes; if None one is allocated with torch (plumbing only).  ``shared_prev``
+    (device int32 [B], as block_table_upload writes it) lets sequences that
+    share blocks read them once per pack; the output is the same.
+    ``scale`` None means 1 / sqrt(head_dim), chosen by the library.
+    """
+    import torch
+    b, hq, hkv, d, bs, nb, lay = _decode_common(out, q, k_cache, v_cache, block_table,
+                                                context_lens, shared_prev, layout)
     need = decode_workspace_bytes(b, hq, hkv, d, bs, max_context_len, total_context_tokens,
                                   q.dtype, unshared_context_tokens)
     if workspace is None:
@@ -317,8 +323,32 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens,
         _dev(block_table, "block_table"), _dev(context_lens, "context_lens"),
         None if shared_prev is None else _dev(shared_prev, "shared_prev"), b, hq, hkv, d, bs,
         nb, block_table.shape[1], int(max_context_len), int(total_context_tokens),
-        int(unshared_context_tokens), float(scale),
-        dt, lay, _dev(workspace, "workspace"), workspace.numel(), _stream_ptr(stream)))
+        int(unshared_context_tokens), 0.0 if scale is None else float(scale),
+        _dtype_code(q), lay, _dev(workspace, "workspace"), workspace.numel(),
+        _stream_ptr(stream)))
+    return out
+
+
+DECODE_SCRATCH_BYTES = _lib.DECODE_SCRATCH_BYTES
+
+
+def paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_table, context_lens,
+                                   max_context_len: int, total_context_tokens: int = -1,
+                                   scale: Optional[float] = None, stream=None,
+                                   layout="head_major", shared_prev=None,
+                                   unshared_context_tokens: int = -1):
+    """paged_attention_decode on the library's static scratch: no device allocation
+    anywhere in the call.  Batches needing more than DECODE_SCRATCH_BYTES of
+    workspace are refused; calls that may overlap on one device race."""
+    b, hq, hkv, d, bs, nb, lay = _decode_common(out, q, k_cache, v_cache, block_table,
+                                                context_lens, shared_prev, layout)
+    _check(lib.pkv_paged_attention_decode_noalloc(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_table, "block_table"), _dev(context_lens, "context_lens"),
+        None if shared_prev is None else _dev(shared_prev, "shared_prev"), b, hq, hkv, d, bs,
+        nb, block_table.shape[1], int(max_context_len), int(total_context_tokens),
+        int(unshared_context_tokens), 0.0 if scale is None else float(scale),
+        _dtype_code(q), lay, _stream_ptr(stream)))
     return out
 
 
@@ -344,13 +374,12 @@ def paged_attention_prefill(out, q, k_cache, v_cache, block_table, context_lens,
     if context_lens.dtype != torch.int32 or query_start.dtype != torch.int32 or \
             query_start.numel() != b + 1:
         raise ValueError("context_lens int32 [n_seqs], query_start int32 [n_seqs + 1]")
-    if scale is None:
-        scale = 0.0   # the library's default, 1 / sqrt(head_dim)
     _check(lib.pkv_paged_attention_prefill(
         _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(block_table, "block_table"), _dev(context_lens, "context_lens"),
         _dev(query_start, "query_start"), b, hq, hkv, d, bs, nb, block_table.shape[1],
-        int(max_query_len), float(scale), _dtype_code(q), lay, _stream_ptr(stream)))
+        int(max_query_len), 0.0 if scale is None else float(scale), _dtype_code(q), lay,
+        _stream_ptr(stream)))
     return out
 
 

@@ -27,6 +27,7 @@ F32 = 0
 BF16 = 1
 
 UPLOAD_INCREMENTAL = 1
+DECODE_SCRATCH_BYTES = 32 << 20   # PKV_DECODE_SCRATCH_BYTES
 LAYOUT_HEAD_MAJOR = 0
 LAYOUT_TOKEN_MAJOR = 1
 
@@ -63,6 +64,9 @@ SIGNATURES = {
     "pkv_paged_attention_decode": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                              _i32, _i32, _i32, _i32, _i64, _i64, C.c_float, C.c_int,
                                              C.c_int, _vp, C.c_size_t, _vp]),
+    "pkv_paged_attention_decode_noalloc": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                                     _i32, _i32, _i32, _i32, _i32, _i32, _i64,
+                                                     _i64, C.c_float, C.c_int, C.c_int, _vp]),
     "pkv_paged_attention_prefill": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                               _i32, _i32, _i32, _i32, _i32, C.c_float, C.c_int,
                                               C.c_int, _vp]),

@@ -52,6 +52,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -1677,18 +1678,48 @@ extern "C" int pkv_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, i
   PKV_TRY_END
 }
 
-extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
-                                          const void* v_cache, const int32_t* d_block_table,
-                                          const int32_t* d_context_lens,
-                                          const int32_t* d_shared_prev, int32_t n_seqs,
-                                          int32_t num_q_heads, int32_t num_kv_heads,
-                                          int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                                          int32_t max_blocks_per_seq, int32_t max_context_len,
-                                          int64_t total_context_tokens,
-                                          int64_t unshared_context_tokens, float scale,
-                                          pkv_dtype dtype, pkv_layout k_layout, void* workspace,
-                                          size_t workspace_bytes, void* stream) {
-  PKV_TRY_BEGIN
+// ---------------------------------------------------------------------------
+// Library-owned scratch for pkv_paged_attention_decode_noalloc, for callers
+// that cannot allocate device memory.  One copy per device (each device's
+// code object holds its own), held until the process ends.  Host code never
+// uses the array's name as an address: the device address is looked up once
+// per device with hipGetSymbolAddress and kept in scratch_ptr.
+// ---------------------------------------------------------------------------
+namespace pkv {
+namespace {
+constexpr size_t kScratchBytes = PKV_DECODE_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+void* scratch_ptr[kMaxScratchDevices] = {};
+std::mutex scratch_mu;
+
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices) return fail(PKV_ERR_UNSUPPORTED, "device id %d", dev);
+  std::lock_guard<std::mutex> lk(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(PKV_ERR_HIP, "hipGetSymbolAddress(decode scratch): %s", hipGetErrorString(e));
+    scratch_ptr[dev] = ptr;
+  }
+  *out = scratch_ptr[dev];
+  return PKV_OK;
+}
+
+// The decode call proper.  With use_scratch the workspace arguments are
+// ignored and the current device's library scratch is used instead.
+int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* d_block_table, const int32_t* d_context_lens,
+                const int32_t* d_shared_prev, int32_t n_seqs, int32_t num_q_heads,
+                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                int32_t max_blocks_per_seq, int32_t max_context_len, int64_t total_context_tokens,
+                int64_t unshared_context_tokens, float scale, pkv_dtype dtype, pkv_layout k_layout,
+                void* workspace, size_t workspace_bytes, bool use_scratch, void* stream) {
   if (n_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
       num_blocks <= 0 || max_blocks_per_seq < 0 || max_context_len < 0)
     return fail(PKV_ERR_INVALID_ARG, "bad sizes");
@@ -1720,8 +1751,17 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   if ((int64_t)c.max_units * num_kv_heads > (int64_t)INT32_MAX)
     return fail(PKV_ERR_UNSUPPORTED, "too many partitions");
   const pkv::Layout lay = pkv::layout_of(n_seqs, num_q_heads, head_dim, c);
-  if (!workspace || workspace_bytes < lay.total)
+  if (use_scratch) {
+    if (lay.total > kScratchBytes)
+      return fail(PKV_ERR_WORKSPACE,
+                  "this batch needs %zu bytes of decode workspace; the library scratch holds %zu "
+                  "(pass a workspace to pkv_paged_attention_decode instead)", lay.total, kScratchBytes);
+    int src = scratch_address(&workspace);
+    if (src) return src;
+    workspace_bytes = kScratchBytes;
+  } else if (!workspace || workspace_bytes < lay.total) {
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, lay.total);
+  }
   int32_t* err = nullptr;
   rc = pkv::device_error_word(&err);
   if (rc) return rc;
@@ -1790,5 +1830,42 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return PKV_OK;
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
+                                          const void* v_cache, const int32_t* d_block_table,
+                                          const int32_t* d_context_lens,
+                                          const int32_t* d_shared_prev, int32_t n_seqs,
+                                          int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                          int32_t max_blocks_per_seq, int32_t max_context_len,
+                                          int64_t total_context_tokens,
+                                          int64_t unshared_context_tokens, float scale,
+                                          pkv_dtype dtype, pkv_layout k_layout, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  PKV_TRY_BEGIN
+  return pkv::decode_impl(out, q, k_cache, v_cache, d_block_table, d_context_lens, d_shared_prev,
+                          n_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                          max_blocks_per_seq, max_context_len, total_context_tokens,
+                          unshared_context_tokens, scale, dtype, k_layout, workspace,
+                          workspace_bytes, false, stream);
+  PKV_TRY_END
+}
+
+extern "C" int pkv_paged_attention_decode_noalloc(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* d_block_table, const int32_t* d_context_lens, const int32_t* d_shared_prev,
+    int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+    int64_t total_context_tokens, int64_t unshared_context_tokens, float scale, pkv_dtype dtype,
+    pkv_layout k_layout, void* stream) {
+  PKV_TRY_BEGIN
+  return pkv::decode_impl(out, q, k_cache, v_cache, d_block_table, d_context_lens, d_shared_prev,
+                          n_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                          max_blocks_per_seq, max_context_len, total_context_tokens,
+                          unshared_context_tokens, scale, dtype, k_layout, nullptr, 0, true, stream);
   PKV_TRY_END
 }
