@@ -174,7 +174,9 @@ def run_beam(args):
                    "parallelism": "single GPU"},
         "decode_tokens_per_s": round(b / (ms_step * 1e-3), 1),
         "decode_ms": round(dec_ms, 4),
-        "decode_bytes_per_step": int(dbytes), "decode_unique_bytes": int(ubytes),
+        "decode_bytes_per_step": int(dbytes),
+        "decode_calls": len(per_call),
+        "decode_bytes_mean_per_call": int(round(float(np.mean(per_call)))), "decode_unique_bytes": int(ubytes),
         "unique_GB_per_s": round(ubytes / (dec_ms * 1e-3) / 1e9, 1),
         "fragmentation": round(st["fragmentation"], 6),
         "copy_on_write": {"pairs": int(len(cow)), "first_step_ms": round(first_copy_ms, 4),
@@ -498,6 +500,11 @@ def run_decode(args, cfg, cpu):
     dec_gbs = dbytes / (dec_ms * 1e-3) / 1e9
     final = base + args.warmup + args.steps
     table_bytes = 4 * int(np.sum(-(-final // p)))
+    # every decode this process ran: the steps at their growing lengths, then
+    # the back-to-back, cold-cache and graph-replay loops (1 + steps replays)
+    # at the final ones; per-dispatch hardware counters average over these
+    per_call = [decode_bytes(base + i + 1, hq, hkv, d, p, s) for i in range(nsteps)]
+    per_call += [dbytes] * (3 * args.steps + 1)
     extra = {}
     if cfg.prefix_len:
         # the shared prefix lives in HBM once: K/V bytes with the prefix counted once
@@ -536,6 +543,8 @@ def run_decode(args, cfg, cpu):
         "GB_per_s_cold": round(dbytes / (cold_ms * 1e-3) / 1e9, 1),
         "gpu_ms_per_step": round(gpu_ms_step, 4),
         "decode_bytes_per_step": int(dbytes),
+        "decode_calls": len(per_call),
+        "decode_bytes_mean_per_call": int(round(float(np.mean(per_call)))),
         "block_table_bytes_read": table_bytes,
         "append_host_ms_per_step": round(host_s[0] * 1e3 / args.steps, 4),
         **extra,
