@@ -116,7 +116,17 @@ __device__ __forceinline__ int kswz(int k) {
 // the row's low four bits are used, so a lane's rows share one swizzle.
 __device__ __forceinline__ int vswz(int d) { return (d & 7) ^ (((d >> 3) & 1) * 3); }
 
-template <int D, int GW>
+// WB (block sizes that are multiples of 16): wave w stages the keys
+// [c0 + 16 w, c0 + 16 w + 16) of each 64-key chunk, which lie in one block, so
+// the block's address is uniform over the wave (scalar registers) and every
+// lane's offsets inside it are fixed for the whole loop.  The keys and values
+// go straight from HBM into LDS (global_load_lds_dwordx4: no staging
+// registers, no vector-ALU address arithmetic), keys two chunks ahead and
+// values one, and the loop is software-pipelined: the score products of chunk
+// i + 1 are issued between the softmax instructions of chunk i.  Otherwise
+// (blocks of 8) each 16-byte piece looks up its own block, is staged through
+// registers, and each chunk runs scores, softmax and values in turn.
+template <int D, int GW, bool WB>
 __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int NT = 256;             // threads: four waves
   constexpr int BT = 16 * (8 / GW);   // query tokens per workgroup
@@ -268,6 +278,88 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     }
   };
 
+  // Wave-group staging (WB): wave w stages the 16 keys [c0 + 16 w, + 16) of
+  // each chunk, KU = D / 32 loads of 64 lanes x 16 bytes for the keys and as
+  // many for the values.  A key load covers KR = 512 / D rows: lane row wkr,
+  // 16-byte column wdc.
+  static_assert(KU == D / 32 && VU == D / 32, "one 16-key group per wave");
+  constexpr int KR = 512 / D;
+  const int wkr = lane / (D / 8), wdc = lane % (D / 8);
+  // one wave's 16-key group of a chunk: the block holding keys [kb, kb + 16),
+  // or for a group past the context end the last group that holds keys (in
+  // bounds; zeroed with the boundary mask)
+  auto group_base = [&](int32_t c0, int64_t& off) -> int32_t {
+    const int32_t kb = c0 + 16 * w;  // uniform
+    const int32_t kl = min(kb, kend - 1) & ~15;
+    const int32_t blk = __builtin_amdgcn_readfirstlane(tab[(kl >> lp) - wb]);
+    off = (int64_t)blk * blk_stride;
+    return kl & (P - 1);  // offset of the group inside its block
+  };
+  // Direct global-to-LDS staging (WB): each global_load_lds_dwordx4 puts
+  // lane i's 16 bytes at the wave-uniform LDS address + 16 i, so a lane loads
+  // whichever global piece belongs at its slot.  Keys: the swizzled rows
+  // above, instruction u covering rows 16 w + u KR .. + KR - 1 (lane: row
+  // + wkr, slot wdc, so the piece wdc ^ kswz(row)).  Values: group-major,
+  // [8-key group][head_dim][8 keys]; wave w fills groups 2 w and 2 w + 1,
+  // instruction u covering head_dim rows 64 (u % VPG) .. + 63 of group
+  // 2 w + u / VPG.  The value-fragment reads of 16 consecutive rows of one
+  // group are then 256 contiguous bytes.
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  typedef __attribute__((address_space(1))) void* gptr_t;
+  constexpr int VPG = D / 64;  // value instructions per 8-key group
+  uint32_t kdoff[KU];          // bytes from the group's first key row
+#pragma unroll
+  for (int u = 0; u < KU; ++u) {
+    const int row = u * KR + wkr;
+    kdoff[u] = (uint32_t)(row * a.ks.tok * 2 + (wdc ^ kswz<D>(16 * w + row)) * 16);
+  }
+  const uint32_t vdoff = (uint32_t)(lane * P * 2);  // bytes: this lane's head_dim row
+  auto vslot = [&](int vbuf, int u) -> uint16_t* {   // instruction u's LDS run
+    return &v_lds[vbuf][((2 * w + u / VPG) * D + (u % VPG) * 64) * 8];
+  };
+  auto kload_direct = [&](int32_t c0, int kbuf) {
+    int64_t boff;
+    const int32_t o = group_base(c0, boff);
+    const char* kbase = (const char*)(kc + boff + khead + (int64_t)o * a.ks.tok);
+#pragma unroll
+    for (int u = 0; u < KU; ++u)
+      __builtin_amdgcn_global_load_lds((gptr_t)(kbase + kdoff[u]),
+                                       (lds_ptr_t)&k_lds[kbuf][(16 * w + u * KR) * KS], 16, 0, 0);
+  };
+  auto vload_direct = [&](int32_t c0, int vbuf) {
+    int64_t boff;
+    const int32_t o = group_base(c0, boff);
+    const char* vbase = (const char*)(vc + boff + vhead + o);
+#pragma unroll
+    for (int u = 0; u < VU; ++u)
+      __builtin_amdgcn_global_load_lds((gptr_t)(vbase + (u % VPG) * 64 * P * 2 + (u / VPG) * 16 + vdoff),
+                                       (lds_ptr_t)vslot(vbuf, u), 16, 0, 0);
+  };
+  // After this wave's loads of a group that reaches past the context end
+  // have landed (vmcnt 0): zero the values of keys >= kend in its own slots
+  // (those slots of the last block hold no token yet; a group wholly past
+  // the end was loaded from the last group that holds keys).
+  auto vfix = [&](int32_t c0, int vbuf) {
+    const int32_t kb = c0 + 16 * w;
+    if (kb + 16 <= kend) return;  // uniform
+#pragma unroll
+    for (int u = 0; u < VU; ++u) {
+      const int32_t t0 = kb + 8 * (u / VPG);
+      const int32_t nv = t0 >= kend ? 0 : min(kend - t0, 8);
+      const uint32_t m0 = nv >= 2 ? 0xffffffffu : (nv == 1 ? 0x0000ffffu : 0u);
+      const uint32_t m1 = nv >= 4 ? 0xffffffffu : (nv == 3 ? 0x0000ffffu : 0u);
+      const uint32_t m2 = nv >= 6 ? 0xffffffffu : (nv == 5 ? 0x0000ffffu : 0u);
+      const uint32_t m3 = nv >= 8 ? 0xffffffffu : (nv == 7 ? 0x0000ffffu : 0u);
+      uint4* sl = reinterpret_cast<uint4*>(vslot(vbuf, u) + lane * 8);
+      uint4 x = *sl;
+      x.x &= m0;
+      x.y &= m1;
+      x.z &= m2;
+      x.w &= m3;
+      *sl = x;
+    }
+  };
+
   f32x4 acc[2][NJ];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
@@ -385,23 +477,245 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
 
   load_tab(0);
   __syncthreads();
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int32_t ci = 0; ci < nchunks; ++ci) {
-    const int32_t c0 = ci * CH;
-    const bool more = ci + 1 < nchunks;  // uniform
-    if (more && min(c0 + 2 * CH, kend) - 1 >= (wb + TW) * P) {
-      // the next chunk leaves the table window; every read of it is behind
-      // the last barrier
-      wb = (c0 + CH) >> lp;
-      load_tab(wb);
+  if constexpr (WB) {
+    // Software-pipelined loop.  Iteration ci runs the softmax of chunk ci in
+    // the same basic block as the score products of chunk ci + 1 (they are
+    // independent, so the in-order issue alternates vector-ALU and
+    // matrix-core instructions), then the value products of chunk ci.  Keys
+    // are staged two chunks ahead, values one: the key buffer of chunk ci is
+    // free once its scores are taken (in iteration ci - 1), the value buffer
+    // of chunk ci - 1 once its products are taken.
+    struct Sc {
+      f32x4 x[2][NH], y[2][NH];
+    };
+    auto scores = [&](int kbuf) -> Sc {
+      const uint16_t* kl = k_lds[kbuf];
+      Sc sc;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) sc.x[t][h] = sc.y[t][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+#pragma unroll
+        for (int i = 0; i < KI; ++i) {
+          const int cb = ((4 * i + r) ^ kx) * 8;
+          const bf16x8 ax = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x) * KS + cb]);
+          const bf16x8 ay = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x + 4) * KS + cb]);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            sc.x[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, qf[t][i], sc.x[t][h], 0, 0, 0);
+            sc.y[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ay, qf[t][i], sc.y[t][h], 0, 0, 0);
+          }
+        }
+      }
+      return sc;
+    };
+    // causal mask of chunk c0's scores (rare: only chunks that reach past
+    // some query's position)
+    auto mask = [&](Sc& sc, int32_t c0) {
+      if (c0 + CH - 1 > base + min(tok0[0], tok0[1])) {  // uniform
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int32_t kx0 = c0 + 32 * h + 8 * r + e;
+              sc.x[t][h][e] = kx0 <= qpos[t] ? sc.x[t][h][e] : -INFINITY;
+              sc.y[t][h][e] = kx0 + 4 <= qpos[t] ? sc.y[t][h][e] : -INFINITY;
+            }
+      }
+    };
+    // Softmax of one chunk: probabilities (bf16) against the running
+    // reference, which moves (branch-free, per column) only when the chunk's
+    // maximum exceeds it by more than 2^8; the accumulators are rescaled
+    // afterwards, in a rare branch, by 2^((m_old - m_new) c).
+    float m_old[2];
+    auto softmax = [&](const Sc& sc, bf16x8 (&pb)[2][NH]) -> bool {
+      bool moved = false;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float x = sc.x[t][0][0];
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x = fmaxf(x, fmaxf(sc.x[t][h][e], sc.y[t][h][e]));
+        const float cm = pair_max16(pair_max32(x));
+        const bool up = (cm - m_run[t]) * c > kRefSlack;
+        m_old[t] = m_run[t];
+        m_run[t] = up ? fmaxf(m_run[t], cm) : m_run[t];
+        moved |= up;
+        const float mc = m_run[t] * c;
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pb[t][h][e] = (__bf16)fast_exp2(fmaf(sc.x[t][h][e], c, -mc));
+            pb[t][h][e + 4] = (__bf16)fast_exp2(fmaf(sc.y[t][h][e], c, -mc));
+          }
+      }
+      return moved;
+    };
+    // Scores of the next chunk fused with the softmax of the current one, in
+    // a fixed issue order: segment k reads two key fragments ahead and issues
+    // the four products of step k (both tiles, chains X and Y); its vector
+    // work is the two row-maximum reductions (segments 0, 1), then an equal
+    // share of the exponentials.  A scheduling fence after every segment
+    // keeps the order, so the matrix core works on the next chunk while the
+    // vector ALU works on this one.
+    auto fused = [&](int kbuf, Sc& nx, const Sc& cu, bf16x8 (&pb)[2][NH]) -> bool {
+      constexpr int NSEG = NH * KI;
+      constexpr int NE = 2 * NH * 8;  // probabilities per lane per chunk
+      const uint16_t* kl = k_lds[kbuf];
+      bf16x8 ax[NSEG], ay[NSEG];
+      auto kread = [&](int k) {
+        const int h = k / KI, i = k % KI;
+        const int cb = ((4 * i + r) ^ kx) * 8;
+        ax[k] = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x) * KS + cb]);
+        ay[k] = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x + 4) * KS + cb]);
+      };
+      auto kmfma = [&](int k) {
+        const int h = k / KI, i = k % KI;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          nx.x[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[k], qf[t][i], i ? nx.x[t][h] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          nx.y[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ay[k], qf[t][i], i ? nx.y[t][h] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        }
+      };
+      bool moved = false;
+      float mc[2];
+      auto rowmax = [&](int t) {
+        float x = cu.x[t][0][0];
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x = fmaxf(x, fmaxf(cu.x[t][h][e], cu.y[t][h][e]));
+        const float cm = pair_max16(pair_max32(x));
+        const bool up = (cm - m_run[t]) * c > kRefSlack;
+        m_old[t] = m_run[t];
+        m_run[t] = up ? fmaxf(m_run[t], cm) : m_run[t];
+        moved |= up;
+        mc[t] = m_run[t] * c;
+      };
+      // probability q (q = ((t * NH + h) * 2 + xy) * 4 + e) of this lane
+      auto prob = [&](int q) {
+        const int e = q & 3, xy = (q >> 2) & 1, h = (q >> 3) % NH, t = (q >> 3) / NH;
+        const float sv = xy ? cu.y[t][h][e] : cu.x[t][h][e];
+        pb[t][h][e + 4 * xy] = (__bf16)fast_exp2(fmaf(sv, c, -mc[t]));
+      };
+      kread(0);
+      if (NSEG > 1) kread(1);
+#pragma unroll
+      for (int k = 0; k < NSEG; ++k) {
+        if (k + 2 < NSEG) kread(k + 2);
+        kmfma(k);
+        if (k < 2) {
+          rowmax(k);
+        } else {
+          constexpr int per = (NE + NSEG - 3) / (NSEG - 2);
+#pragma unroll
+          for (int q = (k - 2) * per; q < (k - 1) * per && q < NE; ++q) prob(q);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return moved;
+    };
+    auto values = [&](int vbuf, const bf16x8 (&pb)[2][NH]) {
+      const uint16_t* vl = v_lds[vbuf];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+          lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[t][h], lsum[t], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(&vl[((4 * h + r) * D + 16 * j + nq) * 8]);
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[t][h], acc[t][j], 0, 0, 0);
+        }
+      }
+    };
+
+    kload_direct(0, 0);
+    vload_direct(0, 0);
+    if (nchunks > 1) kload_direct(CH, 1);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
+    vfix(0, 0);
+    __syncthreads();
+    // one iteration: chunk ci's softmax and value products, chunk ci + 1's
+    // scores into `nxt`; unrolled by two below so that the two score sets
+    // trade roles without register copies
+    auto step = [&](int32_t ci, Sc& cur, Sc& nxt) {
+      const int32_t c0 = ci * CH;
+      const bool more = ci + 1 < nchunks, more2 = ci + 2 < nchunks;  // uniform
+      if (more && min(c0 + 3 * CH, kend) - 1 >= (wb + TW) * P) {
+        // the staged chunks leave the table window; every read of it is
+        // behind the last barrier
+        wb = (c0 + CH) >> lp;
+        load_tab(wb);
+        __syncthreads();
+      }
+      if (more2) kload_direct(c0 + 2 * CH, ci & 1);
+      if (more) vload_direct(c0 + CH, (ci + 1) & 1);
+      if (c0 < wave_kend) {  // uniform over the wave
+        mask(cur, c0);
+        bf16x8 pb[2][NH];
+        bool moved;
+        if (more && c0 + CH < wave_kend) {  // uniform
+          moved = fused((ci + 1) & 1, nxt, cur, pb);
+        } else {
+          moved = softmax(cur, pb);
+        }
+        // keep the probabilities computed here, beside the score products,
+        // rather than sunk past the rare rescale branch below
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int h = 0; h < NH; ++h) asm volatile("" : "+v"(pb[t][h]));
+        if (__builtin_amdgcn_ballot_w64(moved) != 0) {  // rare
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const float alpha = fast_exp2((m_old[t] - m_run[t]) * c);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) acc[t][j] *= alpha;
+            lsum[t] *= alpha;
+          }
+        }
+        values(ci & 1, pb);
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
+      if (more) vfix(c0 + CH, (ci + 1) & 1);
+      __syncthreads();
+    };
+    Sc sa, sb;
+    if (0 < wave_kend) sa = scores(0);  // uniform
+    for (int32_t ci = 0; ci < nchunks; ci += 2) {
+      step(ci, sa, sb);
+      if (ci + 1 < nchunks) step(ci + 1, sb, sa);
+    }
+  } else {
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int32_t ci = 0; ci < nchunks; ++ci) {
+      const int32_t c0 = ci * CH;
+      const bool more = ci + 1 < nchunks;  // uniform
+      if (more && min(c0 + 2 * CH, kend) - 1 >= (wb + TW) * P) {
+        // the next chunk leaves the table window; every read of it is behind
+        // the last barrier
+        wb = (c0 + CH) >> lp;
+        load_tab(wb);
+        __syncthreads();
+      }
+      if (more) gload(c0 + CH);
+      if (c0 < wave_kend) compute(ci & 1, c0);  // uniform over the wave
+      if (more) lstore((ci + 1) & 1);
       __syncthreads();
     }
-    if (more) gload(c0 + CH);
-    if (c0 < wave_kend) compute(ci & 1, c0);  // uniform over the wave
-    if (more) lstore((ci + 1) & 1);
-    __syncthreads();
   }
 
   // totals over the four row groups, then the output rows of each tile
@@ -431,7 +745,8 @@ void launch_prefill_g(PrefillArgs a, int32_t max_q, hipStream_t st) {
   a.n_tiles = (max_q + BT - 1) / BT;
   const int64_t n_groups = (int64_t)a.n_seqs * a.hkv * halves;
   const int64_t wgs = (n_groups + kXcds - 1) / kXcds * kXcds * a.n_tiles;
-  hipLaunchKernelGGL((prefill_mfma_kernel<D, GW>), dim3((unsigned)wgs), dim3(256), 0, st, a);
+  if (a.p >= 16) hipLaunchKernelGGL((prefill_mfma_kernel<D, GW, true>), dim3((unsigned)wgs), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((prefill_mfma_kernel<D, GW, false>), dim3((unsigned)wgs), dim3(256), 0, st, a);
 }
 
 template <int D>
