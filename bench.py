@@ -175,8 +175,7 @@ def run_beam(args):
         "decode_tokens_per_s": round(b / (ms_step * 1e-3), 1),
         "decode_ms": round(dec_ms, 4),
         "decode_bytes_per_step": int(dbytes),
-        "decode_calls": len(per_call),
-        "decode_bytes_mean_per_call": int(round(float(np.mean(per_call)))), "decode_unique_bytes": int(ubytes),
+        "decode_unique_bytes": int(ubytes),
         "unique_GB_per_s": round(ubytes / (dec_ms * 1e-3) / 1e9, 1),
         "fragmentation": round(st["fragmentation"], 6),
         "copy_on_write": {"pairs": int(len(cow)), "first_step_ms": round(first_copy_ms, 4),

@@ -301,7 +301,14 @@ int pkv_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_
  *                    The tables are not
  *                    compared: a count larger than the true shared prefix makes
  *                    that sequence read its predecessor's tokens (in bounds).
- *                    PKV_DECODE_SHARE=off ignores the array.
+ *                    PKV_DECODE_SHARE=off ignores the array.  Runs of
+ *                    more than 16 / G sharing sequences (block sizes of
+ *                    16, 32 or 64 tokens) form wide packs of up to 128 / G
+ *                    sequences (at most 32) whose shared tokens are read
+ *                    once for all their query rows as a dense matrix-core
+ *                    product; those sum in another order, so the
+ *                    bit-identity above holds for narrow packs only
+ *                    (PKV_DECODE_WIDE=off keeps every pack narrow).
  *   max_context_len  >= every L (host knowledge, used for sizing)
  *   total_context_tokens  >= sum of L, or -1 if unknown (a bound from
  *                    n_seqs * max_context_len is used then).  It sizes the

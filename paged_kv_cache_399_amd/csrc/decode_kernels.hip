@@ -57,6 +57,7 @@
 
 #include "device_common.hpp"
 #include "internal.hpp"
+#include "tile_common.hpp"
 
 namespace pkv {
 namespace {
@@ -227,7 +228,7 @@ __device__ __forceinline__ Unit decode_unit(const DecodeArgs& a, int32_t unit) {
 // batch, else 1024), one length bucket per thread.
 // ---------------------------------------------------------------------------
 constexpr int kPlanThreads = 1024;  // the plan workgroup for batches of more than 256 sequences
-constexpr int kPackMax = 16;        // MFMA columns
+constexpr int kPackMax = 32;        // most sequences in one pack (wide packs)
 constexpr int kShareChunk = 32;     // granularity of a pack's shared tokens (the decode chunk)
 
 // Exclusive scans of two non-negative counts at once (packed in 64 bits; each
@@ -384,7 +385,7 @@ __global__ __launch_bounds__(NT) void plan_kernel(DecodeArgs a) {
       if (in) {
         int32_t mn = INT32_MAX;
         for (int32_t i = 1; i < S; ++i) {
-          const int32_t jm = jt[kPackMax + lead + i - base];  // lead + i - base in [-15, NT + 15)
+          const int32_t jm = jt[kPackMax + lead + i - base];  // lead + i - base in [-31, NT + 31)
           if (jm == 0) break;
           mn = min(mn, jm);
           ++k;
@@ -497,6 +498,361 @@ struct MfmaChunk {
   uint4 kx[KI], ky[KI], v[NJ];
 };
 
+// ---------------------------------------------------------------------------
+// Wide packs.  When sequences that share blocks form packs of more than 16
+// MFMA columns (up to 128 / G sequences, pack * G query rows), a pack unit
+// reads the shared tokens [t0, t1) of its first sequence once for all its
+// rows: a dense product, as in paged prefill.  Four waves take two 16-row
+// tiles each (row 16 k + n of tile k is query head (row % G) of pack member
+// row / G); 64-key chunks go straight from HBM into LDS (each wave loads one
+// 16-key group, which lies in one block: P is a multiple of 16), keys two
+// chunks ahead and values one, and the score products of chunk i + 1 are
+// issued between the softmax instructions of chunk i.  Each row's (max, sum,
+// normalised output) goes to its member's partial slot, exactly where the
+// narrow pack path puts that column's partial.
+// ---------------------------------------------------------------------------
+constexpr int kWideRows = 128;     // query rows of a wide pack unit (eight 16-row tiles)
+constexpr int kWideMaxPack = 32;   // sequences a wide pack may hold
+constexpr int kWideTab = 1024;     // block-table entries of one unit (T / P <= 1024)
+constexpr float kWideSlack = 8.f;  // log2 headroom before the running reference moves
+
+template <int D>
+struct WideLds {
+  uint16_t k[2][64 * D];  // key rows, 16-byte pieces swizzled (kswz)
+  uint16_t v[2][64 * D];  // [8-key group][head_dim][8 keys]
+  int32_t tab[kWideTab];
+  int32_t row_slot[kWideRows], row_np[kWideRows];
+};
+
+template <int D, int P>
+__device__ __forceinline__ void wide_pack_unit(const DecodeArgs& a, const Unit& u, int32_t g,
+                                               WideLds<D>& L) {
+  static_assert(P % 16 == 0, "a 16-key group must lie in one block");
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  typedef __attribute__((address_space(1))) void* gptr_t;
+  constexpr int CH = 64, NH = 2, KI = D / 32, NJ = D / 16;
+  constexpr int KU = D / 32, KR = 512 / D, VPG = D / 64;  // staging loads per wave, rows per key load
+  constexpr int NSEG = NH * KI;                            // fused score / softmax segments
+  constexpr int NE = 2 * NH * 8;                           // probabilities per lane per chunk
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = uniform(tid >> 6);
+  const int nq = lane & 15, r = lane >> 4;
+  const int32_t G = a.hq / a.hkv;
+  const int32_t rows = u.pack * G;
+  const int32_t T = a.part_tokens;
+  const int32_t t0 = u.t0, t1 = u.t1;
+  const float c = a.scale_log2;
+
+  // per row: the partial slot and partial count of its member (the narrow
+  // pack path's column rule)
+  if (tid < rows) {
+    const int4 si = a.plan.seq_info[u.b + tid / G];
+    const bool tail = (t1 & (T - 1)) != 0;
+    L.row_slot[tid] = si.x + (tail && si.y > si.z ? si.z : t0 / T);
+    L.row_np[tid] = si.y;
+  }
+  // the first sequence's block ids of keys [t0, t1)
+  const int32_t* trow = a.table + (int64_t)u.b * a.max_blocks;
+  const int32_t blk0 = t0 / P;
+  const int32_t nblk = min((t1 - 1) / P - blk0 + 1, kWideTab);
+  for (int i = tid; i < nblk; i += 256) {
+    int32_t e = trow[blk0 + i];
+    if ((uint32_t)e >= (uint32_t)a.num_blocks) {
+      atomicOr(a.err, PKV_DEVERR_TABLE_ENTRY);
+      e = 0;
+    }
+    L.tab[i] = e;
+  }
+  // query fragments: column nq of tile k (= 2 w + t) is row 16 k + nq;
+  // padding rows repeat the last row and are not written
+  bf16x8 qf[2][KI];
+  int32_t row_of[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int32_t row = 16 * (2 * w + t) + nq;
+    row_of[t] = row;
+    const int32_t rc = min(row, rows - 1);
+    const int32_t mem = rc / G, hh = rc - mem * G;
+    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)(u.b + mem) * a.hq + g * G + hh) * D + 8 * r;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) qf[t][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qrow + 32 * i));
+  }
+
+  const uint16_t* kc = (const uint16_t*)a.kc;
+  const uint16_t* vc = (const uint16_t*)a.vc;
+  const int64_t blk_stride = (int64_t)a.hkv * P * D;
+  const int64_t khead = (int64_t)g * a.ks.head, vhead = (int64_t)g * P * D;
+  const int32_t nchunks = (t1 - t0 + CH - 1) / CH;
+
+  // staging: wave w loads keys [c0 + 16 w, + 16); a group past t1 reads the
+  // last group that holds keys (in bounds) and its values are zeroed
+  const int wkr = lane / (D / 8), wdc = lane % (D / 8);
+  uint32_t kdoff[KU];
+#pragma unroll
+  for (int uu = 0; uu < KU; ++uu) {
+    const int row = uu * KR + wkr;
+    kdoff[uu] = (uint32_t)(row * a.ks.tok * 2 + (wdc ^ kswz<D>(16 * w + row)) * 16);
+  }
+  const uint32_t vdoff = (uint32_t)(lane * P * 2);
+  auto group_base = [&](int32_t c0, int64_t& off) -> int32_t {
+    const int32_t kb = c0 + 16 * w;
+    const int32_t kl = min(kb, t1 - 1) & ~15;
+    const int32_t blk = __builtin_amdgcn_readfirstlane(L.tab[kl / P - blk0]);
+    off = (int64_t)blk * blk_stride;
+    return kl & (P - 1);
+  };
+  auto kload = [&](int32_t c0, int buf) {
+    int64_t boff;
+    const int32_t o = group_base(c0, boff);
+    const char* kbase = (const char*)(kc + boff + khead + (int64_t)o * a.ks.tok);
+#pragma unroll
+    for (int uu = 0; uu < KU; ++uu)
+      __builtin_amdgcn_global_load_lds((gptr_t)(kbase + kdoff[uu]), (lds_ptr_t)&L.k[buf][(16 * w + uu * KR) * D],
+                                       16, 0, 0);
+  };
+  auto vslot = [&](int buf, int uu) -> uint16_t* {
+    return &L.v[buf][((2 * w + uu / VPG) * D + (uu % VPG) * 64) * 8];
+  };
+  auto vload = [&](int32_t c0, int buf) {
+    int64_t boff;
+    const int32_t o = group_base(c0, boff);
+    const char* vbase = (const char*)(vc + boff + vhead + o);
+#pragma unroll
+    for (int uu = 0; uu < KU; ++uu)
+      __builtin_amdgcn_global_load_lds((gptr_t)(vbase + (uu % VPG) * 64 * P * 2 + (uu / VPG) * 16 + vdoff),
+                                       (lds_ptr_t)vslot(buf, uu), 16, 0, 0);
+  };
+  auto vfix = [&](int32_t c0, int buf) {
+    const int32_t kb = c0 + 16 * w;
+    if (kb + 16 <= t1) return;  // uniform
+#pragma unroll
+    for (int uu = 0; uu < KU; ++uu) {
+      const int32_t tg = kb + 8 * (uu / VPG);
+      const int32_t nv = tg >= t1 ? 0 : min(t1 - tg, 8);
+      const uint32_t m0 = nv >= 2 ? 0xffffffffu : (nv == 1 ? 0x0000ffffu : 0u);
+      const uint32_t m1 = nv >= 4 ? 0xffffffffu : (nv == 3 ? 0x0000ffffu : 0u);
+      const uint32_t m2 = nv >= 6 ? 0xffffffffu : (nv == 5 ? 0x0000ffffu : 0u);
+      const uint32_t m3 = nv >= 8 ? 0xffffffffu : (nv == 7 ? 0x0000ffffu : 0u);
+      uint4* sl = reinterpret_cast<uint4*>(vslot(buf, uu) + lane * 8);
+      uint4 x = *sl;
+      x.x &= m0;
+      x.y &= m1;
+      x.z &= m2;
+      x.w &= m3;
+      *sl = x;
+    }
+  };
+
+  f32x4 acc[2][NJ];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 lsum[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  float m_run[2] = {-INFINITY, -INFINITY}, m_old[2];
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+  const int krow_x = 8 * (nq >> 2) + (nq & 3);
+  const int kx = kswz<D>(krow_x);
+
+  struct Sc {
+    f32x4 x[2][NH], y[2][NH];
+  };
+  auto scores = [&](int buf) -> Sc {
+    const uint16_t* kl = L.k[buf];
+    Sc sc;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int h = 0; h < NH; ++h) sc.x[t][h] = sc.y[t][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int i = 0; i < KI; ++i) {
+        const int cb = ((4 * i + r) ^ kx) * 8;
+        const bf16x8 ax = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x) * D + cb]);
+        const bf16x8 ay = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x + 4) * D + cb]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          sc.x[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, qf[t][i], sc.x[t][h], 0, 0, 0);
+          sc.y[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ay, qf[t][i], sc.y[t][h], 0, 0, 0);
+        }
+      }
+    return sc;
+  };
+  // keys at or past t1 in the last chunk (uniform test)
+  auto mask = [&](Sc& sc, int32_t c0) {
+    if (c0 + CH > t1) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int32_t kx0 = c0 + 32 * h + 8 * r + e;
+            sc.x[t][h][e] = kx0 < t1 ? sc.x[t][h][e] : -INFINITY;
+            sc.y[t][h][e] = kx0 + 4 < t1 ? sc.y[t][h][e] : -INFINITY;
+          }
+    }
+  };
+  float mc[2];
+  bool moved;
+  auto rowmax = [&](const Sc& cu, int t) {
+    float x = cu.x[t][0][0];
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x = fmaxf(x, fmaxf(cu.x[t][h][e], cu.y[t][h][e]));
+    const float cm = pair_max16(pair_max32(x));
+    const bool up = (cm - m_run[t]) * c > kWideSlack;
+    m_old[t] = m_run[t];
+    m_run[t] = up ? fmaxf(m_run[t], cm) : m_run[t];
+    moved |= up;
+    mc[t] = m_run[t] * c;
+  };
+  auto prob = [&](const Sc& cu, bf16x8 (&pb)[2][NH], int q) {
+    const int e = q & 3, xy = (q >> 2) & 1, h = (q >> 3) % NH, t = (q >> 3) / NH;
+    const float sv = xy ? cu.y[t][h][e] : cu.x[t][h][e];
+    pb[t][h][e + 4 * xy] = (__bf16)fast_exp2(fmaf(sv, c, -mc[t]));
+  };
+  // softmax of `cu` fused with the score products of the next chunk into `nx`
+  auto fused = [&](int kbuf, Sc& nx, const Sc& cu, bf16x8 (&pb)[2][NH]) {
+    const uint16_t* kl = L.k[kbuf];
+    bf16x8 ax[NSEG], ay[NSEG];
+    auto kread = [&](int k) {
+      const int h = k / KI, i = k % KI;
+      const int cb = ((4 * i + r) ^ kx) * 8;
+      ax[k] = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x) * D + cb]);
+      ay[k] = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x + 4) * D + cb]);
+    };
+    auto kmfma = [&](int k) {
+      const int h = k / KI, i = k % KI;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        nx.x[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[k], qf[t][i], i ? nx.x[t][h] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        nx.y[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ay[k], qf[t][i], i ? nx.y[t][h] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      }
+    };
+    kread(0);
+    if (NSEG > 1) kread(1);
+#pragma unroll
+    for (int k = 0; k < NSEG; ++k) {
+      if (k + 2 < NSEG) kread(k + 2);
+      kmfma(k);
+      if (k < 2) {
+        rowmax(cu, k);
+      } else {
+        constexpr int per = (NE + NSEG - 3) / (NSEG - 2);
+#pragma unroll
+        for (int q = (k - 2) * per; q < (k - 1) * per && q < NE; ++q) prob(cu, pb, q);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto softmax = [&](const Sc& cu, bf16x8 (&pb)[2][NH]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) rowmax(cu, t);
+#pragma unroll
+    for (int q = 0; q < NE; ++q) prob(cu, pb, q);
+  };
+  auto values = [&](int buf, const bf16x8 (&pb)[2][NH]) {
+    const uint16_t* vl = L.v[buf];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int h = 0; h < NH; ++h) lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[t][h], lsum[t], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&vl[((4 * h + r) * D + 16 * j + nq) * 8]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[t][h], acc[t][j], 0, 0, 0);
+      }
+  };
+
+  // prologue: keys of chunks 0 and 1, values of chunk 0
+  __syncthreads();  // table window and row slots
+  kload(t0, 0);
+  vload(t0, 0);
+  if (nchunks > 1) kload(t0 + CH, 1);
+  __builtin_amdgcn_s_waitcnt(0);
+  vfix(t0, 0);
+  __syncthreads();
+  auto step = [&](int32_t ci, Sc& cur, Sc& nxt) {
+    const int32_t c0 = t0 + ci * CH;
+    const bool more = ci + 1 < nchunks, more2 = ci + 2 < nchunks;  // uniform
+    if (more2) kload(c0 + 2 * CH, ci & 1);
+    if (more) vload(c0 + CH, (ci + 1) & 1);
+    mask(cur, c0);
+    bf16x8 pb[2][NH];
+    moved = false;
+    if (more) {
+      fused((ci + 1) & 1, nxt, cur, pb);
+    } else {
+      softmax(cur, pb);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int h = 0; h < NH; ++h) asm volatile("" : "+v"(pb[t][h]));
+    if (__builtin_amdgcn_ballot_w64(moved) != 0) {  // rare: a reference moved
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float alpha = fast_exp2((m_old[t] - m_run[t]) * c);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[t][j] *= alpha;
+        lsum[t] *= alpha;
+      }
+    }
+    values(ci & 1, pb);
+    __builtin_amdgcn_s_waitcnt(0);
+    if (more) vfix(c0 + CH, (ci + 1) & 1);
+    __syncthreads();
+  };
+  Sc sa = scores(0), sb;
+  // every wave has read chunk 0's keys before step 0 loads chunk 2 over them
+  __syncthreads();
+  for (int32_t ci = 0; ci < nchunks; ci += 2) {
+    step(ci, sa, sb);
+    if (ci + 1 < nchunks) step(ci + 1, sb, sa);
+  }
+
+  // per row: (reference max in log2 units, sum, normalised output) to the
+  // member's slot, or the output itself for a member with one partial
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int32_t row = row_of[t];
+    if (row >= rows) continue;
+    const int32_t mem = row / G, hh = row - mem * G;
+    const int32_t qh = g * G + hh, seq = u.b + mem;
+    const float l = lsum[t][0];
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int32_t slot = L.row_slot[row], np = L.row_np[row];
+    if (np == 1) {
+      uint16_t* orow = (uint16_t*)a.out + ((int64_t)seq * a.hq + qh) * D + 4 * r;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) store_f32(orow + 16 * j + e, acc[t][j][e] * inv);
+    } else {
+      float* po = a.plan.part_o + ((int64_t)slot * a.hq + qh) * D + 4 * r;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const f32x4 x = acc[t][j] * inv;
+        __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(po + 16 * j));
+      }
+      if (r == 0) {
+        float* ml = a.plan.part_ml + ((int64_t)slot * a.hq + qh) * 2;
+        ml[0] = m_run[t] * c;
+        ml[1] = l;
+      }
+    }
+  }
+}
+
 // Workgroup of W waves per (partition, KV head) unit.  Wave w streams the
 // tokens [t0 + w TW, t0 + (w + 1) TW) of the partition (TW = T / W) with its
 // own running max, sum and accumulator; the W states are combined through
@@ -504,16 +860,32 @@ struct MfmaChunk {
 // once per wave: partial-result writes interleaved with the key/value read
 // stream cost far more than their byte count.
 template <int D, int P, int W, bool MIXED>
-__global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void decode_mfma_kernel(DecodeArgs a) {
   using Chunk = MfmaChunk<D, P>;
   constexpr int KI = Chunk::KI, NJ = Chunk::NJ;
   constexpr int CH = 32;     // tokens per chunk
   constexpr int DP = D + 4;  // padded LDS row of one head's accumulator
   static_assert((P < 8 || P % 8 == 0) && (P <= CH ? CH % P == 0 : P % CH == 0), "block size");
-  __shared__ float red_o[W][16][DP];
-  __shared__ float red_m[W][16], red_l[W][16];
-  __shared__ int32_t tab_lds[W][P < 8 ? 512 : 1];
-  __shared__ int32_t col_slot[16], col_np[16];  // per column of a pack: partial slot, partitions
+  // LDS: the combine buffers of this path, or (wide pack units, compiled into
+  // the kernel that batches with packs launch) the wide path's staging, in
+  // one allocation
+  struct NarrowLds {
+    float red_o[W][16][DP];
+    float red_m[W][16], red_l[W][16];
+    int32_t tab_lds[W][P < 8 ? 512 : 1];
+    int32_t col_slot[16], col_np[16];  // per column of a pack: partial slot, partitions
+  };
+  constexpr bool kWide = MIXED && W == 4 && P % 16 == 0;
+  constexpr size_t kLdsBytes =
+      kWide && sizeof(WideLds<D>) > sizeof(NarrowLds) ? sizeof(WideLds<D>) : sizeof(NarrowLds);
+  __shared__ __align__(16) unsigned char lds_raw[kLdsBytes];
+  NarrowLds& nl = *reinterpret_cast<NarrowLds*>(lds_raw);
+  auto& red_o = nl.red_o;
+  auto& red_m = nl.red_m;
+  auto& red_l = nl.red_l;
+  auto& tab_lds = nl.tab_lds;
+  auto& col_slot = nl.col_slot;
+  auto& col_np = nl.col_np;
 
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
@@ -523,6 +895,12 @@ __global__ __launch_bounds__(64 * W) void decode_mfma_kernel(DecodeArgs a) {
   const Unit u = decode_unit(a, unit);
   if (!u.valid) return;             // uniform over the workgroup
   const int32_t G = a.hq / a.hkv;
+  if constexpr (kWide) {
+    if (u.pack * G > 16) {  // uniform: a pack wider than the MFMA columns
+      wide_pack_unit<D, P>(a, u, g, *reinterpret_cast<WideLds<D>*>(lds_raw));
+      return;
+    }
+  }
   const int n = lane & 15, r = lane >> 4;
   // MFMA column n: query head n % G of pack member n / G (the unit's own
   // sequence when the pack is one sequence); columns >= pack * G are padding
@@ -1789,8 +2167,15 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   // columns take 16 / G sequences' head groups).  A hint that nothing is
   // shared (unshared == total) skips the array and the plan's pack pass.
   a.pack_max = 1;
-  if (d_shared_prev && c.may_pack && c.kind == pkv::kKindMfma && !pkv::env_is("PKV_DECODE_SHARE", "off"))
-    a.pack_max = std::max(1, std::min(pkv::kPackMax, 16 / (num_q_heads / num_kv_heads)));
+  if (d_shared_prev && c.may_pack && c.kind == pkv::kKindMfma && !pkv::env_is("PKV_DECODE_SHARE", "off")) {
+    // narrow packs fill the 16 MFMA columns (16 / G sequences); wide packs
+    // (four waves, blocks of 16, 32 or 64 tokens, units of at most
+    // kWideTab blocks) take up to 128 / G sequences, read with a dense product
+    const int32_t G = num_q_heads / num_kv_heads;
+    const bool wide = c.waves_per_group == 4 && block_size % 16 == 0 &&
+                      c.part_tokens / block_size <= pkv::kWideTab && !pkv::env_is("PKV_DECODE_WIDE", "off");
+    a.pack_max = wide ? std::min(pkv::kWideMaxPack, pkv::kWideRows / G) : std::max(1, 16 / G);
+  }
   a.len_cap = std::min<int64_t>((int64_t)max_blocks_per_seq * block_size, max_context_len);
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.plan.counts = (int32_t*)(ws + lay.counts);

@@ -39,6 +39,7 @@
 
 #include "device_common.hpp"
 #include "internal.hpp"
+#include "tile_common.hpp"
 
 namespace pkv {
 namespace {
@@ -75,38 +76,8 @@ constexpr float kRefSlack = 8.f;
 
 constexpr int kXcds = 8;  // accelerator complex dies (separate L2 caches) on MI355X
 
-// Pairwise maxima with lane swaps on the vector ALU: v_permlane32_swap
-// exchanges the upper half of one register with the lower half of another;
-// with both operands equal, its two results hold the values of lanes l and
-// l ^ 32 (v_permlane16_swap: of 16-lane rows, l and l ^ 16), in the same
-// order in every lane, so both lanes of a pair get the same bits.
-__device__ __forceinline__ float pair_max32(float v) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, v);
-  const auto x = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__builtin_bit_cast(float, (uint32_t)x[0]), __builtin_bit_cast(float, (uint32_t)x[1]));
-}
-__device__ __forceinline__ float pair_max16(float v) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, v);
-  const auto x = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  return fmaxf(__builtin_bit_cast(float, (uint32_t)x[0]), __builtin_bit_cast(float, (uint32_t)x[1]));
-}
-
-// LDS layout of the staged chunk.
-//
-// Key rows sit in LDS unpadded, with the 16-byte piece c of key row k stored
-// at piece c ^ kswz(k).  One score-fragment read covers key rows
-// {8a + b (+4) : a, b < 4} (the MFMA row order that gives each lane eight
-// consecutive keys) at one piece index.  With rows padded by one piece
-// (a uniform stride) those rows shared banks: on gfx950 the bank-conflict
-// counter (SQ_LDS_BANK_CONFLICT) showed 4 extra cycles per such read, and 0
-// with this swizzle (probe kernels of the exact address patterns).  The XOR
-// uses row bits 0, 1, 3 and 4; bits 2 and 5 (chain Y, second half) are not
-// used, so all rows a lane reads share one swizzle.
-template <int D>
-__device__ __forceinline__ int kswz(int k) {
-  if constexpr (D == 128) return (k & 3) | (((k >> 3) & 3) << 2);
-  return ((k & 3) | (((k >> 3) & 1) << 2)) ^ (((k >> 4) & 1) * 3);
-}
+// pair_max32 / pair_max16 (row-group maxima) and kswz (the key-row LDS
+// swizzle) are in tile_common.hpp.
 
 // Value rows (one head_dim row of a chunk's 64 keys, token-minor) sit
 // unpadded too, piece c of row d at c ^ vswz(d).  The value-fragment reads
@@ -693,6 +664,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     };
     Sc sa, sb;
     if (0 < wave_kend) sa = scores(0);  // uniform
+    // every wave has read chunk 0's keys before step 0 loads chunk 2 over them
+    __syncthreads();
     for (int32_t ci = 0; ci < nchunks; ci += 2) {
       step(ci, sa, sb);
       if (ci + 1 < nchunks) step(ci + 1, sb, sa);
