@@ -28,7 +28,10 @@
 // partition they share: the matrix-core kernel then gives each packed
 // sequence's query heads their own MFMA columns and reads the shared keys and
 // values once for the pack.  Each column's arithmetic is what its own unit
-// would do, so results are bit-identical with or without packing.
+// would do, so results are bit-identical with or without packing.  Longer runs
+// form wide packs of up to 128 / G sequences, whose shared tokens are read once
+// for all their query rows as a dense product (wide_pack_unit; another
+// summation order, within the same tolerance).
 //
 // Partition kernels:
 //  * decode_mfma_kernel (bf16, head_dim 64/128, block size 1..64, G <= 16):
