@@ -72,10 +72,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 struct Plan {
   int32_t* counts;     // [0] units to run (0 if the plan overflowed), [1] full-length units
-  int4* seq_info;      // [n_seqs]: (first slot, partials, partitions, unused); slots are contiguous
+  int4* seq_info;      // [n_seqs]: (first slot, partials, partitions, leading piece slots);
+                       // slots are contiguous
   int2* seq_pack;      // [n_seqs]: (tokens its pack shares or 0, pack size if it leads a pack
                        // else 0), kept between plan passes when one pass does not cover the batch
-  int4* work;          // [max_units]: (sequence, first token, end token, sequences in the pack)
+  int4* work;          // [max_units]: (sequence, first token, end token, sequences in the pack
+                       // | (piece + 1) << 16 for a piece of a wide pack's shared partition)
   int2* work_out;      // [max_units]: (partial slot, partials) of the unit's first sequence
   float* part_ml;      // [max_units * Hq * 2] per slot: running max (log2 units), sum
   float* part_o;       // [max_units * Hq * D] per slot: normalised partial output
@@ -91,6 +93,7 @@ struct DecodeArgs {
   const int32_t* shared;  // tokens each sequence holds in its predecessor's blocks, or null
   int32_t n_seqs, hq, hkv, d, p, num_blocks, max_blocks, part_tokens, max_units;
   int32_t pack_max;  // sequences one unit may take (1: no packing)
+  int32_t wide_split;  // pieces each whole shared partition of a wide pack is cut into (1: none)
   KStrides ks;       // key cache: elements between KV heads, between tokens
   int64_t len_cap;   // min(max_blocks * p, max_context_len): longer contexts are clamped
   float scale_log2;  // scale * log2(e): scores are kept in log2 units
@@ -184,7 +187,7 @@ __device__ __forceinline__ int32_t uniform(int32_t v) { return __builtin_amdgcn_
 // [t0, t1) of sequences b .. b + pack - 1 (pack > 1 only for whole shared
 // partitions); slot and nparts belong to sequence b.
 struct Unit {
-  int32_t b, t0, t1, pack, slot, nparts, valid;
+  int32_t b, t0, t1, pack, piece, slot, nparts, valid;
 };
 
 __device__ __forceinline__ Unit decode_unit(const DecodeArgs& a, int32_t unit) {
@@ -196,7 +199,8 @@ __device__ __forceinline__ Unit decode_unit(const DecodeArgs& a, int32_t unit) {
   u.b = w.x;
   u.t0 = w.y;
   u.t1 = w.z;
-  u.pack = w.w;
+  u.pack = w.w & 0xffff;
+  u.piece = w.w >> 16;  // 0, or 1 + the piece of a wide pack's split shared partition
   u.slot = o.x;
   u.nparts = o.y;
   return u;
@@ -227,6 +231,12 @@ __device__ __forceinline__ Unit decode_unit(const DecodeArgs& a, int32_t unit) {
 // remainder [Ls, min((j0+1) T, L)) (slot first + j0); a member with no
 // remainder takes the tail in slot first + j0.  Everything from partition
 // j0 + 1 on (from j0 if Ls % T == 0) is the member's own.
+// A wide pack (k G > 16 query rows, read as one dense product) costs far more
+// per token than a streaming unit, so each of its whole shared partitions is
+// cut into wide_split pieces of T / wide_split tokens (one unit each); every
+// member keeps nsub = floor(Ls/T) (wide_split - 1) more slots for pieces 1 ..,
+// placed before its partition slots (seq_info.w = nsub, partition j at slot
+// first + nsub + j).
 // One workgroup of NT threads (the smallest of 64, 128, 256 that covers the
 // batch, else 1024), one length bucket per thread.
 // ---------------------------------------------------------------------------
@@ -333,6 +343,7 @@ __global__ __launch_bounds__(NT) void plan_kernel(DecodeArgs a) {
   const int32_t T = a.part_tokens;
   const int64_t cap = a.len_cap;
   const int32_t S = a.pack_max;
+  const int32_t G = a.hq / a.hkv;
   const int tid = threadIdx.x;
   bucket[tid] = 0;
   if (tid < kPackMax) jt[tid] = 0;  // no sequence before the first
@@ -400,31 +411,39 @@ __global__ __launch_bounds__(NT) void plan_kernel(DecodeArgs a) {
     const int32_t extra = (tail > 0 && L > Ls) ? 1 : 0;
     const bool leader = in && b == lead && k >= 2;
     const int32_t own_start = nshf + (tail > 0 ? 1 : 0);
-    const int32_t nrows = in ? (leader ? nshf : 0) + max(nfull - own_start, 0) : 0;
-    const int32_t count = in ? np + extra : 0;
+    // a wide pack cuts each whole shared partition into SW pieces; pieces
+    // 1 .. SW - 1 of partition j take the member's slots first + j (SW - 1)
+    // + piece - 1, ahead of its partition slots (so nsub = nshf (SW - 1))
+    const int32_t SW = (k >= 2 && k * G > 16) ? a.wide_split : 1;
+    const int32_t nsub = nshf * (SW - 1), Tw = T / SW;
+    const int32_t nrows = in ? (leader ? nshf * SW : 0) + max(nfull - own_start, 0) : 0;
+    const int32_t count = in ? np + extra + nsub : 0;
     int2 tot;
     const int2 ex = block_exclusive_scan2(nrows, count, smem64, &tot);
     const int32_t r0 = row_base + ex.x, f0 = slot_base + ex.y;
     if (in) {
-      a.plan.seq_info[b] = make_int4(f0, count, np, 0);
+      a.plan.seq_info[b] = make_int4(f0, count, np, nsub);
       if (a.n_seqs > NT) a.plan.seq_pack[b] = make_int2(Ls, leader ? k : 0);  // for pass 2
+      const int32_t fp = f0 + nsub;  // slot of partition 0
       int32_t row = r0;
       if (leader)
-        for (int32_t j = 0; j < nshf; ++j, ++row)
-          if (row < a.max_units) {
-            a.plan.work[row] = make_int4(b, j * T, (j + 1) * T, k);
-            a.plan.work_out[row] = make_int2(f0 + j, count);
-          }
+        for (int32_t j = 0; j < nshf; ++j)
+          for (int32_t q = 0; q < SW; ++q, ++row)
+            if (row < a.max_units) {
+              const int32_t code = SW > 1 ? (q + 1) << 16 : 0;
+              a.plan.work[row] = make_int4(b, j * T + q * Tw, j * T + (q + 1) * Tw, k | code);
+              a.plan.work_out[row] = make_int2(q == 0 ? fp + j : f0 + j * (SW - 1) + q - 1, count);
+            }
       for (int32_t j = own_start; j < nfull; ++j, ++row)
         if (row < a.max_units) {
           a.plan.work[row] = make_int4(b, j * T, (j + 1) * T, 1);
-          a.plan.work_out[row] = make_int2(f0 + j, count);
+          a.plan.work_out[row] = make_int2(fp + j, count);
         }
-      short_units(T, L, Ls, leader ? k : 0, f0, [&](int32_t t0, int32_t t1, int32_t, int32_t) {
+      short_units(T, L, Ls, leader ? k : 0, fp, [&](int32_t t0, int32_t t1, int32_t, int32_t) {
         atomicAdd(&bucket[bucket_of(t1 - t0)], 1);
       });
       keep_L = L;
-      keep_first = f0;
+      keep_first = fp;
       keep_count = count;
       keep_Ls = Ls;
       keep_k = leader ? k : 0;
@@ -457,7 +476,7 @@ __global__ __launch_bounds__(NT) void plan_kernel(DecodeArgs a) {
         L = length_of(b, false);
         const int4 si = a.plan.seq_info[b];
         const int2 sp = a.plan.seq_pack[b];
-        first = si.x;
+        first = si.x + si.w;
         count = si.y;
         Ls = sp.x;
         kl = sp.y;
@@ -546,12 +565,18 @@ __device__ __forceinline__ void wide_pack_unit(const DecodeArgs& a, const Unit& 
   const int32_t t0 = u.t0, t1 = u.t1;
   const float c = a.scale_log2;
 
-  // per row: the partial slot and partial count of its member (the narrow
-  // pack path's column rule)
+  // per row: the partial slot and partial count of its member.  Piece q >= 1
+  // of shared partition j: slot first + j (SW - 1) + q - 1; otherwise the
+  // narrow pack path's column rule, after the member's nsub piece slots
   if (tid < rows) {
     const int4 si = a.plan.seq_info[u.b + tid / G];
-    const bool tail = (t1 & (T - 1)) != 0;
-    L.row_slot[tid] = si.x + (tail && si.y > si.z ? si.z : t0 / T);
+    const int32_t j = t0 / T;
+    if (u.piece >= 2) {
+      L.row_slot[tid] = si.x + j * (a.wide_split - 1) + u.piece - 2;
+    } else {
+      const bool tail = u.piece == 0 && (t1 & (T - 1)) != 0;
+      L.row_slot[tid] = si.x + si.w + (tail && si.y > si.w + si.z ? si.z : j);
+    }
     L.row_np[tid] = si.y;
   }
   // the first sequence's block ids of keys [t0, t1)
@@ -914,10 +939,11 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void decode_mfma_kernel(Dec
   if (u.pack > 1 && threadIdx.x < NC) {
     // a shared piece of partition j = t0 / T of every member: slot first + j,
     // except a tail (t1 % T != 0) of a member that continues past it, which
-    // goes to its extra slot first + partitions
+    // goes to its extra slot first + partitions (narrow packs hold no split
+    // pieces: si.w = 0)
     const int4 si = a.plan.seq_info[u.b + (int32_t)threadIdx.x / G];
     const bool tail = (u.t1 & (a.part_tokens - 1)) != 0;
-    col_slot[threadIdx.x] = si.x + (tail && si.y > si.z ? si.z : u.t0 / a.part_tokens);
+    col_slot[threadIdx.x] = si.x + si.w + (tail && si.y > si.w + si.z ? si.z : u.t0 / a.part_tokens);
     col_np[threadIdx.x] = si.y;
   }
 
@@ -1829,6 +1855,8 @@ struct Choice {
   int64_t max_units;
   bool need_partials;
   bool may_pack;  // sized for packs of sharing sequences (one extra slot per sequence)
+  bool wide;          // packs may be wide (dense product over up to kWideRows query rows)
+  int32_t wide_split; // pieces per whole shared partition of a wide pack
 };
 
 enum { kMathAuto, kMathValu, kMathMfma, kMathDpp, kMathGeneric };
@@ -1921,8 +1949,23 @@ int choose(int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t p, int32_
   out->kind = kind;
   out->waves_per_group = W;
   out->part_tokens = T;
-  // a split shared partition adds one slot (and one unit) per sequence
-  out->max_units = std::max<int64_t>(1, std::min(by_len, by_total)) + (may_pack ? n_seqs : 0);
+  // wide packs: four waves, blocks of 16, 32 or 64 tokens (a 16-key group in
+  // one block), units of at most kWideTab blocks
+  out->wide = may_pack && W == 4 && p % 16 == 0 && T / p <= kWideTab && !env_is("PKV_DECODE_WIDE", "off");
+  out->wide_split = 1;
+  if (out->wide) {
+    // pieces of at least one 64-key chunk.  Measured on 128 sequences sharing
+    // a 2048-token prefix (T = 2048, packs of 32): whole partitions 0.0756 ms,
+    // halves 0.0693, quarters 0.0729, eighths 0.0791 (more pieces, more
+    // partials to write and merge)
+    const int32_t want_split = std::max(1, env_int("PKV_WIDE_SPLIT", 2));
+    while (out->wide_split * 2 <= want_split && T / (out->wide_split * 2) >= 64) out->wide_split *= 2;
+  }
+  // a split shared partition adds one slot (and one unit) per sequence; the
+  // pieces of wide packs add wide_split - 1 per whole shared partition
+  const int64_t whole = std::min<int64_t>((int64_t)n_seqs * (L / T), total / T);
+  out->max_units = std::max<int64_t>(1, std::min(by_len, by_total)) + (may_pack ? n_seqs : 0) +
+                   (int64_t)(out->wide_split - 1) * whole;
   out->need_partials = T < L || may_pack;
   out->may_pack = may_pack;
   return PKV_OK;
@@ -2175,10 +2218,9 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     // (four waves, blocks of 16, 32 or 64 tokens, units of at most
     // kWideTab blocks) take up to 128 / G sequences, read with a dense product
     const int32_t G = num_q_heads / num_kv_heads;
-    const bool wide = c.waves_per_group == 4 && block_size % 16 == 0 &&
-                      c.part_tokens / block_size <= pkv::kWideTab && !pkv::env_is("PKV_DECODE_WIDE", "off");
-    a.pack_max = wide ? std::min(pkv::kWideMaxPack, pkv::kWideRows / G) : std::max(1, 16 / G);
+    a.pack_max = c.wide ? std::min(pkv::kWideMaxPack, pkv::kWideRows / G) : std::max(1, 16 / G);
   }
+  a.wide_split = a.pack_max > 1 && c.wide ? c.wide_split : 1;
   a.len_cap = std::min<int64_t>((int64_t)max_blocks_per_seq * block_size, max_context_len);
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.plan.counts = (int32_t*)(ws + lay.counts);
