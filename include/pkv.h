@@ -80,6 +80,8 @@ extern "C" {
 #define PKV_DEVERR_COPY_PAIR     4 /* copy_blocks pair outside [0, num_blocks)      */
 #define PKV_DEVERR_CONTEXT_LEN   8 /* context length < 0 or > table capacity       */
 #define PKV_DEVERR_WORK_OVERFLOW 16/* more partitions than the workspace was sized */
+#define PKV_DEVERR_PLAN          32/* planned decode: the workspace holds no plan for
+                                       this sizing (nothing was computed)          */
 
 typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
 
@@ -365,6 +367,45 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
                                float scale, pkv_dtype dtype,
                                pkv_layout k_layout, void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/* The decode split in two, for a step that attends several times over the
+ * same block tables and lengths (one call per model layer: "The Block Table
+ * Map" is per sequence, shared by every layer's cache).  pkv_decode_plan runs
+ * only the plan kernel of pkv_paged_attention_decode: it reads d_context_lens
+ * and d_shared_prev and writes the unit list into the workspace.
+ * pkv_paged_attention_decode_planned then runs the partition and merge
+ * kernels on that plan, any number of times; its result is bit-identical to
+ * pkv_paged_attention_decode with the same arguments.
+ *   Arguments: as pkv_paged_attention_decode.  The plan call takes the sizing
+ *          arguments (n_seqs, head counts, head_dim, block_size,
+ *          max_blocks_per_seq, max_context_len, total_context_tokens,
+ *          unshared_context_tokens, dtype), d_context_lens, d_shared_prev
+ *          (NULL or not) and the workspace; the planned call must pass the
+ *          same values, the same workspace, and context lengths and shared
+ *          counts unchanged since the plan ran (stream order).
+ *   Checks: the plan records a stamp of its sizing in the workspace; a
+ *          planned call whose sizing differs (or whose workspace holds no
+ *          plan) computes nothing, leaves out unwritten and sets
+ *          PKV_DEVERR_PLAN.  Changed lengths are not detected.  The planned
+ *          call needs 16-byte aligned q, out and caches when the shape takes
+ *          the matrix-core or DPP kernel (UNSUPPORTED otherwise).
+ * Errors: as pkv_paged_attention_decode. */
+int pkv_decode_plan(const int32_t* d_context_lens, const int32_t* d_shared_prev, int32_t n_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t max_blocks_per_seq, int32_t max_context_len,
+                    int64_t total_context_tokens, int64_t unshared_context_tokens,
+                    pkv_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+int pkv_paged_attention_decode_planned(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* d_block_table,
+                                       const int32_t* d_context_lens,
+                                       const int32_t* d_shared_prev, int32_t n_seqs,
+                                       int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                       int32_t max_blocks_per_seq, int32_t max_context_len,
+                                       int64_t total_context_tokens,
+                                       int64_t unshared_context_tokens, float scale,
+                                       pkv_dtype dtype, pkv_layout k_layout, void* workspace,
+                                       size_t workspace_bytes, void* stream);
 
 /* Decode without any device allocation, for callers that cannot allocate
  * (code under graph capture, tight serving loops, harnesses that forbid

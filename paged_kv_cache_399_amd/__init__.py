@@ -25,7 +25,8 @@ from ._lib import (DEVERR_CONTEXT_LEN, DEVERR_COPY_PAIR, DEVERR_SLOT,  # noqa: F
 lib = _lib.load()
 
 __all__ = ["PkvError", "BlockPool", "cache_append", "copy_blocks", "decode_workspace_bytes",
-           "paged_attention_decode", "paged_attention_decode_noalloc", "paged_attention_prefill",
+           "paged_attention_decode", "paged_attention_decode_noalloc", "decode_plan",
+           "paged_attention_decode_planned", "paged_attention_prefill",
            "check_device_errors", "version", "lib", "DECODE_SCRATCH_BYTES"]
 
 
@@ -319,6 +320,64 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_table, context_lens,
     if workspace.numel() < need:
         raise ValueError(f"workspace has {workspace.numel()} bytes, {need} needed")
     _check(lib.pkv_paged_attention_decode(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_table, "block_table"), _dev(context_lens, "context_lens"),
+        None if shared_prev is None else _dev(shared_prev, "shared_prev"), b, hq, hkv, d, bs,
+        nb, block_table.shape[1], int(max_context_len), int(total_context_tokens),
+        int(unshared_context_tokens), 0.0 if scale is None else float(scale),
+        _dtype_code(q), lay, _dev(workspace, "workspace"), workspace.numel(),
+        _stream_ptr(stream)))
+    return out
+
+
+def decode_plan(context_lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                block_size: int, max_blocks_per_seq: int, max_context_len: int,
+                total_context_tokens: int = -1, workspace=None, dtype=None, stream=None,
+                shared_prev=None, unshared_context_tokens: int = -1):
+    """The plan kernel of a decode alone: writes the unit list for these sizing
+    arguments and the current context lengths into ``workspace`` (required),
+    for paged_attention_decode_planned calls with the same arguments."""
+    import torch
+    if workspace is None:
+        raise ValueError("decode_plan needs the workspace the planned decode will use")
+    if context_lens.dtype != torch.int32:
+        raise ValueError("context_lens must be int32 [n_seqs]")
+    b = context_lens.numel()
+    if shared_prev is not None and (shared_prev.dtype != torch.int32 or shared_prev.numel() != b):
+        raise ValueError("shared_prev must be int32 [n_seqs]")
+    dt = torch.bfloat16 if dtype is None else dtype
+    need = decode_workspace_bytes(b, num_q_heads, num_kv_heads, head_dim, block_size,
+                                  max_context_len, total_context_tokens, dt,
+                                  unshared_context_tokens)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace has {workspace.numel()} bytes, {need} needed")
+    code = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}.get(dt)
+    if code is None:
+        raise TypeError(f"unsupported dtype {dt}")
+    _check(lib.pkv_decode_plan(
+        _dev(context_lens, "context_lens"),
+        None if shared_prev is None else _dev(shared_prev, "shared_prev"), b, int(num_q_heads),
+        int(num_kv_heads), int(head_dim), int(block_size), int(max_blocks_per_seq),
+        int(max_context_len), int(total_context_tokens), int(unshared_context_tokens), code,
+        _dev(workspace, "workspace"), workspace.numel(), _stream_ptr(stream)))
+
+
+def paged_attention_decode_planned(out, q, k_cache, v_cache, block_table, context_lens,
+                                   max_context_len: int, total_context_tokens: int = -1,
+                                   scale: Optional[float] = None, workspace=None, stream=None,
+                                   layout="head_major", shared_prev=None,
+                                   unshared_context_tokens: int = -1):
+    """paged_attention_decode without its plan kernel: ``workspace`` (required)
+    holds the plan decode_plan wrote for the same sizing arguments and lengths."""
+    if workspace is None:
+        raise ValueError("a planned decode needs the workspace decode_plan wrote")
+    b, hq, hkv, d, bs, nb, lay = _decode_common(out, q, k_cache, v_cache, block_table,
+                                                context_lens, shared_prev, layout)
+    need = decode_workspace_bytes(b, hq, hkv, d, bs, max_context_len, total_context_tokens,
+                                  q.dtype, unshared_context_tokens)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace has {workspace.numel()} bytes, {need} needed")
+    _check(lib.pkv_paged_attention_decode_planned(
         _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(block_table, "block_table"), _dev(context_lens, "context_lens"),
         None if shared_prev is None else _dev(shared_prev, "shared_prev"), b, hq, hkv, d, bs,

@@ -22,6 +22,7 @@ DEVERR_SLOT = 2
 DEVERR_COPY_PAIR = 4
 DEVERR_CONTEXT_LEN = 8
 DEVERR_WORK_OVERFLOW = 16
+DEVERR_PLAN = 32
 
 F32 = 0
 BF16 = 1
@@ -64,6 +65,12 @@ SIGNATURES = {
     "pkv_paged_attention_decode": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                              _i32, _i32, _i32, _i32, _i64, _i64, C.c_float, C.c_int,
                                              C.c_int, _vp, C.c_size_t, _vp]),
+    "pkv_decode_plan": (C.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i64,
+                                  C.c_int, _vp, C.c_size_t, _vp]),
+    "pkv_paged_attention_decode_planned": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                                     _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i64,
+                                                     C.c_float, C.c_int, C.c_int, _vp, C.c_size_t,
+                                                     _vp]),
     "pkv_paged_attention_decode_noalloc": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                                      _i32, _i32, _i32, _i32, _i32, _i32, _i64,
                                                      _i64, C.c_float, C.c_int, C.c_int, _vp]),

@@ -71,7 +71,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct Plan {
-  int32_t* counts;     // [0] units to run (0 if the plan overflowed), [1] full-length units
+  int32_t* counts;     // [0] units to run (0 if the plan overflowed), [1] full-length units,
+                       // [2], [3] the sizing stamp of the call that planned
   int4* seq_info;      // [n_seqs]: (first slot, partials, partitions, leading piece slots);
                        // slots are contiguous
   int2* seq_pack;      // [n_seqs]: (tokens its pack shares or 0, pack size if it leads a pack
@@ -97,6 +98,7 @@ struct DecodeArgs {
   KStrides ks;       // key cache: elements between KV heads, between tokens
   int64_t len_cap;   // min(max_blocks * p, max_context_len): longer contexts are clamped
   float scale_log2;  // scale * log2(e): scores are kept in log2 units
+  int2 stamp;        // the plan's sizing (partition length, units, packs), hashed on the host
   Plan plan;
   int32_t* err;
 };
@@ -190,8 +192,19 @@ struct Unit {
   int32_t b, t0, t1, pack, piece, slot, nparts, valid;
 };
 
+// A plan made for other sizing (a planned decode whose workspace holds
+// another call's plan) runs nothing and is flagged.
+__device__ __forceinline__ bool plan_matches(const DecodeArgs& a) {
+  return a.plan.counts[2] == a.stamp.x && a.plan.counts[3] == a.stamp.y;
+}
+
 __device__ __forceinline__ Unit decode_unit(const DecodeArgs& a, int32_t unit) {
   Unit u;
+  if (!plan_matches(a)) {
+    if (unit == 0 && threadIdx.x == 0) atomicOr(a.err, PKV_DEVERR_PLAN);
+    u.valid = false;
+    return u;
+  }
   u.valid = unit < a.plan.counts[0];
   if (!u.valid) return u;
   const int4 w = a.plan.work[unit];
@@ -494,6 +507,8 @@ __global__ __launch_bounds__(NT) void plan_kernel(DecodeArgs a) {
     if (overflow) atomicOr(a.err, PKV_DEVERR_WORK_OVERFLOW);
     a.plan.counts[0] = overflow ? 0 : F + R;  // run nothing rather than overlapping rows
     a.plan.counts[1] = F;
+    a.plan.counts[2] = a.stamp.x;
+    a.plan.counts[3] = a.stamp.y;
   }
 }
 
@@ -1691,6 +1706,7 @@ __global__ __launch_bounds__(1024) void merge_kernel(DecodeArgs a) {
   const int32_t g = blockIdx.x - b * a.hkv;
   const int4 si = a.plan.seq_info[b];
   const int32_t f0 = si.x, n = si.y;
+  if (!plan_matches(a)) return;       // another call's plan (flagged by the partition kernel)
   if (n <= 1) return;                 // uniform
   if (a.plan.counts[0] == 0) return;  // plan overflowed
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -1981,7 +1997,7 @@ Layout layout_of(int32_t n_seqs, int32_t hq, int32_t d, const Choice& c) {
   Layout l;
   size_t off = 0;
   l.counts = off;
-  off = align256(off + 2 * sizeof(int32_t));
+  off = align256(off + 4 * sizeof(int32_t));
   l.seq_info = off;
   off = align256(off + (size_t)n_seqs * sizeof(int4));
   l.seq_pack = off;
@@ -2135,6 +2151,26 @@ int scratch_address(void** out) {
   return PKV_OK;
 }
 
+// The plan's sizing stamp: every input of the plan kernel except the device
+// lengths and shared counts (FNV-1a over them; never zero in both words).
+int2 plan_stamp(const Choice& c, const DecodeArgs& a) {
+  const int64_t v[] = {a.n_seqs, a.hq, a.hkv, a.part_tokens, a.max_units, a.pack_max,
+                       a.wide_split, c.kind, a.len_cap, a.shared ? 1 : 0};
+  uint64_t h = 1469598103934665603ull;
+  for (int64_t x : v)
+    for (int i = 0; i < 8; ++i) {
+      h ^= (uint64_t)(x >> (8 * i)) & 0xff;
+      h *= 1099511628211ull;
+    }
+  return make_int2((int32_t)(uint32_t)(h >> 32), (int32_t)((uint32_t)h | 1u));
+}
+
+enum DecodeMode {
+  kPlanAndRun,  // plan, partition, merge (pkv_paged_attention_decode)
+  kPlanOnly,    // plan into the workspace (pkv_decode_plan)
+  kRunPlanned,  // partition and merge on the workspace's plan (pkv_paged_attention_decode_planned)
+};
+
 // The decode call proper.  With use_scratch the workspace arguments are
 // ignored and the current device's library scratch is used instead.
 int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -2143,9 +2179,11 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                 int32_t max_blocks_per_seq, int32_t max_context_len, int64_t total_context_tokens,
                 int64_t unshared_context_tokens, float scale, pkv_dtype dtype, pkv_layout k_layout,
-                void* workspace, size_t workspace_bytes, bool use_scratch, void* stream) {
+                void* workspace, size_t workspace_bytes, bool use_scratch, DecodeMode mode,
+                void* stream) {
+  const bool plan_only = mode == kPlanOnly;
   if (n_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-      num_blocks <= 0 || max_blocks_per_seq < 0 || max_context_len < 0)
+      (!plan_only && num_blocks <= 0) || max_blocks_per_seq < 0 || max_context_len < 0)
     return fail(PKV_ERR_INVALID_ARG, "bad sizes");
   if (num_q_heads % num_kv_heads) return fail(PKV_ERR_INVALID_ARG, "num_q_heads is not a multiple of num_kv_heads");
   if (num_q_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "more than 65535 query heads");
@@ -2154,7 +2192,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   if (!pkv::resolve_scale(&scale, head_dim))
     return fail(PKV_ERR_INVALID_ARG, "scale must be 0 (1/sqrt(head_dim)) or finite and positive");
   if (n_seqs == 0) return PKV_OK;
-  if (!out || !q || !k_cache || !v_cache || !d_context_lens || (max_blocks_per_seq > 0 && !d_block_table))
+  if (!d_context_lens ||
+      (!plan_only && (!out || !q || !k_cache || !v_cache || (max_blocks_per_seq > 0 && !d_block_table))))
     return fail(PKV_ERR_INVALID_ARG, "NULL pointer");
   if ((int64_t)max_blocks_per_seq * block_size < max_context_len)
     return fail(PKV_ERR_INVALID_ARG, "max_context_len exceeds the block-table capacity");
@@ -2162,11 +2201,11 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   int rc = pkv::choose(n_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
                        total_context_tokens, unshared_context_tokens, dtype, &c);
   if (rc) return rc;
-  if (c.kind != pkv::kKindGeneric) {
+  if (c.kind != pkv::kKindGeneric && !plan_only) {
     const uintptr_t mis = (uintptr_t)out | (uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache;
     if (mis % 16) {
-      const int mode = pkv::math_mode();
-      if (mode == pkv::kMathMfma || mode == pkv::kMathDpp)
+      const int math = pkv::math_mode();
+      if (math == pkv::kMathMfma || math == pkv::kMathDpp || mode == kRunPlanned)
         return fail(PKV_ERR_UNSUPPORTED, "this decode kernel needs 16-byte aligned buffers");
       // same partition length and workspace; the generic kernel takes any
       c.kind = pkv::kKindGeneric;
@@ -2231,13 +2270,21 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.plan.part_ml = c.need_partials ? (float*)(ws + lay.part_ml) : nullptr;
   a.plan.part_o = c.need_partials ? (float*)(ws + lay.part_o) : nullptr;
   a.err = err;
+  a.stamp = plan_stamp(c, a);
 
   hipStream_t st = (hipStream_t)stream;
-  // fewer plan threads finish sooner (fewer waves per SIMD on one compute unit)
-  if (n_seqs <= 64) hipLaunchKernelGGL(pkv::plan_kernel<64>, dim3(1), dim3(64), 0, st, a);
-  else if (n_seqs <= 128) hipLaunchKernelGGL(pkv::plan_kernel<128>, dim3(1), dim3(128), 0, st, a);
-  else if (n_seqs <= 256) hipLaunchKernelGGL(pkv::plan_kernel<256>, dim3(1), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(pkv::plan_kernel<pkv::kPlanThreads>, dim3(1), dim3(pkv::kPlanThreads), 0, st, a);
+  if (mode != kRunPlanned) {
+    // fewer plan threads finish sooner (fewer waves per SIMD on one compute unit)
+    if (n_seqs <= 64) hipLaunchKernelGGL(pkv::plan_kernel<64>, dim3(1), dim3(64), 0, st, a);
+    else if (n_seqs <= 128) hipLaunchKernelGGL(pkv::plan_kernel<128>, dim3(1), dim3(128), 0, st, a);
+    else if (n_seqs <= 256) hipLaunchKernelGGL(pkv::plan_kernel<256>, dim3(1), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(pkv::plan_kernel<pkv::kPlanThreads>, dim3(1), dim3(pkv::kPlanThreads), 0, st, a);
+  }
+  if (plan_only) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode plan launch: %s", hipGetErrorString(e));
+    return PKV_OK;
+  }
   const int64_t waves = c.max_units * num_kv_heads;
   if (c.kind == pkv::kKindMfma) {
     const int32_t W = c.waves_per_group;
@@ -2281,7 +2328,38 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, const void* 
                           n_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                           max_blocks_per_seq, max_context_len, total_context_tokens,
                           unshared_context_tokens, scale, dtype, k_layout, workspace,
-                          workspace_bytes, false, stream);
+                          workspace_bytes, false, pkv::kPlanAndRun, stream);
+  PKV_TRY_END
+}
+
+extern "C" int pkv_decode_plan(const int32_t* d_context_lens, const int32_t* d_shared_prev,
+                               int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                               int32_t max_context_len, int64_t total_context_tokens,
+                               int64_t unshared_context_tokens, pkv_dtype dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  PKV_TRY_BEGIN
+  return pkv::decode_impl(nullptr, nullptr, nullptr, nullptr, nullptr, d_context_lens, d_shared_prev,
+                          n_seqs, num_q_heads, num_kv_heads, head_dim, block_size, 0,
+                          max_blocks_per_seq, max_context_len, total_context_tokens,
+                          unshared_context_tokens, 0.f, dtype, PKV_LAYOUT_HEAD_MAJOR, workspace,
+                          workspace_bytes, false, pkv::kPlanOnly, stream);
+  PKV_TRY_END
+}
+
+extern "C" int pkv_paged_attention_decode_planned(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* d_block_table, const int32_t* d_context_lens, const int32_t* d_shared_prev,
+    int32_t n_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+    int64_t total_context_tokens, int64_t unshared_context_tokens, float scale, pkv_dtype dtype,
+    pkv_layout k_layout, void* workspace, size_t workspace_bytes, void* stream) {
+  PKV_TRY_BEGIN
+  return pkv::decode_impl(out, q, k_cache, v_cache, d_block_table, d_context_lens, d_shared_prev,
+                          n_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                          max_blocks_per_seq, max_context_len, total_context_tokens,
+                          unshared_context_tokens, scale, dtype, k_layout, workspace,
+                          workspace_bytes, false, pkv::kRunPlanned, stream);
   PKV_TRY_END
 }
 
@@ -2296,6 +2374,7 @@ extern "C" int pkv_paged_attention_decode_noalloc(
   return pkv::decode_impl(out, q, k_cache, v_cache, d_block_table, d_context_lens, d_shared_prev,
                           n_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                           max_blocks_per_seq, max_context_len, total_context_tokens,
-                          unshared_context_tokens, scale, dtype, k_layout, nullptr, 0, true, stream);
+                          unshared_context_tokens, scale, dtype, k_layout, nullptr, 0, true,
+                          pkv::kPlanAndRun, stream);
   PKV_TRY_END
 }

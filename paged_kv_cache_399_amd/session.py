@@ -19,8 +19,8 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-from . import (BlockPool, cache_append, copy_blocks, decode_workspace_bytes,
-               paged_attention_decode, paged_attention_prefill)
+from . import (BlockPool, cache_append, copy_blocks, decode_plan, decode_workspace_bytes,
+               paged_attention_decode, paged_attention_decode_planned, paged_attention_prefill)
 
 
 def _poison_value(dtype):
@@ -147,15 +147,26 @@ class PagedKVCache:
                                                           d_shared_prev=m.shared)
         m.uploaded = True
 
-    def attend(self, m, q, out, scale=None, stream=None):
+    def attend(self, m, q, out, scale=None, stream=None, planned=False):
+        """Decode attention for the batch; planned=True reuses the plan that
+        plan(m) made for the current lengths (e.g. every layer of one step)."""
         if m.max_len > m.ws_max_len or m.total > m.ws_total:
             raise ValueError("batch outgrew the workspace sized in prepare()")
         # the sizing hints stay the prepared ones, so the partition size (and
         # with it the summation order) is fixed for the life of the batch
-        return paged_attention_decode(out, q, self.k_cache, self.v_cache, m.table, m.lens,
-                                      m.ws_max_len, m.ws_total, scale, m.workspace, stream,
-                                      self.layout, shared_prev=m.shared,
-                                      unshared_context_tokens=m.ws_unshared)
+        fn = paged_attention_decode_planned if planned else paged_attention_decode
+        return fn(out, q, self.k_cache, self.v_cache, m.table, m.lens, m.ws_max_len, m.ws_total,
+                  scale, m.workspace, stream, self.layout, shared_prev=m.shared,
+                  unshared_context_tokens=m.ws_unshared)
+
+    def plan(self, m, stream=None):
+        """Plan the decode of the batch's current lengths once (decode_plan);
+        attend(..., planned=True) then skips the plan kernel."""
+        if m.max_len > m.ws_max_len or m.total > m.ws_total:
+            raise ValueError("batch outgrew the workspace sized in prepare()")
+        decode_plan(m.lens, m.num_q_heads, self.num_kv_heads, self.head_dim, self.block_size,
+                    m.max_blocks, m.ws_max_len, m.ws_total, m.workspace, self.dtype, stream,
+                    shared_prev=m.shared, unshared_context_tokens=m.ws_unshared)
 
     def capture_attend(self, m, q, out, scale=None):
         """Record one decode call (plan, partition, merge kernels) into a HIP graph.

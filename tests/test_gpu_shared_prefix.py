@@ -289,6 +289,21 @@ def test_more_sequences_than_one_plan_pass(monkeypatch):
     kv.close()
 
 
+def test_wide_pack_pieces_across_plan_passes(monkeypatch):
+    """1120 sequences in fork groups of 40 at G = 4 (wide packs of 32 and 8
+    sequences) sharing 300 or 320 tokens at T = 128: every pack's whole shared
+    partitions are cut into 64-token pieces with their own partial slots, a
+    shared tail follows, and packs cross the plan's 1024-sequence passes (the
+    second pass reads each member's piece-slot count back)."""
+    monkeypatch.setenv("PKV_PARTITION_TOKENS", "128")
+    groups = [(300 + (i % 2) * 20, [(i + j) % 5 for j in range(40)]) for i in range(28)]
+    kv, batch, keys, vals = _forest(groups, 2, 64, 16, seed=77)
+    assert len(batch) == 1120
+    worst, most = _step_and_check(kv, batch, keys, vals, 8, seed=77, steps=1, t=128)
+    say(f"  1120 sequences: max shared {most}, max err {worst:.3e}")
+    kv.close()
+
+
 @pytest.mark.parametrize("groups_n", [22, 67, 90])
 def test_packs_across_plan_sizes(monkeypatch, groups_n):
     """Fork groups of three in batches of 66, 201 and 270 sequences: packs and
