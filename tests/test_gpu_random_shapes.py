@@ -4,7 +4,8 @@ Each case draws a dtype, a head grouping, head_dim, block size, key layout,
 partition length, decode kernel (automatic or forced, among those that take
 the shape) and a batch of context lengths, then checks slots and both caches
 bit for bit and attention against float64 through the library's whole decode
-step.  The draws are fixed by the case number, so a failure names its case.
+step, and the same decode split into a plan and a planned call (bit-identical).
+The draws are fixed by the case number, so a failure names its case.
 """
 import numpy as np
 import pytest
@@ -80,6 +81,15 @@ def test_random_decode_case(monkeypatch, case):
     assert np.array_equal(np.ascontiguousarray(host_bits(kc_case.kv.k_cache)).view(view), kc.view(view))
     assert np.array_equal(np.ascontiguousarray(host_bits(kc_case.kv.v_cache)).view(view), vc.view(view))
     err = check_attention(kc_case)
+    # the same decode split into plan + planned call, on a workspace cleared of
+    # the full call's plan: bit-identical
+    kv, m = kc_case.kv, kc_case.meta
+    m.workspace.zero_()
+    kv.plan(m)
+    out_p = torch.full_like(kc_case.w.q, float("nan"))
+    kv.attend(m, kc_case.w.q, out_p, planned=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out_p, kc_case.out), "planned decode differs from the full call"
     say(f"  case {case}: max err {err:.3e}")
 
 
