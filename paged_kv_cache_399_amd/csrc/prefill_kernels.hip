@@ -259,10 +259,18 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   // one wave's 16-key group of a chunk: the block holding keys [kb, kb + 16),
   // or for a group past the context end the last group that holds keys (in
   // bounds; zeroed with the boundary mask)
-  auto group_base = [&](int32_t c0, int64_t& off) -> int32_t {
+  // (direct: the entry read from the table row itself, for the first chunks,
+  // staged before the table window is in LDS)
+  auto group_base = [&](int32_t c0, int64_t& off, bool direct = false) -> int32_t {
     const int32_t kb = c0 + 16 * w;  // uniform
     const int32_t kl = min(kb, kend - 1) & ~15;
-    const int32_t blk = __builtin_amdgcn_readfirstlane(tab[(kl >> lp) - wb]);
+    int32_t blk;
+    if (direct) {
+      blk = __builtin_amdgcn_readfirstlane(trow[kl >> lp]);
+      if ((uint32_t)blk >= (uint32_t)a.num_blocks) blk = 0;  // flagged by the window load
+    } else {
+      blk = __builtin_amdgcn_readfirstlane(tab[(kl >> lp) - wb]);
+    }
     off = (int64_t)blk * blk_stride;
     return kl & (P - 1);  // offset of the group inside its block
   };
@@ -288,18 +296,18 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   auto vslot = [&](int vbuf, int u) -> uint16_t* {   // instruction u's LDS run
     return &v_lds[vbuf][((2 * w + u / VPG) * D + (u % VPG) * 64) * 8];
   };
-  auto kload_direct = [&](int32_t c0, int kbuf) {
+  auto kload_direct = [&](int32_t c0, int kbuf, bool direct = false) {
     int64_t boff;
-    const int32_t o = group_base(c0, boff);
+    const int32_t o = group_base(c0, boff, direct);
     const char* kbase = (const char*)(kc + boff + khead + (int64_t)o * a.ks.tok);
 #pragma unroll
     for (int u = 0; u < KU; ++u)
       __builtin_amdgcn_global_load_lds((gptr_t)(kbase + kdoff[u]),
                                        (lds_ptr_t)&k_lds[kbuf][(16 * w + u * KR) * KS], 16, 0, 0);
   };
-  auto vload_direct = [&](int32_t c0, int vbuf) {
+  auto vload_direct = [&](int32_t c0, int vbuf, bool direct = false) {
     int64_t boff;
-    const int32_t o = group_base(c0, boff);
+    const int32_t o = group_base(c0, boff, direct);
     const char* vbase = (const char*)(vc + boff + vhead + o);
 #pragma unroll
     for (int u = 0; u < VU; ++u)
@@ -446,6 +454,13 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     }
   };
 
+  if constexpr (WB) {
+    // the first chunks' blocks straight from the table row, so their loads
+    // are in flight while the table window is brought into LDS
+    kload_direct(0, 0, true);
+    vload_direct(0, 0, true);
+    if (nchunks > 1) kload_direct(CH, 1, true);
+  }
   load_tab(0);
   __syncthreads();
   if constexpr (WB) {
@@ -611,9 +626,6 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
       }
     };
 
-    kload_direct(0, 0);
-    vload_direct(0, 0);
-    if (nchunks > 1) kload_direct(CH, 1);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
     vfix(0, 0);
     __syncthreads();
