@@ -45,12 +45,17 @@ def _q_like(q, rng):
     return torch.from_numpy(rng.standard_normal(tuple(q.shape)).astype(np.float32)).to(q.dtype).to(q.device)
 
 
-@pytest.mark.parametrize("name,forced_t", [("tiny", None), ("small_mha", None), ("gqa", None),
-                                           ("gqa", 128), ("prefix", None), ("prefix", 256)])
-def test_planned_layers_equal_the_full_decode(monkeypatch, name, forced_t):
+@pytest.mark.parametrize("name,forced_t,math", [
+    ("tiny", None, None),          # fp32: generic kernel
+    ("small_mha", None, None),     # multi-head bf16: matrix cores
+    ("small_mha", None, "dpp"),    # the DPP kernel
+    ("gqa", None, None), ("gqa", 128, None), ("prefix", None, None), ("prefix", 256, None)])
+def test_planned_layers_equal_the_full_decode(monkeypatch, name, forced_t, math):
     import torch
     if forced_t:
         monkeypatch.setenv("PKV_PARTITION_TOKENS", str(forced_t))
+    if math:
+        monkeypatch.setenv("PKV_DECODE_MATH", math)
     case = build_case(CONFIGS[name], seed=3)
     worst = check_attention(case)
     kv, w = case.kv, case.w
@@ -73,7 +78,7 @@ def test_planned_layers_equal_the_full_decode(monkeypatch, name, forced_t):
             kv.attend(m, q, o)
             torch.cuda.synchronize()
             assert torch.equal(planned[i], o), f"step {step}, layer {i}: planned decode differs"
-    say(f"  {name} T={forced_t}: {layers} layers x 2 steps bit-identical; max err {worst:.3e}")
+    say(f"  {name} T={forced_t} math={math}: {layers} layers x 2 steps bit-identical; max err {worst:.3e}")
     kv.close()
 
 
