@@ -668,7 +668,9 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
             lsum[t] *= alpha;
           }
         }
+        __builtin_amdgcn_s_setprio(1);  // value products issue first on this SIMD
         values(ci & 1, pb);
+        __builtin_amdgcn_s_setprio(0);
       }
       __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
       if (more) vfix(c0 + CH, (ci + 1) & 1);
