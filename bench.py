@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=DEFAULT_STEPS)
     ap.add_argument("--warmup", type=int, default=DEFAULT_WARMUP)
-    ap.add_argument("--config", default="long", help="tiny|small_mha|gqa|long|prefix|beam|prefill|prefill_chunk|admission|admission_small")
+    ap.add_argument("--config", default="long", help="tiny|small_mha|gqa|long|prefix|mha|beam|prefill|prefill_chunk|admission|admission_small")
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--layout", default="head_major", choices=["head_major", "token_major"],
                     help="key cache order inside a block: [Hkv, P, D] or [P, Hkv, D]")

@@ -86,6 +86,10 @@ CONFIGS: Dict[str, DecodeConfig] = {
                          length_lo=16, length_hi=32768),
     "prefix": DecodeConfig("prefix", 128, 32, 8, 128, 16, "bf16", "prefix",
                            length_lo=1, length_hi=1024, prefix_len=2048),
+    # multi-head attention (no head sharing) at the GQA workload's lengths: 64
+    # sequences, 32 query and 32 KV heads of 128 dims
+    "mha": DecodeConfig("mha", 64, 32, 32, 128, 16, "bf16", "uniform",
+                        length_lo=128, length_hi=4096),
 }
 
 

@@ -55,6 +55,18 @@ def test_small_configs_bit_exact_cache_and_attention(name):
     say(f"  max err {err:.3e}")
 
 
+def test_mha_workload_every_sequence():
+    """The multi-head workload (64 sequences, 32/32 heads, D = 128, lengths
+    U[128, 4096]) on the matrix-core kernel: slots bit-exact against the
+    oracle pool model, every output of every sequence against float64."""
+    case = build_case(CONFIGS["mha"], seed=0)
+    _, pre, dec, _, _ = oracle_slots(case.cfg, case.w)
+    assert np.array_equal(case.prefill_slots, pre)
+    assert np.array_equal(case.decode_slots, dec)
+    err = check_attention(case)
+    say(f"  mha: 64 of 64 sequences, max err {err:.3e}")
+
+
 def test_tiny_single_token_sequence_returns_its_value():
     case = build_case(CONFIGS["tiny"], seed=0)
     # sequence 0 has length 1: its output is its only value vector, exactly
