@@ -550,17 +550,23 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     // share of the exponentials.  A scheduling fence after every segment
     // keeps the order, so the matrix core works on the next chunk while the
     // vector ALU works on this one.
-    auto fused = [&](int kbuf, Sc& nx, const Sc& cu, bf16x8 (&pb)[2][NH]) -> bool {
-      constexpr int NSEG = NH * KI;
-      constexpr int NE = 2 * NH * 8;  // probabilities per lane per chunk
+    // key fragments of one chunk for the fused step: segment k's pair
+    constexpr int NSEG = NH * KI;
+    struct Kf {
+      bf16x8 x[NSEG], y[NSEG];
+    };
+    auto kread = [&](int kbuf, Kf& f, int k) {
       const uint16_t* kl = k_lds[kbuf];
-      bf16x8 ax[NSEG], ay[NSEG];
-      auto kread = [&](int k) {
-        const int h = k / KI, i = k % KI;
-        const int cb = ((4 * i + r) ^ kx) * 8;
-        ax[k] = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x) * KS + cb]);
-        ay[k] = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x + 4) * KS + cb]);
-      };
+      const int h = k / KI, i = k % KI;
+      const int cb = ((4 * i + r) ^ kx) * 8;
+      f.x[k] = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x) * KS + cb]);
+      f.y[k] = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x + 4) * KS + cb]);
+    };
+    // (the caller has read segment 0 into kf)
+    auto fused = [&](int kbuf, Kf& kf, Sc& nx, const Sc& cu, bf16x8 (&pb)[2][NH]) -> bool {
+      constexpr int NE = 2 * NH * 8;  // probabilities per lane per chunk
+      bf16x8 (&ax)[NSEG] = kf.x;
+      bf16x8 (&ay)[NSEG] = kf.y;
       auto kmfma = [&](int k) {
         const int h = k / KI, i = k % KI;
 #pragma unroll
@@ -590,11 +596,10 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
         const float sv = xy ? cu.y[t][h][e] : cu.x[t][h][e];
         pb[t][h][e + 4 * xy] = (__bf16)fast_exp2(fmaf(sv, c, -mc[t]));
       };
-      kread(0);
-      if (NSEG > 1) kread(1);
+      if (NSEG > 1) kread(kbuf, kf, 1);
 #pragma unroll
       for (int k = 0; k < NSEG; ++k) {
-        if (k + 2 < NSEG) kread(k + 2);
+        if (k + 2 < NSEG) kread(kbuf, kf, k + 2);
         kmfma(k);
         if (k < 2) {
           rowmax(k);
@@ -607,22 +612,38 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
       }
       return moved;
     };
+    // Value products of one chunk.  The value fragments are read VA head_dim
+    // tiles ahead of their products, in a fixed order (a scheduling fence
+    // after every tile), so each LDS read has the products of the tiles
+    // before it to hide behind; left to itself the compiler reuses one
+    // register quad and waits for every read.  The row sums need no fragment
+    // and cover the first reads.
     auto values = [&](int vbuf, const bf16x8 (&pb)[2][NH]) {
+      constexpr int VA = 3;
       const uint16_t* vl = v_lds[vbuf];
+      bf16x8 av[NJ][NH];
+      auto vread = [&](int j) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+          av[j][h] = *reinterpret_cast<const bf16x8*>(&vl[((4 * h + r) * D + 16 * j + nq) * 8]);
+      };
+#pragma unroll
+      for (int j = 0; j < VA && j < NJ; ++j) vread(j);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int h = 0; h < NH; ++h)
           lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[t][h], lsum[t], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
+        if (j + VA < NJ) vread(j + VA);
 #pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(&vl[((4 * h + r) * D + 16 * j + nq) * 8]);
+        for (int h = 0; h < NH; ++h)
 #pragma unroll
           for (int t = 0; t < 2; ++t)
-            acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[t][h], acc[t][j], 0, 0, 0);
-        }
+            acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[j][h], pb[t][h], acc[t][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
 
@@ -642,14 +663,19 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
         load_tab(wb);
         __syncthreads();
       }
+      // the next chunk's first key fragments are read before this step's
+      // loads are issued, so their LDS latency passes while those wait to issue
+      const bool fuse = c0 < wave_kend && more && c0 + CH < wave_kend;  // uniform
+      Kf kf;
+      if (fuse) kread((ci + 1) & 1, kf, 0);
       if (more2) kload_direct(c0 + 2 * CH, ci & 1);
       if (more) vload_direct(c0 + CH, (ci + 1) & 1);
       if (c0 < wave_kend) {  // uniform over the wave
         mask(cur, c0);
         bf16x8 pb[2][NH];
         bool moved;
-        if (more && c0 + CH < wave_kend) {  // uniform
-          moved = fused((ci + 1) & 1, nxt, cur, pb);
+        if (fuse) {
+          moved = fused((ci + 1) & 1, kf, nxt, cur, pb);
         } else {
           moved = softmax(cur, pb);
         }
