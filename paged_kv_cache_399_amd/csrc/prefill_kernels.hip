@@ -583,11 +583,16 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
         for (int h = 0; h < NH; ++h)
 #pragma unroll
           for (int e = 0; e < 4; ++e) x = fmaxf(x, fmaxf(cu.x[t][h][e], cu.y[t][h][e]));
-        const float cm = pair_max16(pair_max32(x));
-        const bool up = (cm - m_run[t]) * c > kRefSlack;
+        // the column's maximum over its four lanes is needed only where the
+        // reference moves: tested on each lane's own maximum first (a rare,
+        // uniform branch)
         m_old[t] = m_run[t];
-        m_run[t] = up ? fmaxf(m_run[t], cm) : m_run[t];
-        moved |= up;
+        if (__builtin_amdgcn_ballot_w64((x - m_run[t]) * c > kRefSlack) != 0) {
+          const float cm = pair_max16(pair_max32(x));
+          const bool up = (cm - m_run[t]) * c > kRefSlack;
+          m_run[t] = up ? fmaxf(m_run[t], cm) : m_run[t];
+          moved |= up;
+        }
         mc[t] = m_run[t] * c;
       };
       // probability q (q = ((t * NH + h) * 2 + xy) * 4 + e) of this lane
