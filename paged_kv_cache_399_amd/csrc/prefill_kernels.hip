@@ -686,8 +686,6 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
         load_tab(wb);
         __syncthreads();
       }
-      // the next chunk's first key fragments are read before this step's
-      // loads are issued, so their LDS latency passes while those wait to issue
       const bool fuse = c0 < wave_kend && more && c0 + CH < wave_kend;  // uniform
       Kf kf;
       if (more2) kload_direct(c0 + 2 * CH, ci & 1);
