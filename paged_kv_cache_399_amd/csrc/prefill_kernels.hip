@@ -175,16 +175,6 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     for (int i = 0; i < KI; ++i)
       qf[t][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qrow + 32 * i));
   }
-  if constexpr (WB) {
-    // WB: queries pre-scaled by scale * log2(e) (rounded to bf16), so scores
-    // come out in log2 units and the exponent argument needs no multiply
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < KI; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[t][i][e] = (__bf16)((float)qf[t][i][e] * c);
-  }
 
   const uint16_t* kc = (const uint16_t*)a.kc;
   const uint16_t* vc = (const uint16_t*)a.vc;
@@ -523,17 +513,11 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
             }
       }
     };
-    // Scores are kept relative to a per-column reference M (log2 units): the
-    // queries are pre-scaled by scale * log2(e) and each score product chain
-    // starts from -M (negq) instead of zero, so a probability is one
-    // exponential of the product's result.  The reference moves only when a
-    // chunk's maximum passes it by more than 2^8 in probability; delta is how
-    // far this chunk moves it (0 otherwise), and in a rare branch afterwards
-    // the accumulators are rescaled by 2^-delta and the next chunk's scores,
-    // already taken against the old reference, are re-based.
-    float delta[2] = {0.f, 0.f};
-    f32x4 negq[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    // softmax of one chunk (a wave's last, not fused with the next scores)
+    // Softmax of one chunk: probabilities (bf16) against the running
+    // reference, which moves (branch-free, per column) only when the chunk's
+    // maximum exceeds it by more than 2^8; the accumulators are rescaled
+    // afterwards, in a rare branch, by 2^((m_old - m_new) c).
+    float m_old[2];
     auto softmax = [&](const Sc& sc, bf16x8 (&pb)[2][NH]) -> bool {
       bool moved = false;
 #pragma unroll
@@ -544,15 +528,17 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) x = fmaxf(x, fmaxf(sc.x[t][h][e], sc.y[t][h][e]));
         const float cm = pair_max16(pair_max32(x));
-        const bool up = cm > kRefSlack;
-        delta[t] = up ? cm : 0.f;
+        const bool up = (cm - m_run[t]) * c > kRefSlack;
+        m_old[t] = m_run[t];
+        m_run[t] = up ? fmaxf(m_run[t], cm) : m_run[t];
         moved |= up;
+        const float mc = m_run[t] * c;
 #pragma unroll
         for (int h = 0; h < NH; ++h)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            pb[t][h][e] = (__bf16)fast_exp2(sc.x[t][h][e] - delta[t]);
-            pb[t][h][e + 4] = (__bf16)fast_exp2(sc.y[t][h][e] - delta[t]);
+            pb[t][h][e] = (__bf16)fast_exp2(fmaf(sc.x[t][h][e], c, -mc));
+            pb[t][h][e + 4] = (__bf16)fast_exp2(fmaf(sc.y[t][h][e], c, -mc));
           }
       }
       return moved;
@@ -577,7 +563,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
       f.y[k] = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x + 4) * KS + cb]);
     };
     // (the caller has read segment 0 into kf)
-    auto fused = [&](int kbuf, Kf& kf, Sc& nx, Sc& cu, bf16x8 (&pb)[2][NH]) -> bool {
+    auto fused = [&](int kbuf, Kf& kf, Sc& nx, const Sc& cu, bf16x8 (&pb)[2][NH]) -> bool {
       constexpr int NE = 2 * NH * 8;  // probabilities per lane per chunk
       bf16x8 (&ax)[NSEG] = kf.x;
       bf16x8 (&ay)[NSEG] = kf.y;
@@ -585,11 +571,12 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
         const int h = k / KI, i = k % KI;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          nx.x[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[k], qf[t][i], i ? nx.x[t][h] : negq[t], 0, 0, 0);
-          nx.y[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ay[k], qf[t][i], i ? nx.y[t][h] : negq[t], 0, 0, 0);
+          nx.x[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[k], qf[t][i], i ? nx.x[t][h] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          nx.y[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ay[k], qf[t][i], i ? nx.y[t][h] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         }
       };
       bool moved = false;
+      float mc[2];
       auto rowmax = [&](int t) {
         float x = cu.x[t][0][0];
 #pragma unroll
@@ -598,27 +585,22 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
           for (int e = 0; e < 4; ++e) x = fmaxf(x, fmaxf(cu.x[t][h][e], cu.y[t][h][e]));
         // the column's maximum over its four lanes is needed only where the
         // reference moves: tested on each lane's own maximum first (a rare,
-        // uniform branch), which then also re-bases this chunk's scores
-        delta[t] = 0.f;
-        if (__builtin_amdgcn_ballot_w64(x > kRefSlack) != 0) {
+        // uniform branch)
+        m_old[t] = m_run[t];
+        if (__builtin_amdgcn_ballot_w64((x - m_run[t]) * c > kRefSlack) != 0) {
           const float cm = pair_max16(pair_max32(x));
-          const bool up = cm > kRefSlack;
-          delta[t] = up ? cm : 0.f;
+          const bool up = (cm - m_run[t]) * c > kRefSlack;
+          m_run[t] = up ? fmaxf(m_run[t], cm) : m_run[t];
           moved |= up;
-#pragma unroll
-          for (int h = 0; h < NH; ++h) {
-            cu.x[t][h] -= delta[t];
-            cu.y[t][h] -= delta[t];
-          }
         }
+        mc[t] = m_run[t] * c;
       };
       // probability q (q = ((t * NH + h) * 2 + xy) * 4 + e) of this lane
       auto prob = [&](int q) {
         const int e = q & 3, xy = (q >> 2) & 1, h = (q >> 3) % NH, t = (q >> 3) / NH;
         const float sv = xy ? cu.y[t][h][e] : cu.x[t][h][e];
-        pb[t][h][e + 4 * xy] = (__bf16)fast_exp2(sv);
+        pb[t][h][e + 4 * xy] = (__bf16)fast_exp2(fmaf(sv, c, -mc[t]));
       };
-      kread(kbuf, kf, 0);
       if (NSEG > 1) kread(kbuf, kf, 1);
 #pragma unroll
       for (int k = 0; k < NSEG; ++k) {
@@ -686,8 +668,11 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
         load_tab(wb);
         __syncthreads();
       }
+      // the next chunk's first key fragments are read before this step's
+      // loads are issued, so their LDS latency passes while those wait to issue
       const bool fuse = c0 < wave_kend && more && c0 + CH < wave_kend;  // uniform
       Kf kf;
+      if (fuse) kread((ci + 1) & 1, kf, 0);
       if (more2) kload_direct(c0 + 2 * CH, ci & 1);
       if (more) vload_direct(c0 + CH, (ci + 1) & 1);
       if (c0 < wave_kend) {  // uniform over the wave
@@ -705,22 +690,13 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int h = 0; h < NH; ++h) asm volatile("" : "+v"(pb[t][h]));
-        if (__builtin_amdgcn_ballot_w64(moved) != 0) {  // rare: a reference moved
+        if (__builtin_amdgcn_ballot_w64(moved) != 0) {  // rare
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
-            const float alpha = fast_exp2(-delta[t]);
+            const float alpha = fast_exp2((m_old[t] - m_run[t]) * c);
 #pragma unroll
             for (int j = 0; j < NJ; ++j) acc[t][j] *= alpha;
             lsum[t] *= alpha;
-            const float nm = negq[t][0] - delta[t];
-            negq[t] = f32x4{nm, nm, nm, nm};
-            if (fuse) {  // the next chunk's scores were taken against the old reference
-#pragma unroll
-              for (int h = 0; h < NH; ++h) {
-                nxt.x[t][h] -= delta[t];
-                nxt.y[t][h] -= delta[t];
-              }
-            }
           }
         }
         __builtin_amdgcn_s_setprio(1);  // value products issue first on this SIMD
@@ -732,27 +708,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
       __syncthreads();
     };
     Sc sa, sb;
-    if (0 < wave_kend) {  // uniform
-      // the first chunk (key 0 is visible to every query) sets each column's
-      // reference to its maximum
-      sa = scores(0);
-      mask(sa, 0);
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        float x = sa.x[t][0][0];
-#pragma unroll
-        for (int h = 0; h < NH; ++h)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x = fmaxf(x, fmaxf(sa.x[t][h][e], sa.y[t][h][e]));
-        const float m0 = pair_max16(pair_max32(x));
-        negq[t] = f32x4{-m0, -m0, -m0, -m0};
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          sa.x[t][h] -= m0;
-          sa.y[t][h] -= m0;
-        }
-      }
-    }
+    if (0 < wave_kend) sa = scores(0);  // uniform
     // every wave has read chunk 0's keys before step 0 loads chunk 2 over them
     __syncthreads();
     for (int32_t ci = 0; ci < nchunks; ci += 2) {
