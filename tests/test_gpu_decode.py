@@ -141,6 +141,47 @@ def test_every_path_matches_oracle(monkeypatch, env):
         say(f"  {cfg.name} {env}: max err {err:.3e}")
 
 
+@pytest.mark.parametrize("env", [
+    {"PKV_DECODE_MATH": "mfma"},
+    {"PKV_DECODE_MATH": "dpp"},
+    {"PKV_DECODE_MATH": "valu"},
+    {"PKV_DECODE_MATH": "generic"},
+    {"PKV_PARTITION_TOKENS": "64"},
+])
+def test_large_scores_every_path(monkeypatch, env):
+    """Scale 8 / sqrt(D): scores spread over tens of log2 units, so the
+    softmax is dominated by a few keys and each partition's running maximum
+    keeps moving.  Every kernel, split or not, against float64 at that scale;
+    the shared-prefix batch runs the pack paths."""
+    import torch
+    from oracle import attention as oatt
+    from tests.paged_case import gpu_out
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    for cfg in (SMALL_GQA, CONFIGS["small_mha"], dataclasses.replace(CONFIGS["prefix"], batch=24)):
+        case = build_case(cfg, seed=6, run_decode=False)
+        w, kv, m = case.w, case.kv, case.meta
+        rows = torch.from_numpy(w.cu[1:] - 1).to("cuda")
+        kv.append_decode_tokens(m, w.ctx_k.index_select(0, rows).contiguous(),
+                                w.ctx_v.index_select(0, rows).contiguous())
+        scale = 8.0 / np.sqrt(cfg.head_dim)
+        out = torch.full_like(w.q, float("nan"))
+        kv.attend(m, w.q, out, scale=scale)
+        torch.cuda.synchronize()
+        case.out = out
+        worst = 0.0
+        for b in range(cfg.batch):
+            k, v = w.seq_kv(b)
+            ref = oatt.decode(host_bits(w.q[b]), host_bits(k), host_bits(v), scale)
+            got = gpu_out(case, b)
+            assert np.isfinite(got).all()
+            err = float(np.abs(got - ref).max())
+            assert err <= BF16_TOL, f"{cfg.name} sequence {b}: max abs err {err}"
+            worst = max(worst, err)
+        say(f"  {cfg.name} {env}: max err {worst:.3e}")
+        kv.close()
+
+
 def test_split_and_single_pass_agree(monkeypatch):
     import torch
     a = build_case(SMALL_GQA, seed=2).out.clone()
