@@ -115,6 +115,21 @@ def test_prefill_block_permutation_is_bit_identical_and_poison_free():
     assert torch.equal(a, c)
 
 
+@pytest.mark.parametrize("p", [64, 128, 256])
+def test_large_blocks(p):
+    """Blocks of 64-256 tokens: several 16-key staging groups and several
+    64-key chunks per block, a last block filled only in part, and contexts
+    that end inside a block."""
+    ctx = [0, 5, 300, 1000]
+    new = [150, 77, 64, 200]
+    out, ref, _ = _run(16, 4, 128, p, ctx, new, seed=p)
+    got = out.double().cpu().numpy()
+    assert np.isfinite(got).all()
+    err = float(np.abs(got - ref).max())
+    say(f"  p={p}: max err {err:.3e}")
+    assert err <= BF16_TOL
+
+
 @pytest.mark.parametrize("p", [8, 16, 32])
 @pytest.mark.parametrize("shape", ["rising", "falling"])
 def test_running_reference_moves_within_a_sequence(shape, p):
