@@ -62,12 +62,6 @@ struct PrefillArgs {
   int32_t* err;
 };
 
-// Plain cached loads: a key/value chunk is read by every query tile of the
-// sequence, so unlike decode the second reader should find it in L2.
-__device__ __forceinline__ uint4 load16(const uint16_t* p) {
-  return *reinterpret_cast<const uint4*>(p);
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // How far (log2 units) a chunk's maximum score may exceed the running
@@ -79,25 +73,15 @@ constexpr int kXcds = 8;  // accelerator complex dies (separate L2 caches) on MI
 // pair_max32 / pair_max16 (row-group maxima) and kswz (the key-row LDS
 // swizzle) are in tile_common.hpp.
 
-// Value rows (one head_dim row of a chunk's 64 keys, token-minor) sit
-// unpadded too, piece c of row d at c ^ vswz(d).  The value-fragment reads
-// (rows 16 j + 0..15 at one piece index) still show 4 extra cycles per read
-// on the counter, as they did with padded rows; the swizzle is kept for the
-// smaller footprint (the staging writes are conflict-free either way).  Only
-// the row's low four bits are used, so a lane's rows share one swizzle.
-__device__ __forceinline__ int vswz(int d) { return (d & 7) ^ (((d >> 3) & 1) * 3); }
-
-// WB (block sizes that are multiples of 16): wave w stages the keys
-// [c0 + 16 w, c0 + 16 w + 16) of each 64-key chunk, which lie in one block, so
-// the block's address is uniform over the wave (scalar registers) and every
-// lane's offsets inside it are fixed for the whole loop.  The keys and values
-// go straight from HBM into LDS (global_load_lds_dwordx4: no staging
-// registers, no vector-ALU address arithmetic), keys two chunks ahead and
-// values one, and the loop is software-pipelined: the score products of chunk
-// i + 1 are issued between the softmax instructions of chunk i.  Otherwise
-// (blocks of 8) each 16-byte piece looks up its own block, is staged through
-// registers, and each chunk runs scores, softmax and values in turn.
-template <int D, int GW, bool WB>
+// Wave w stages the keys [c0 + 16 w, c0 + 16 w + 16) of each 64-key chunk,
+// which lie in one block (two with blocks of 8), so the blocks' addresses are
+// uniform over the wave (scalar registers) and every lane's offsets inside
+// them are fixed for the whole loop.  The keys and values go straight from
+// HBM into LDS (global_load_lds_dwordx4: no staging registers, no vector-ALU
+// address arithmetic), keys two chunks ahead and values one, and the loop is
+// software-pipelined: the score products of chunk i + 1 are issued between
+// the softmax instructions of chunk i.
+template <int D, int GW>
 __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int NT = 256;             // threads: four waves
   constexpr int BT = 16 * (8 / GW);   // query tokens per workgroup
@@ -106,13 +90,12 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int KI = D / 32;          // score MFMA steps over head_dim
   constexpr int NJ = D / 16;          // value MFMA output tiles over head_dim
   constexpr int KS = D;               // LDS key row (elements); 16-byte pieces swizzled, see kswz
-  constexpr int VS = CH;              // LDS value row (elements); 16-byte pieces swizzled, see vswz
   constexpr int KU = CH * D / 8 / NT; // 16-byte key pieces per thread per chunk
   constexpr int VU = D * CH / 8 / NT; // 16-byte value pieces per thread per chunk
   constexpr int TW = 1024;            // block-table window (entries)
   static_assert(KU >= 1 && VU >= 1, "chunk pieces");
   __shared__ __align__(16) uint16_t k_lds[2][CH * KS];
-  __shared__ __align__(16) uint16_t v_lds[2][D * VS];
+  __shared__ __align__(16) uint16_t v_lds[2][D * CH];
   __shared__ int32_t tab[TW];
 
   const int32_t G = a.hq / a.hkv;
@@ -200,81 +183,40 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     }
   };
 
-  // cooperative chunk staging: key rows and value-tile runs, 16-byte pieces
-  uint4 kst[KU], vst[VU];
-  auto gload = [&](int32_t c0) {
-#pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int p = tid + u * NT;
-      const int key = p / (D / 8), dc = p % (D / 8);
-      const int32_t t = min(c0 + key, kend - 1);
-      const int64_t blk = tab[(t >> lp) - wb];
-      kst[u] = load16(kc + blk * blk_stride + khead + (int64_t)(t & (P - 1)) * a.ks.tok + dc * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < VU; ++u) {
-      const int p = tid + u * NT;
-      const int dim = p / (CH / 8), qq = p % (CH / 8);
-      const int32_t t0 = c0 + 8 * qq;                 // 8 keys inside one block (P % 8 == 0)
-      const int32_t t = min(t0, (kend - 1) & ~7);
-      const int64_t blk = tab[(t >> lp) - wb];
-      uint4 x = load16(vc + blk * blk_stride + vhead + (int64_t)dim * P + (t & (P - 1)));
-      // keys at or past the context end: zero, so unused slots cannot leak
-      const int32_t nv = t0 >= kend ? 0 : min(kend - t0, 8);
-      if (nv < 8) {
-        const uint32_t m0 = nv >= 2 ? 0xffffffffu : (nv == 1 ? 0x0000ffffu : 0u);
-        const uint32_t m1 = nv >= 4 ? 0xffffffffu : (nv == 3 ? 0x0000ffffu : 0u);
-        const uint32_t m2 = nv >= 6 ? 0xffffffffu : (nv == 5 ? 0x0000ffffu : 0u);
-        const uint32_t m3 = nv >= 8 ? 0xffffffffu : (nv == 7 ? 0x0000ffffu : 0u);
-        x.x &= m0;
-        x.y &= m1;
-        x.z &= m2;
-        x.w &= m3;
-      }
-      vst[u] = x;
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int p = tid + u * NT;
-      const int key = p / (D / 8), dc = p % (D / 8);
-      *reinterpret_cast<uint4*>(&k_lds[buf][key * KS + (dc ^ kswz<D>(key)) * 8]) = kst[u];
-    }
-#pragma unroll
-    for (int u = 0; u < VU; ++u) {
-      const int p = tid + u * NT;
-      const int dim = p / (CH / 8), qq = p % (CH / 8);
-      *reinterpret_cast<uint4*>(&v_lds[buf][dim * VS + (qq ^ vswz(dim)) * 8]) = vst[u];
-    }
-  };
-
-  // Wave-group staging (WB): wave w stages the 16 keys [c0 + 16 w, + 16) of
+  // Wave-group staging: wave w stages the 16 keys [c0 + 16 w, + 16) of
   // each chunk, KU = D / 32 loads of 64 lanes x 16 bytes for the keys and as
   // many for the values.  A key load covers KR = 512 / D rows: lane row wkr,
   // 16-byte column wdc.
   static_assert(KU == D / 32 && VU == D / 32, "one 16-key group per wave");
   constexpr int KR = 512 / D;
   const int wkr = lane / (D / 8), wdc = lane % (D / 8);
-  // one wave's 16-key group of a chunk: the block holding keys [kb, kb + 16),
-  // or for a group past the context end the last group that holds keys (in
-  // bounds; zeroed with the boundary mask)
-  // (direct: the entry read from the table row itself, for the first chunks,
-  // staged before the table window is in LDS)
-  auto group_base = [&](int32_t c0, int64_t& off, bool direct = false) -> int32_t {
+  // one wave's 16-key group of a chunk: keys [kb, kb + 16), or for a group
+  // past the context end the last group that holds keys (in bounds; zeroed
+  // with the boundary mask).  With blocks of 16 or more the group lies in one
+  // block (offA; offB the same); with blocks of 8 its keys 8..15 lie in a
+  // second block (offB), the tile's last block where the group ends early.
+  // (direct: the entries read from the table row itself, for the first
+  // chunks, staged before the table window is in LDS)
+  const bool p8 = P < 16;  // uniform
+  auto group_base = [&](int32_t c0, int64_t& offA, int64_t& offB, bool direct = false) -> int32_t {
     const int32_t kb = c0 + 16 * w;  // uniform
     const int32_t kl = min(kb, kend - 1) & ~15;
-    int32_t blk;
+    const int32_t la = kl >> lp, lb2 = p8 ? min(la + 1, last_blk) : la;
+    int32_t ba, bb;
     if (direct) {
-      blk = __builtin_amdgcn_readfirstlane(trow[kl >> lp]);
-      if ((uint32_t)blk >= (uint32_t)a.num_blocks) blk = 0;  // flagged by the window load
+      ba = __builtin_amdgcn_readfirstlane(trow[la]);
+      bb = p8 ? __builtin_amdgcn_readfirstlane(trow[lb2]) : ba;
+      if ((uint32_t)ba >= (uint32_t)a.num_blocks) ba = 0;  // flagged by the window load
+      if ((uint32_t)bb >= (uint32_t)a.num_blocks) bb = 0;
     } else {
-      blk = __builtin_amdgcn_readfirstlane(tab[(kl >> lp) - wb]);
+      ba = __builtin_amdgcn_readfirstlane(tab[la - wb]);
+      bb = p8 ? __builtin_amdgcn_readfirstlane(tab[lb2 - wb]) : ba;
     }
-    off = (int64_t)blk * blk_stride;
-    return kl & (P - 1);  // offset of the group inside its block
+    offA = (int64_t)ba * blk_stride;
+    offB = (int64_t)bb * blk_stride;
+    return kl & (P - 1);  // offset of the group inside its (first) block
   };
-  // Direct global-to-LDS staging (WB): each global_load_lds_dwordx4 puts
+  // Direct global-to-LDS staging: each global_load_lds_dwordx4 puts
   // lane i's 16 bytes at the wave-uniform LDS address + 16 i, so a lane loads
   // whichever global piece belongs at its slot.  Keys: the swizzled rows
   // above, instruction u covering rows 16 w + u KR .. + KR - 1 (lane: row
@@ -286,33 +228,41 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   typedef __attribute__((address_space(3))) void* lds_ptr_t;
   typedef __attribute__((address_space(1))) void* gptr_t;
   constexpr int VPG = D / 64;  // value instructions per 8-key group
-  uint32_t kdoff[KU];          // bytes from the group's first key row
+  uint32_t kdoff[KU];          // bytes from the first key row of the instruction's block
 #pragma unroll
   for (int u = 0; u < KU; ++u) {
     const int row = u * KR + wkr;
-    kdoff[u] = (uint32_t)(row * a.ks.tok * 2 + (wdc ^ kswz<D>(16 * w + row)) * 16);
+    const int grow = p8 && u * KR >= 8 ? row - 8 : row;  // (rows 8..15 of blocks of 8: second block)
+    kdoff[u] = (uint32_t)(grow * a.ks.tok * 2 + (wdc ^ kswz<D>(16 * w + row)) * 16);
   }
   const uint32_t vdoff = (uint32_t)(lane * P * 2);  // bytes: this lane's head_dim row
   auto vslot = [&](int vbuf, int u) -> uint16_t* {   // instruction u's LDS run
     return &v_lds[vbuf][((2 * w + u / VPG) * D + (u % VPG) * 64) * 8];
   };
+  // (instruction u covers key rows u KR .. u KR + KR - 1 of the group, all
+  // in one block also with blocks of 8, since KR divides 8; value
+  // instruction u covers the 8-key group u / VPG, one block of 8)
   auto kload_direct = [&](int32_t c0, int kbuf, bool direct = false) {
-    int64_t boff;
-    const int32_t o = group_base(c0, boff, direct);
-    const char* kbase = (const char*)(kc + boff + khead + (int64_t)o * a.ks.tok);
+    int64_t oa, ob;
+    const int32_t o = group_base(c0, oa, ob, direct);
+    const char* ka = (const char*)(kc + oa + khead + (int64_t)o * a.ks.tok);
+    const char* kb2 = (const char*)(kc + ob + khead);
 #pragma unroll
     for (int u = 0; u < KU; ++u)
-      __builtin_amdgcn_global_load_lds((gptr_t)(kbase + kdoff[u]),
+      __builtin_amdgcn_global_load_lds((gptr_t)((p8 && u * KR >= 8 ? kb2 : ka) + kdoff[u]),
                                        (lds_ptr_t)&k_lds[kbuf][(16 * w + u * KR) * KS], 16, 0, 0);
   };
   auto vload_direct = [&](int32_t c0, int vbuf, bool direct = false) {
-    int64_t boff;
-    const int32_t o = group_base(c0, boff, direct);
-    const char* vbase = (const char*)(vc + boff + vhead + o);
+    int64_t oa, ob;
+    const int32_t o = group_base(c0, oa, ob, direct);
+    const char* va = (const char*)(vc + oa + vhead + o);
+    const char* vb2 = (const char*)(vc + ob + vhead);
 #pragma unroll
-    for (int u = 0; u < VU; ++u)
-      __builtin_amdgcn_global_load_lds((gptr_t)(vbase + (u % VPG) * 64 * P * 2 + (u / VPG) * 16 + vdoff),
+    for (int u = 0; u < VU; ++u) {
+      const char* vb = p8 ? (u / VPG ? vb2 : va) : va + (u / VPG) * 16;
+      __builtin_amdgcn_global_load_lds((gptr_t)(vb + (u % VPG) * 64 * P * 2 + vdoff),
                                        (lds_ptr_t)vslot(vbuf, u), 16, 0, 0);
+    }
   };
   // After this wave's loads of a group that reaches past the context end
   // have landed (vmcnt 0): zero the values of keys >= kend in its own slots
@@ -355,16 +305,30 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   const int krow_x = 8 * (nq >> 2) + (nq & 3);  // key of chain-X row nq within the chunk
   // the swizzle of every key row this lane reads (chains X and Y, both halves)
   const int kx = kswz<D>(krow_x);
-  const int vx = vswz(nq);  // the swizzle of value rows 16 j + nq
-
-  auto compute = [&](int buf, int32_t c0) {
-    const uint16_t* kl = k_lds[buf];
-    const uint16_t* vl = v_lds[buf];
-    f32x4 sx[2][NH], sy[2][NH];
+  // the first chunks' blocks straight from the table row, so their loads are
+  // in flight while the table window is brought into LDS
+  kload_direct(0, 0, true);
+  vload_direct(0, 0, true);
+  if (nchunks > 1) kload_direct(CH, 1, true);
+  load_tab(0);
+  __syncthreads();
+  // Software-pipelined loop.  Iteration ci runs the softmax of chunk ci in
+  // the same basic block as the score products of chunk ci + 1 (they are
+  // independent, so the in-order issue alternates vector-ALU and
+  // matrix-core instructions), then the value products of chunk ci.  Keys
+  // are staged two chunks ahead, values one: the key buffer of chunk ci is
+  // free once its scores are taken (in iteration ci - 1), the value buffer
+  // of chunk ci - 1 once its products are taken.
+  struct Sc {
+    f32x4 x[2][NH], y[2][NH];
+  };
+  auto scores = [&](int kbuf) -> Sc {
+    const uint16_t* kl = k_lds[kbuf];
+    Sc sc;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int h = 0; h < NH; ++h) sx[t][h] = sy[t][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int h = 0; h < NH; ++h) sc.x[t][h] = sc.y[t][h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
 #pragma unroll
@@ -374,366 +338,230 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
         const bf16x8 ay = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x + 4) * KS + cb]);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          sx[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, qf[t][i], sx[t][h], 0, 0, 0);
-          sy[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ay, qf[t][i], sy[t][h], 0, 0, 0);
+          sc.x[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, qf[t][i], sc.x[t][h], 0, 0, 0);
+          sc.y[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ay, qf[t][i], sc.y[t][h], 0, 0, 0);
         }
       }
     }
-    float s[2][NH][8];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int h = 0; h < NH; ++h)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          s[t][h][e] = sx[t][h][e];
-          s[t][h][e + 4] = sy[t][h][e];
-        }
-    // Rare cases first, each one uniform branch, so that the common path
-    // below (exponentials and both tiles' products) is one straight block.
-    if (c0 + CH - 1 > base + min(tok0[0], tok0[1])) {  // the chunk reaches past some query's position
+    return sc;
+  };
+  // causal mask of chunk c0's scores (rare: only chunks that reach past
+  // some query's position)
+  auto mask = [&](Sc& sc, int32_t c0) {
+    if (c0 + CH - 1 > base + min(tok0[0], tok0[1])) {  // uniform
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int h = 0; h < NH; ++h)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) s[t][h][e] = c0 + 32 * h + 8 * r + e <= qpos[t] ? s[t][h][e] : -INFINITY;
+          for (int e = 0; e < 4; ++e) {
+            const int32_t kx0 = c0 + 32 * h + 8 * r + e;
+            sc.x[t][h][e] = kx0 <= qpos[t] ? sc.x[t][h][e] : -INFINITY;
+            sc.y[t][h][e] = kx0 + 4 <= qpos[t] ? sc.y[t][h][e] : -INFINITY;
+          }
     }
-    float cm[2];
+  };
+  // Softmax of one chunk: probabilities (bf16) against the running
+  // reference, which moves (branch-free, per column) only when the chunk's
+  // maximum exceeds it by more than 2^8; the accumulators are rescaled
+  // afterwards, in a rare branch, by 2^((m_old - m_new) c).
+  float m_old[2];
+  auto softmax = [&](const Sc& sc, bf16x8 (&pb)[2][NH]) -> bool {
+    bool moved = false;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      float x = s[t][0][0];
+      float x = sc.x[t][0][0];
 #pragma unroll
       for (int h = 0; h < NH; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x = fmaxf(x, s[t][h][e]);
-      cm[t] = pair_max16(pair_max32(x));
-    }
-    // The reference maximum m_run moves only when a chunk's maximum exceeds
-    // it by more than 2^8 (in probability): until then probabilities are at
-    // most 256, and accumulator and sum share the stale reference, so nothing
-    // needs rescaling.  Finite after the first chunk (key 0 lies in the first
-    // chunk of every query), which always moves it.
-    if (__builtin_amdgcn_ballot_w64((cm[0] - m_run[0]) * c > kRefSlack ||
-                                    (cm[1] - m_run[1]) * c > kRefSlack) != 0) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        if (__builtin_amdgcn_ballot_w64((cm[t] - m_run[t]) * c > kRefSlack) != 0) {  // uniform
-          const float m_new = fmaxf(m_run[t], cm[t]);
-          const float alpha = fast_exp2((m_run[t] - m_new) * c);
-          m_run[t] = m_new;
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) acc[t][j] *= alpha;
-          lsum[t] *= alpha;
-        }
-      }
-    }
-    bf16x8 pb[2][NH];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
+        for (int e = 0; e < 4; ++e) x = fmaxf(x, fmaxf(sc.x[t][h][e], sc.y[t][h][e]));
+      const float cm = pair_max16(pair_max32(x));
+      const bool up = (cm - m_run[t]) * c > kRefSlack;
+      m_old[t] = m_run[t];
+      m_run[t] = up ? fmaxf(m_run[t], cm) : m_run[t];
+      moved |= up;
       const float mc = m_run[t] * c;
 #pragma unroll
       for (int h = 0; h < NH; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[t][h][e] = (__bf16)fast_exp2(fmaf(s[t][h][e], c, -mc));
+        for (int e = 0; e < 4; ++e) {
+          pb[t][h][e] = (__bf16)fast_exp2(fmaf(sc.x[t][h][e], c, -mc));
+          pb[t][h][e + 4] = (__bf16)fast_exp2(fmaf(sc.y[t][h][e], c, -mc));
+        }
     }
+    return moved;
+  };
+  // Scores of the next chunk fused with the softmax of the current one, in
+  // a fixed issue order: segment k reads two key fragments ahead and issues
+  // the four products of step k (both tiles, chains X and Y); its vector
+  // work is the two row-maximum reductions (segments 0, 1), then an equal
+  // share of the exponentials.  A scheduling fence after every segment
+  // keeps the order, so the matrix core works on the next chunk while the
+  // vector ALU works on this one.
+  // key fragments of one chunk for the fused step: segment k's pair
+  constexpr int NSEG = NH * KI;
+  struct Kf {
+    bf16x8 x[NSEG], y[NSEG];
+  };
+  auto kread = [&](int kbuf, Kf& f, int k) {
+    const uint16_t* kl = k_lds[kbuf];
+    const int h = k / KI, i = k % KI;
+    const int cb = ((4 * i + r) ^ kx) * 8;
+    f.x[k] = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x) * KS + cb]);
+    f.y[k] = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x + 4) * KS + cb]);
+  };
+  // (the caller has read segment 0 into kf)
+  auto fused = [&](int kbuf, Kf& kf, Sc& nx, const Sc& cu, bf16x8 (&pb)[2][NH]) -> bool {
+    constexpr int NE = 2 * NH * 8;  // probabilities per lane per chunk
+    bf16x8 (&ax)[NSEG] = kf.x;
+    bf16x8 (&ay)[NSEG] = kf.y;
+    auto kmfma = [&](int k) {
+      const int h = k / KI, i = k % KI;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        nx.x[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[k], qf[t][i], i ? nx.x[t][h] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        nx.y[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ay[k], qf[t][i], i ? nx.y[t][h] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      }
+    };
+    bool moved = false;
+    float mc[2];
+    auto rowmax = [&](int t) {
+      float x = cu.x[t][0][0];
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x = fmaxf(x, fmaxf(cu.x[t][h][e], cu.y[t][h][e]));
+      // the column's maximum over its four lanes is needed only where the
+      // reference moves: tested on each lane's own maximum first (a rare,
+      // uniform branch)
+      m_old[t] = m_run[t];
+      if (__builtin_amdgcn_ballot_w64((x - m_run[t]) * c > kRefSlack) != 0) {
+        const float cm = pair_max16(pair_max32(x));
+        const bool up = (cm - m_run[t]) * c > kRefSlack;
+        m_run[t] = up ? fmaxf(m_run[t], cm) : m_run[t];
+        moved |= up;
+      }
+      mc[t] = m_run[t] * c;
+    };
+    // probability q (q = ((t * NH + h) * 2 + xy) * 4 + e) of this lane
+    auto prob = [&](int q) {
+      const int e = q & 3, xy = (q >> 2) & 1, h = (q >> 3) % NH, t = (q >> 3) / NH;
+      const float sv = xy ? cu.y[t][h][e] : cu.x[t][h][e];
+      pb[t][h][e + 4 * xy] = (__bf16)fast_exp2(fmaf(sv, c, -mc[t]));
+    };
+    if (NSEG > 1) kread(kbuf, kf, 1);
+#pragma unroll
+    for (int k = 0; k < NSEG; ++k) {
+      if (k + 2 < NSEG) kread(kbuf, kf, k + 2);
+      kmfma(k);
+      if (k < 2) {
+        rowmax(k);
+      } else {
+        constexpr int per = (NE + NSEG - 3) / (NSEG - 2);
+#pragma unroll
+        for (int q = (k - 2) * per; q < (k - 1) * per && q < NE; ++q) prob(q);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return moved;
+  };
+  // Value products of one chunk.  The value fragments are read VA head_dim
+  // tiles ahead of their products, in a fixed order (a scheduling fence
+  // after every tile), so each LDS read has the products of the tiles
+  // before it to hide behind; left to itself the compiler reuses one
+  // register quad and waits for every read.  The row sums need no fragment
+  // and cover the first reads.
+  auto values = [&](int vbuf, const bf16x8 (&pb)[2][NH]) {
+    constexpr int VA = 3;
+    const uint16_t* vl = v_lds[vbuf];
+    bf16x8 av[NJ][NH];
+    auto vread = [&](int j) {
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+        av[j][h] = *reinterpret_cast<const bf16x8*>(&vl[((4 * h + r) * D + 16 * j + nq) * 8]);
+    };
+#pragma unroll
+    for (int j = 0; j < VA && j < NJ; ++j) vread(j);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int h = 0; h < NH; ++h)
         lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[t][h], lsum[t], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
+      if (j + VA < NJ) vread(j + VA);
 #pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&vl[(16 * j + nq) * VS + ((4 * h + r) ^ vx) * 8]);
+      for (int h = 0; h < NH; ++h)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
-          acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[t][h], acc[t][j], 0, 0, 0);
-      }
+          acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[j][h], pb[t][h], acc[t][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  if constexpr (WB) {
-    // the first chunks' blocks straight from the table row, so their loads
-    // are in flight while the table window is brought into LDS
-    kload_direct(0, 0, true);
-    vload_direct(0, 0, true);
-    if (nchunks > 1) kload_direct(CH, 1, true);
-  }
-  load_tab(0);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
+  vfix(0, 0);
   __syncthreads();
-  if constexpr (WB) {
-    // Software-pipelined loop.  Iteration ci runs the softmax of chunk ci in
-    // the same basic block as the score products of chunk ci + 1 (they are
-    // independent, so the in-order issue alternates vector-ALU and
-    // matrix-core instructions), then the value products of chunk ci.  Keys
-    // are staged two chunks ahead, values one: the key buffer of chunk ci is
-    // free once its scores are taken (in iteration ci - 1), the value buffer
-    // of chunk ci - 1 once its products are taken.
-    struct Sc {
-      f32x4 x[2][NH], y[2][NH];
-    };
-    auto scores = [&](int kbuf) -> Sc {
-      const uint16_t* kl = k_lds[kbuf];
-      Sc sc;
+  // one iteration: chunk ci's softmax and value products, chunk ci + 1's
+  // scores into `nxt`; unrolled by two below so that the two score sets
+  // trade roles without register copies
+  auto step = [&](int32_t ci, Sc& cur, Sc& nxt) {
+    const int32_t c0 = ci * CH;
+    const bool more = ci + 1 < nchunks, more2 = ci + 2 < nchunks;  // uniform
+    if (more && min(c0 + 3 * CH, kend) - 1 >= (wb + TW) * P) {
+      // the staged chunks leave the table window; every read of it is
+      // behind the last barrier
+      wb = (c0 + CH) >> lp;
+      load_tab(wb);
+      __syncthreads();
+    }
+    // the next chunk's first key fragments are read before this step's
+    // loads are issued, so their LDS latency passes while those wait to issue
+    const bool fuse = c0 < wave_kend && more && c0 + CH < wave_kend;  // uniform
+    Kf kf;
+    if (fuse) kread((ci + 1) & 1, kf, 0);
+    if (more2) kload_direct(c0 + 2 * CH, ci & 1);
+    if (more) vload_direct(c0 + CH, (ci + 1) & 1);
+    if (c0 < wave_kend) {  // uniform over the wave
+      mask(cur, c0);
+      bf16x8 pb[2][NH];
+      bool moved;
+      if (fuse) {
+        moved = fused((ci + 1) & 1, kf, nxt, cur, pb);
+      } else {
+        moved = softmax(cur, pb);
+      }
+      // keep the probabilities computed here, beside the score products,
+      // rather than sunk past the rare rescale branch below
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int h = 0; h < NH; ++h) sc.x[t][h] = sc.y[t][h] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int h = 0; h < NH; ++h) {
-#pragma unroll
-        for (int i = 0; i < KI; ++i) {
-          const int cb = ((4 * i + r) ^ kx) * 8;
-          const bf16x8 ax = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x) * KS + cb]);
-          const bf16x8 ay = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x + 4) * KS + cb]);
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            sc.x[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, qf[t][i], sc.x[t][h], 0, 0, 0);
-            sc.y[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ay, qf[t][i], sc.y[t][h], 0, 0, 0);
-          }
-        }
-      }
-      return sc;
-    };
-    // causal mask of chunk c0's scores (rare: only chunks that reach past
-    // some query's position)
-    auto mask = [&](Sc& sc, int32_t c0) {
-      if (c0 + CH - 1 > base + min(tok0[0], tok0[1])) {  // uniform
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int h = 0; h < NH; ++h)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int32_t kx0 = c0 + 32 * h + 8 * r + e;
-              sc.x[t][h][e] = kx0 <= qpos[t] ? sc.x[t][h][e] : -INFINITY;
-              sc.y[t][h][e] = kx0 + 4 <= qpos[t] ? sc.y[t][h][e] : -INFINITY;
-            }
-      }
-    };
-    // Softmax of one chunk: probabilities (bf16) against the running
-    // reference, which moves (branch-free, per column) only when the chunk's
-    // maximum exceeds it by more than 2^8; the accumulators are rescaled
-    // afterwards, in a rare branch, by 2^((m_old - m_new) c).
-    float m_old[2];
-    auto softmax = [&](const Sc& sc, bf16x8 (&pb)[2][NH]) -> bool {
-      bool moved = false;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        float x = sc.x[t][0][0];
-#pragma unroll
-        for (int h = 0; h < NH; ++h)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x = fmaxf(x, fmaxf(sc.x[t][h][e], sc.y[t][h][e]));
-        const float cm = pair_max16(pair_max32(x));
-        const bool up = (cm - m_run[t]) * c > kRefSlack;
-        m_old[t] = m_run[t];
-        m_run[t] = up ? fmaxf(m_run[t], cm) : m_run[t];
-        moved |= up;
-        const float mc = m_run[t] * c;
-#pragma unroll
-        for (int h = 0; h < NH; ++h)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            pb[t][h][e] = (__bf16)fast_exp2(fmaf(sc.x[t][h][e], c, -mc));
-            pb[t][h][e + 4] = (__bf16)fast_exp2(fmaf(sc.y[t][h][e], c, -mc));
-          }
-      }
-      return moved;
-    };
-    // Scores of the next chunk fused with the softmax of the current one, in
-    // a fixed issue order: segment k reads two key fragments ahead and issues
-    // the four products of step k (both tiles, chains X and Y); its vector
-    // work is the two row-maximum reductions (segments 0, 1), then an equal
-    // share of the exponentials.  A scheduling fence after every segment
-    // keeps the order, so the matrix core works on the next chunk while the
-    // vector ALU works on this one.
-    // key fragments of one chunk for the fused step: segment k's pair
-    constexpr int NSEG = NH * KI;
-    struct Kf {
-      bf16x8 x[NSEG], y[NSEG];
-    };
-    auto kread = [&](int kbuf, Kf& f, int k) {
-      const uint16_t* kl = k_lds[kbuf];
-      const int h = k / KI, i = k % KI;
-      const int cb = ((4 * i + r) ^ kx) * 8;
-      f.x[k] = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x) * KS + cb]);
-      f.y[k] = *reinterpret_cast<const bf16x8*>(&kl[(32 * h + krow_x + 4) * KS + cb]);
-    };
-    // (the caller has read segment 0 into kf)
-    auto fused = [&](int kbuf, Kf& kf, Sc& nx, const Sc& cu, bf16x8 (&pb)[2][NH]) -> bool {
-      constexpr int NE = 2 * NH * 8;  // probabilities per lane per chunk
-      bf16x8 (&ax)[NSEG] = kf.x;
-      bf16x8 (&ay)[NSEG] = kf.y;
-      auto kmfma = [&](int k) {
-        const int h = k / KI, i = k % KI;
+        for (int h = 0; h < NH; ++h) asm volatile("" : "+v"(pb[t][h]));
+      if (__builtin_amdgcn_ballot_w64(moved) != 0) {  // rare
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          nx.x[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax[k], qf[t][i], i ? nx.x[t][h] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          nx.y[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ay[k], qf[t][i], i ? nx.y[t][h] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          const float alpha = fast_exp2((m_old[t] - m_run[t]) * c);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) acc[t][j] *= alpha;
+          lsum[t] *= alpha;
         }
-      };
-      bool moved = false;
-      float mc[2];
-      auto rowmax = [&](int t) {
-        float x = cu.x[t][0][0];
-#pragma unroll
-        for (int h = 0; h < NH; ++h)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x = fmaxf(x, fmaxf(cu.x[t][h][e], cu.y[t][h][e]));
-        // the column's maximum over its four lanes is needed only where the
-        // reference moves: tested on each lane's own maximum first (a rare,
-        // uniform branch)
-        m_old[t] = m_run[t];
-        if (__builtin_amdgcn_ballot_w64((x - m_run[t]) * c > kRefSlack) != 0) {
-          const float cm = pair_max16(pair_max32(x));
-          const bool up = (cm - m_run[t]) * c > kRefSlack;
-          m_run[t] = up ? fmaxf(m_run[t], cm) : m_run[t];
-          moved |= up;
-        }
-        mc[t] = m_run[t] * c;
-      };
-      // probability q (q = ((t * NH + h) * 2 + xy) * 4 + e) of this lane
-      auto prob = [&](int q) {
-        const int e = q & 3, xy = (q >> 2) & 1, h = (q >> 3) % NH, t = (q >> 3) / NH;
-        const float sv = xy ? cu.y[t][h][e] : cu.x[t][h][e];
-        pb[t][h][e + 4 * xy] = (__bf16)fast_exp2(fmaf(sv, c, -mc[t]));
-      };
-      if (NSEG > 1) kread(kbuf, kf, 1);
-#pragma unroll
-      for (int k = 0; k < NSEG; ++k) {
-        if (k + 2 < NSEG) kread(kbuf, kf, k + 2);
-        kmfma(k);
-        if (k < 2) {
-          rowmax(k);
-        } else {
-          constexpr int per = (NE + NSEG - 3) / (NSEG - 2);
-#pragma unroll
-          for (int q = (k - 2) * per; q < (k - 1) * per && q < NE; ++q) prob(q);
-        }
-        __builtin_amdgcn_sched_barrier(0);
       }
-      return moved;
-    };
-    // Value products of one chunk.  The value fragments are read VA head_dim
-    // tiles ahead of their products, in a fixed order (a scheduling fence
-    // after every tile), so each LDS read has the products of the tiles
-    // before it to hide behind; left to itself the compiler reuses one
-    // register quad and waits for every read.  The row sums need no fragment
-    // and cover the first reads.
-    auto values = [&](int vbuf, const bf16x8 (&pb)[2][NH]) {
-      constexpr int VA = 3;
-      const uint16_t* vl = v_lds[vbuf];
-      bf16x8 av[NJ][NH];
-      auto vread = [&](int j) {
-#pragma unroll
-        for (int h = 0; h < NH; ++h)
-          av[j][h] = *reinterpret_cast<const bf16x8*>(&vl[((4 * h + r) * D + 16 * j + nq) * 8]);
-      };
-#pragma unroll
-      for (int j = 0; j < VA && j < NJ; ++j) vread(j);
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int h = 0; h < NH; ++h)
-          lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[t][h], lsum[t], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        if (j + VA < NJ) vread(j + VA);
-#pragma unroll
-        for (int h = 0; h < NH; ++h)
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-            acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[j][h], pb[t][h], acc[t][j], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-
+      __builtin_amdgcn_s_setprio(1);  // value products issue first on this SIMD
+      values(ci & 1, pb);
+      __builtin_amdgcn_s_setprio(0);
+    }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
-    vfix(0, 0);
+    if (more) vfix(c0 + CH, (ci + 1) & 1);
     __syncthreads();
-    // one iteration: chunk ci's softmax and value products, chunk ci + 1's
-    // scores into `nxt`; unrolled by two below so that the two score sets
-    // trade roles without register copies
-    auto step = [&](int32_t ci, Sc& cur, Sc& nxt) {
-      const int32_t c0 = ci * CH;
-      const bool more = ci + 1 < nchunks, more2 = ci + 2 < nchunks;  // uniform
-      if (more && min(c0 + 3 * CH, kend) - 1 >= (wb + TW) * P) {
-        // the staged chunks leave the table window; every read of it is
-        // behind the last barrier
-        wb = (c0 + CH) >> lp;
-        load_tab(wb);
-        __syncthreads();
-      }
-      // the next chunk's first key fragments are read before this step's
-      // loads are issued, so their LDS latency passes while those wait to issue
-      const bool fuse = c0 < wave_kend && more && c0 + CH < wave_kend;  // uniform
-      Kf kf;
-      if (fuse) kread((ci + 1) & 1, kf, 0);
-      if (more2) kload_direct(c0 + 2 * CH, ci & 1);
-      if (more) vload_direct(c0 + CH, (ci + 1) & 1);
-      if (c0 < wave_kend) {  // uniform over the wave
-        mask(cur, c0);
-        bf16x8 pb[2][NH];
-        bool moved;
-        if (fuse) {
-          moved = fused((ci + 1) & 1, kf, nxt, cur, pb);
-        } else {
-          moved = softmax(cur, pb);
-        }
-        // keep the probabilities computed here, beside the score products,
-        // rather than sunk past the rare rescale branch below
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int h = 0; h < NH; ++h) asm volatile("" : "+v"(pb[t][h]));
-        if (__builtin_amdgcn_ballot_w64(moved) != 0) {  // rare
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const float alpha = fast_exp2((m_old[t] - m_run[t]) * c);
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) acc[t][j] *= alpha;
-            lsum[t] *= alpha;
-          }
-        }
-        __builtin_amdgcn_s_setprio(1);  // value products issue first on this SIMD
-        values(ci & 1, pb);
-        __builtin_amdgcn_s_setprio(0);
-      }
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
-      if (more) vfix(c0 + CH, (ci + 1) & 1);
-      __syncthreads();
-    };
-    Sc sa, sb;
-    if (0 < wave_kend) sa = scores(0);  // uniform
-    // every wave has read chunk 0's keys before step 0 loads chunk 2 over them
-    __syncthreads();
-    for (int32_t ci = 0; ci < nchunks; ci += 2) {
-      step(ci, sa, sb);
-      if (ci + 1 < nchunks) step(ci + 1, sb, sa);
-    }
-  } else {
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int32_t ci = 0; ci < nchunks; ++ci) {
-      const int32_t c0 = ci * CH;
-      const bool more = ci + 1 < nchunks;  // uniform
-      if (more && min(c0 + 2 * CH, kend) - 1 >= (wb + TW) * P) {
-        // the next chunk leaves the table window; every read of it is behind
-        // the last barrier
-        wb = (c0 + CH) >> lp;
-        load_tab(wb);
-        __syncthreads();
-      }
-      if (more) gload(c0 + CH);
-      if (c0 < wave_kend) compute(ci & 1, c0);  // uniform over the wave
-      if (more) lstore((ci + 1) & 1);
-      __syncthreads();
-    }
+  };
+  Sc sa, sb;
+  if (0 < wave_kend) sa = scores(0);  // uniform
+  // every wave has read chunk 0's keys before step 0 loads chunk 2 over them
+  __syncthreads();
+  for (int32_t ci = 0; ci < nchunks; ci += 2) {
+    step(ci, sa, sb);
+    if (ci + 1 < nchunks) step(ci + 1, sb, sa);
   }
 
   // totals over the four row groups, then the output rows of each tile
@@ -763,8 +591,7 @@ void launch_prefill_g(PrefillArgs a, int32_t max_q, hipStream_t st) {
   a.n_tiles = (max_q + BT - 1) / BT;
   const int64_t n_groups = (int64_t)a.n_seqs * a.hkv * halves;
   const int64_t wgs = (n_groups + kXcds - 1) / kXcds * kXcds * a.n_tiles;
-  if (a.p >= 16) hipLaunchKernelGGL((prefill_mfma_kernel<D, GW, true>), dim3((unsigned)wgs), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((prefill_mfma_kernel<D, GW, false>), dim3((unsigned)wgs), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, GW>), dim3((unsigned)wgs), dim3(256), 0, st, a);
 }
 
 template <int D>
