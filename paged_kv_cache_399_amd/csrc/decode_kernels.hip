@@ -542,8 +542,8 @@ struct MfmaChunk {
 // rows: a dense product, as in paged prefill.  Four waves take two 16-row
 // tiles each (row 16 k + n of tile k is query head (row % G) of pack member
 // row / G); 64-key chunks go straight from HBM into LDS (each wave loads one
-// 16-key group, which lies in one block: P is a multiple of 16), keys two
-// chunks ahead and values one, and the score products of chunk i + 1 are
+// 16-key group, which lies in one block, or in two with blocks of 8), keys
+// two chunks ahead and values one, and the score products of chunk i + 1 are
 // issued between the softmax instructions of chunk i.  Each row's (max, sum,
 // normalised output) goes to its member's partial slot, exactly where the
 // narrow pack path puts that column's partial.
@@ -564,7 +564,7 @@ struct WideLds {
 template <int D, int P>
 __device__ __forceinline__ void wide_pack_unit(const DecodeArgs& a, const Unit& u, int32_t g,
                                                WideLds<D>& L) {
-  static_assert(P % 16 == 0, "a 16-key group must lie in one block");
+  static_assert(P % 8 == 0, "a 16-key group must lie in one block, or in two of 8");
   typedef __attribute__((address_space(3))) void* lds_ptr_t;
   typedef __attribute__((address_space(1))) void* gptr_t;
   constexpr int CH = 64, NH = 2, KI = D / 32, NJ = D / 16;
@@ -628,42 +628,55 @@ __device__ __forceinline__ void wide_pack_unit(const DecodeArgs& a, const Unit& 
   const int32_t nchunks = (t1 - t0 + CH - 1) / CH;
 
   // staging: wave w loads keys [c0 + 16 w, + 16); a group past t1 reads the
-  // last group that holds keys (in bounds) and its values are zeroed
+  // last group that holds keys (in bounds) and its values are zeroed.  With
+  // blocks of 8 the group's keys 8..15 come from a second block (the unit's
+  // last block where the group ends early); each load covers KR = 4 or 8 key
+  // rows and each value load one 8-key group, so every load stays inside one
+  // block.
   const int wkr = lane / (D / 8), wdc = lane % (D / 8);
-  uint32_t kdoff[KU];
+  uint32_t kdoff[KU];  // bytes from the first key row of the load's block
 #pragma unroll
   for (int uu = 0; uu < KU; ++uu) {
     const int row = uu * KR + wkr;
-    kdoff[uu] = (uint32_t)(row * a.ks.tok * 2 + (wdc ^ kswz<D>(16 * w + row)) * 16);
+    const int grow = P == 8 && uu * KR >= 8 ? row - 8 : row;
+    kdoff[uu] = (uint32_t)(grow * a.ks.tok * 2 + (wdc ^ kswz<D>(16 * w + row)) * 16);
   }
   const uint32_t vdoff = (uint32_t)(lane * P * 2);
-  auto group_base = [&](int32_t c0, int64_t& off) -> int32_t {
+  const int32_t blk_last = (t1 - 1) / P;
+  auto group_base = [&](int32_t c0, int64_t& offA, int64_t& offB) -> int32_t {
     const int32_t kb = c0 + 16 * w;
     const int32_t kl = min(kb, t1 - 1) & ~15;
-    const int32_t blk = __builtin_amdgcn_readfirstlane(L.tab[kl / P - blk0]);
-    off = (int64_t)blk * blk_stride;
+    const int32_t ba = __builtin_amdgcn_readfirstlane(L.tab[kl / P - blk0]);
+    int32_t bb = ba;
+    if constexpr (P == 8) bb = __builtin_amdgcn_readfirstlane(L.tab[min(kl / P + 1, blk_last) - blk0]);
+    offA = (int64_t)ba * blk_stride;
+    offB = (int64_t)bb * blk_stride;
     return kl & (P - 1);
   };
   auto kload = [&](int32_t c0, int buf) {
-    int64_t boff;
-    const int32_t o = group_base(c0, boff);
-    const char* kbase = (const char*)(kc + boff + khead + (int64_t)o * a.ks.tok);
+    int64_t oa, ob;
+    const int32_t o = group_base(c0, oa, ob);
+    const char* ka = (const char*)(kc + oa + khead + (int64_t)o * a.ks.tok);
+    const char* kb2 = (const char*)(kc + ob + khead);
 #pragma unroll
     for (int uu = 0; uu < KU; ++uu)
-      __builtin_amdgcn_global_load_lds((gptr_t)(kbase + kdoff[uu]), (lds_ptr_t)&L.k[buf][(16 * w + uu * KR) * D],
-                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gptr_t)((P == 8 && uu * KR >= 8 ? kb2 : ka) + kdoff[uu]),
+                                       (lds_ptr_t)&L.k[buf][(16 * w + uu * KR) * D], 16, 0, 0);
   };
   auto vslot = [&](int buf, int uu) -> uint16_t* {
     return &L.v[buf][((2 * w + uu / VPG) * D + (uu % VPG) * 64) * 8];
   };
   auto vload = [&](int32_t c0, int buf) {
-    int64_t boff;
-    const int32_t o = group_base(c0, boff);
-    const char* vbase = (const char*)(vc + boff + vhead + o);
+    int64_t oa, ob;
+    const int32_t o = group_base(c0, oa, ob);
+    const char* va = (const char*)(vc + oa + vhead + o);
+    const char* vb2 = (const char*)(vc + ob + vhead);
 #pragma unroll
-    for (int uu = 0; uu < KU; ++uu)
-      __builtin_amdgcn_global_load_lds((gptr_t)(vbase + (uu % VPG) * 64 * P * 2 + (uu / VPG) * 16 + vdoff),
+    for (int uu = 0; uu < KU; ++uu) {
+      const char* vb = P == 8 ? (uu / VPG ? vb2 : va) : va + (uu / VPG) * 16;
+      __builtin_amdgcn_global_load_lds((gptr_t)(vb + (uu % VPG) * 64 * P * 2 + vdoff),
                                        (lds_ptr_t)vslot(buf, uu), 16, 0, 0);
+    }
   };
   auto vfix = [&](int32_t c0, int buf) {
     const int32_t kb = c0 + 16 * w;
@@ -918,7 +931,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void decode_mfma_kernel(Dec
     int32_t tab_lds[W][P < 8 ? 512 : 1];
     int32_t col_slot[16], col_np[16];  // per column of a pack: partial slot, partitions
   };
-  constexpr bool kWide = MIXED && W == 4 && P % 16 == 0;
+  constexpr bool kWide = MIXED && W == 4 && P % 8 == 0;
   constexpr size_t kLdsBytes =
       kWide && sizeof(WideLds<D>) > sizeof(NarrowLds) ? sizeof(WideLds<D>) : sizeof(NarrowLds);
   __shared__ __align__(16) unsigned char lds_raw[kLdsBytes];
@@ -1970,9 +1983,9 @@ int choose(int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t p, int32_
   out->kind = kind;
   out->waves_per_group = W;
   out->part_tokens = T;
-  // wide packs: four waves, blocks of 16, 32 or 64 tokens (a 16-key group in
-  // one block), units of at most kWideTab blocks
-  out->wide = may_pack && W == 4 && p % 16 == 0 && T / p <= kWideTab && !env_is("PKV_DECODE_WIDE", "off");
+  // wide packs: four waves, blocks of 8 to 64 tokens (a 16-key group in one
+  // block, or two of 8), units of at most kWideTab blocks
+  out->wide = may_pack && W == 4 && p % 8 == 0 && T / p <= kWideTab && !env_is("PKV_DECODE_WIDE", "off");
   out->wide_split = 1;
   if (out->wide) {
     // pieces of at least one 64-key chunk.  Measured on 128 sequences sharing
@@ -2259,7 +2272,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.pack_max = 1;
   if (d_shared_prev && c.may_pack && c.kind == pkv::kKindMfma && !pkv::env_is("PKV_DECODE_SHARE", "off")) {
     // narrow packs fill the 16 MFMA columns (16 / G sequences); wide packs
-    // (four waves, blocks of 16, 32 or 64 tokens, units of at most
+    // (four waves, blocks of 8 to 64 tokens, units of at most
     // kWideTab blocks) take up to 128 / G sequences, read with a dense product
     const int32_t G = num_q_heads / num_kv_heads;
     a.pack_max = c.wide ? std::min(pkv::kWideMaxPack, pkv::kWideRows / G) : std::max(1, 16 / G);

@@ -152,6 +152,10 @@ CASES = [
     (32, 8, 128, 16, "head_major", 256, [(1000, [0] * 20 + [1] * 10 + [300] * 10), (70, [1] * 36)], False),
     (16, 8, 64, 32, "token_major", 128, [(700, [0, 5, 90, 0, 33, 2, 1, 64, 0, 7, 3, 11])], False),
     (16, 2, 128, 64, "head_major", 256, [(2100, list(range(0, 40)))], False),
+    # wide packs over blocks of 8 (a 16-key group spans two blocks; shared lengths that end
+    # inside a block, inside a 16-key group and past a partition edge)
+    (32, 8, 128, 8, "head_major", 256, [(1003, [0] * 20 + [1] * 10 + [300] * 10), (77, [1] * 36)], False),
+    (32, 8, 128, 8, "token_major", 128, [(517, [0, 3, 9, 0, 64, 2, 1, 15, 0, 7, 3, 11])], False),
 ]
 
 
@@ -355,15 +359,16 @@ def test_graph_replay_with_packs(monkeypatch):
     kv.close()
 
 
+@pytest.mark.parametrize("p", [16, 8])
 @pytest.mark.parametrize("t", [256, None])
-def test_wide_packs_do_not_depend_on_block_placement(monkeypatch, t):
+def test_wide_packs_do_not_depend_on_block_placement(monkeypatch, t, p):
     """The same forks on two different physical placements: wide-pack decode
     (runs of 40 and 12 sequences at G = 4) gives bit-identical outputs, and
     both match float64."""
     import torch
     if t:
         monkeypatch.setenv("PKV_PARTITION_TOKENS", str(t))
-    hq, hkv, d, p = 32, 8, 128, 16
+    hq, hkv, d = 32, 8, 128
     groups = [(1500, [i % 7 for i in range(40)]), (333, [50] * 12)]
     outs = []
     for perm in (1, 2):
