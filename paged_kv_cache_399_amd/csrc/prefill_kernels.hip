@@ -13,8 +13,9 @@
 // whole tile of queries, so it is staged once in LDS per workgroup and all
 // waves run both products on matrix cores from there.
 //
-// Work decomposition: grid (query tiles, sequences, KV heads x head halves);
-// a workgroup of four waves takes 128 query rows: BT = 128 / GW query tokens
+// Work decomposition: one workgroup per (query tile, sequence, KV head, head
+// half), on a one-dimensional XCD-aware grid (see prefill_mfma_kernel); a
+// workgroup of four waves takes 128 query rows: BT = 128 / GW query tokens
 // of GW query heads of one KV head (GW = G, or 8 halves of a 16-head group).
 // Wave w takes two 16-row tiles, k = 2w and 2w + 1, tile k being tokens
 // 16 (k / GW) .. + 15 of head k % GW, so every key / value fragment a wave
