@@ -232,7 +232,8 @@ def run_prefill(args):
     torch.cuda.set_device(0)
     w = make_prefill_workload(cfg, args.seed, dev)
     b, hq, hkv, d, p = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
-    kv = PagedKVCache(w.num_blocks, p, hkv, d, torch.bfloat16, dev, w.free_order, fill=0.0)
+    kv = PagedKVCache(w.num_blocks, p, hkv, d, torch.bfloat16, dev, w.free_order, fill=0.0,
+                      layout=args.layout)
     seqs = kv.new_sequences(b)
     if cfg.context:
         slots, _ = kv.pool.append_slots(seqs, [cfg.context] * b)
@@ -249,13 +250,13 @@ def run_prefill(args):
     # the attention alone, back to back on the final state
     for _ in range(args.warmup):
         paged_attention_prefill(out, w.q, kv.k_cache, kv.v_cache, m.table, m.lens, m.query_start,
-                                cfg.new, stream=stream)
+                                cfg.new, stream=stream, layout=kv.layout)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(args.steps):
         paged_attention_prefill(out, w.q, kv.k_cache, kv.v_cache, m.table, m.lens, m.query_start,
-                                cfg.new, stream=stream)
+                                cfg.new, stream=stream, layout=kv.layout)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
@@ -269,7 +270,7 @@ def run_prefill(args):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "batch": b, "context": cfg.context, "new_tokens": cfg.new,
                    "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d, "block_size": p,
-                   "seed": args.seed, "parallelism": "single GPU"},
+                   "k_layout": args.layout, "seed": args.seed, "parallelism": "single GPU"},
         "tokens_per_s": round(b * cfg.new / (ms * 1e-3), 1),
         "extend_ms_first_call": round(extend_ms, 3),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
