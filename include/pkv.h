@@ -454,9 +454,10 @@ int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_c
  *                     PKV_DEVERR_CONTEXT_LEN
  *   scale             as in pkv_paged_attention_decode (0 = 1 / sqrt(head_dim))
  * Both products run on matrix cores; key/value chunks of 64 tokens are staged
- * once per workgroup in LDS and shared by a tile of queries.  Supported: bf16,
- * head_dim 64 / 128, block_size a power of two from 8 to 256, G in {1, 2, 4, 8, 16},
- * fewer than 2^24 workgroups (n_seqs x Hkv x query tiles of 128 / G tokens),
+ * once per workgroup in LDS and shared by a tile of queries: 128 query rows,
+ * 128 / GW tokens of GW heads, GW the largest of 8, 4, 2, 1 dividing G.
+ * Supported: bf16, head_dim 64 / 128, block_size a power of two from 8 to 256,
+ * any G, fewer than 2^24 workgroups (n_seqs x Hkv x G / GW x query tiles),
  * 16-byte aligned q, out and caches.  A sequence whose length
  * is out of range is skipped (its rows unwritten) and flagged
  * (PKV_DEVERR_CONTEXT_LEN); bad table entries are clamped and flagged.

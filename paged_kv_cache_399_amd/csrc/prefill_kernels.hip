@@ -16,7 +16,8 @@
 // Work decomposition: one workgroup per (query tile, sequence, KV head, head
 // half), on a one-dimensional XCD-aware grid (see prefill_mfma_kernel); a
 // workgroup of four waves takes 128 query rows: BT = 128 / GW query tokens
-// of GW query heads of one KV head (GW = G, or 8 halves of a 16-head group).
+// of GW query heads of one KV head (GW the largest of 8, 4, 2, 1 dividing G;
+// the G / GW parts of a head group take workgroups of their own).
 // Wave w takes two 16-row tiles, k = 2w and 2w + 1, tile k being tokens
 // 16 (k / GW) .. + 15 of head k % GW, so every key / value fragment a wave
 // reads from LDS feeds two matrix-core products.  Tiles are launched
@@ -595,13 +596,18 @@ void launch_prefill_g(PrefillArgs a, int32_t max_q, hipStream_t st) {
   hipLaunchKernelGGL((prefill_mfma_kernel<D, GW>), dim3((unsigned)wgs), dim3(256), 0, st, a);
 }
 
+// Query heads per workgroup for G query heads per KV head: the largest of 8,
+// 4, 2, 1 that divides G (a workgroup's 128 rows are 128 / GW tokens of GW
+// heads; the G / GW parts of a head group take workgroups of their own).
+int32_t prefill_gw(int32_t G) { return G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1; }
+
 template <int D>
 void launch_prefill(const PrefillArgs& a, int32_t max_q, hipStream_t st) {
-  switch (a.hq / a.hkv) {
+  switch (prefill_gw(a.hq / a.hkv)) {
     case 1: launch_prefill_g<D, 1>(a, max_q, st); break;
     case 2: launch_prefill_g<D, 2>(a, max_q, st); break;
     case 4: launch_prefill_g<D, 4>(a, max_q, st); break;
-    default: launch_prefill_g<D, 8>(a, max_q, st); break;  // 8, or 16 in two halves
+    default: launch_prefill_g<D, 8>(a, max_q, st); break;
   }
 }
 
@@ -630,14 +636,13 @@ extern "C" int pkv_paged_attention_prefill(void* out, const void* q, const void*
     return fail(PKV_ERR_INVALID_ARG, "scale must be 0 (1/sqrt(head_dim)) or finite and positive");
   const int32_t G = num_q_heads / num_kv_heads;
   const bool pow2 = block_size >= 8 && block_size <= 256 && (block_size & (block_size - 1)) == 0;
-  if (dtype != PKV_BF16 || (head_dim != 64 && head_dim != 128) || !pow2 ||
-      (G != 1 && G != 2 && G != 4 && G != 8 && G != 16))
+  if (dtype != PKV_BF16 || (head_dim != 64 && head_dim != 128) || !pow2)
     return fail(PKV_ERR_UNSUPPORTED,
-                "prefill needs bf16, head_dim 64/128, block_size a power of two in [8, 256], "
-                "G in {1,2,4,8,16}");
+                "prefill needs bf16, head_dim 64/128, block_size a power of two in [8, 256]");
   {
-    const int64_t bt = 16 * 8 / std::min<int32_t>(G, 8);
-    const int64_t groups = (int64_t)n_seqs * num_kv_heads * (G > 8 ? 2 : 1);
+    const int32_t GW = pkv::prefill_gw(G);
+    const int64_t bt = 16 * 8 / GW;
+    const int64_t groups = (int64_t)n_seqs * num_kv_heads * (G / GW);
     // one-dimensional grid: workgroups x 256 threads must stay below 2^32
     if (((groups + 7) / 8 * 8) * ((max_query_len + bt - 1) / bt) >= (int64_t)1 << 24)
       return fail(PKV_ERR_UNSUPPORTED, "grid too large (2^24 workgroups)");

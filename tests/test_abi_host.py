@@ -153,7 +153,7 @@ def test_prefill_argument_validation_without_device():
     assert call(p=24) == L.ERR_UNSUPPORTED          # not a power of two
     assert call(p=4) == L.ERR_UNSUPPORTED           # shorter than one 16-byte value run
     assert call(p=512) == L.ERR_UNSUPPORTED
-    assert call(hq=24, hkv=8) == L.ERR_UNSUPPORTED  # G = 3
+    assert call(hq=24, hkv=8, n_seqs=0) == L.OK     # G = 3 is taken (one head per workgroup row set)
     assert call(d=96) == L.ERR_UNSUPPORTED
     assert call(dtype=L.F32) == L.ERR_UNSUPPORTED
     assert call(hq=30, hkv=8) == L.ERR_INVALID_ARG  # Hq % Hkv != 0

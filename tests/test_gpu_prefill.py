@@ -84,6 +84,10 @@ def _run(hq, hkv, d, p, ctx_lens, new_lens, seed, free_order=None, fill=None, la
 @pytest.mark.parametrize("hq,hkv,d,p", [
     (8, 8, 128, 16), (8, 4, 64, 8), (16, 4, 128, 16), (32, 8, 128, 32), (16, 2, 64, 16),
     (16, 1, 128, 16),
+    # head groups that are not powers of two: G = 3, 5, 6, 7, 12, 10 (one, one, two, one,
+    # four and two heads per workgroup)
+    (3, 1, 128, 16), (10, 2, 64, 8), (12, 2, 128, 16), (28, 4, 128, 16), (24, 2, 128, 32),
+    (40, 4, 64, 16),
 ])
 def test_prefill_chunks_match_oracle(hq, hkv, d, p):
     ctx = [0, 0, 5, 100, 333, 16, 1000]

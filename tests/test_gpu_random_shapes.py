@@ -96,7 +96,7 @@ def test_random_decode_case(monkeypatch, case):
 def _draw_prefill(case):
     rng = np.random.default_rng(9100 + case)
     hkv = int(rng.choice([1, 2, 4, 8]))
-    g = int(rng.choice([1, 2, 4, 8, 16]))
+    g = int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 12, 16]))
     d = int(rng.choice([64, 128]))
     p = int(rng.choice([8, 16, 32, 64, 128, 256]))
     layout = "token_major" if rng.random() < 0.3 else "head_major"
@@ -106,7 +106,7 @@ def _draw_prefill(case):
     return dict(hq=hkv * g, hkv=hkv, d=d, p=p, layout=layout, ctx=ctx, new=new)
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(16))
 def test_random_prefill_case(case):
     from tests.test_gpu_prefill import _run
     from tests.paged_case import BF16_TOL
