@@ -305,7 +305,7 @@ int pkv_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_
  *                    that sequence read its predecessor's tokens (in bounds).
  *                    PKV_DECODE_SHARE=off ignores the array.  Runs of
  *                    more than 16 / G sharing sequences (block sizes of
- *                    16, 32 or 64 tokens) form wide packs of up to 128 / G
+ *                    8 to 64 tokens) form wide packs of up to 128 / G
  *                    sequences (at most 32) whose shared tokens are read
  *                    once for all their query rows as a dense matrix-core
  *                    product; those sum in another order, so the
