@@ -405,6 +405,16 @@ def run_decode(args, cfg, cpu):
     w = make_workload(cfg, args.seed, dev, extra_steps=nsteps)
     b, hq, hkv, d, p = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
     s = 2 if cfg.dtype == "bf16" else 4
+    # a workload with a fixed pool (tiny: 16 blocks) holds only so many appended tokens
+    need = int(np.sum(-(-(w.lengths + nsteps) // p)))
+    if cfg.prefix_len == 0 and need > w.num_blocks:
+        fit = 0
+        while int(np.sum(-(-(w.lengths + fit + 1) // p))) <= w.num_blocks:
+            fit += 1
+        print(json.dumps({"error": f"{cfg.name}: its {w.num_blocks}-block pool holds {fit} decode steps "
+                                   f"after the context, not warmup + steps = {nsteps} "
+                                   f"(e.g. --steps {max(fit - 1, 1)} --warmup 1)"}), flush=True)
+        sys.exit(2)
     kv = PagedKVCache(w.num_blocks, p, hkv, d, w.torch_dtype, dev, w.free_order, fill=0.0,
                       layout=args.layout, share_blocks=not args.no_share)
     if cfg.prefix_len:
