@@ -336,8 +336,11 @@ int pkv_decode_workspace_bytes(int32_t n_seqs, int32_t num_q_heads, int32_t num_
  * several partitions are combined by a merge kernel.  The summation order
  * depends only on logical positions, T and the wave split, so results do not
  * depend on where the blocks sit.  Arithmetic is fp32.  Kernel per shape:
- *   - bf16, head_dim 64/128, block_size 1, 2, 4, ..., 64, 1 <= G <= 16: matrix
- *     cores (score and value products as 16x16x32 bf16 MFMA, head group as N);
+ *   - bf16, head_dim 64/128, block_size 1, 2, 4, ..., 64, any G: matrix
+ *     cores (score and value products as 16x16x32 bf16 MFMA, head group as N;
+ *     G > 16 runs as ceil(G / 16) column sets of at most 16 heads, adjacent
+ *     workgroups that each read the KV head's keys and values, with cached
+ *     loads, and take no packs; such shapes need 16-byte aligned buffers);
  *   - fp32 (or bf16 shapes the matrix-core kernel does not take) with G <= 4,
  *     head_dim 64/128, block_size * element size a multiple of 16 bytes:
  *     vector ALU with DPP row reductions;

@@ -34,10 +34,11 @@
 // summation order, within the same tolerance).
 //
 // Partition kernels:
-//  * decode_mfma_kernel (bf16, head_dim 64/128, block size 1..64, G <= 16):
+//  * decode_mfma_kernel (bf16, head_dim 64/128, block size 1..64, any G):
 //    scores and the value product run on v_mfma_f32_16x16x32_bf16 with the
 //    head group (or a pack's head groups) as the 16-wide N dimension, padded
-//    with zero queries.  Each lane loads exactly the 16-byte operand fragments
+//    with zero queries; a group of more than 16 heads runs as several column
+//    sets, one workgroup each.  Each lane loads exactly the 16-byte operand fragments
 //    it feeds to the matrix core straight from HBM (keys token-major, values
 //    token-minor), with the next 32-token chunk's loads in flight while the
 //    current one is computed.  The score fragment a lane receives is already
@@ -95,6 +96,10 @@ struct DecodeArgs {
   int32_t n_seqs, hq, hkv, d, p, num_blocks, max_blocks, part_tokens, max_units;
   int32_t pack_max;  // sequences one unit may take (1: no packing)
   int32_t wide_split;  // pieces each whole shared partition of a wide pack is cut into (1: none)
+  // The G query heads of a KV head run in gparts column sets of at most gcols
+  // heads (one set of G unless G > 16, the matrix-core kernel's columns);
+  // each set is a workgroup of its own, in the partition and merge kernels.
+  int32_t gparts, gcols;
   KStrides ks;       // key cache: elements between KV heads, between tokens
   int64_t len_cap;   // min(max_blocks * p, max_context_len): longer contexts are clamped
   float scale_log2;  // scale * log2(e): scores are kept in log2 units
@@ -945,24 +950,30 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void decode_mfma_kernel(Dec
 
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
-  const int32_t unit = blockIdx.x / a.hkv;
-  const int32_t g = blockIdx.x - unit * a.hkv;
+  // workgroup: (unit, KV head g, column set `part` of g's query heads)
+  const int32_t hkv_v = a.hkv * a.gparts;
+  const int32_t unit = blockIdx.x / hkv_v;
+  const int32_t gv = blockIdx.x - unit * hkv_v;
+  const int32_t g = gv / a.gparts, part = gv - g * a.gparts;
   if (unit >= a.max_units) return;  // uniform over the workgroup
   const Unit u = decode_unit(a, unit);
   if (!u.valid) return;             // uniform over the workgroup
   const int32_t G = a.hq / a.hkv;
   if constexpr (kWide) {
-    if (u.pack * G > 16) {  // uniform: a pack wider than the MFMA columns
+    if (u.pack > 1 && u.pack * G > 16) {  // uniform: a pack wider than the MFMA columns
       wide_pack_unit<D, P>(a, u, g, *reinterpret_cast<WideLds<D>*>(lds_raw));
       return;
     }
   }
   const int n = lane & 15, r = lane >> 4;
-  // MFMA column n: query head n % G of pack member n / G (the unit's own
-  // sequence when the pack is one sequence); columns >= pack * G are padding
-  const int32_t NC = u.pack * G;
-  const int32_t mem = n / G;
-  const int32_t head = g * G + (n - mem * G);
+  // MFMA column n: query head h0 + n % GC of pack member n / GC (the unit's
+  // own sequence when the pack is one sequence; packs have one column set,
+  // GC = G); columns >= NC are padding
+  const int32_t GC = a.gcols;
+  const int32_t h0 = g * G + part * GC;
+  const int32_t NC = a.gparts > 1 ? min(GC, G - part * GC) : u.pack * G;
+  const int32_t mem = n / GC;
+  const int32_t head = h0 + (n - mem * GC);
   const bool head_ok = n < NC;
   if (u.pack > 1 && threadIdx.x < NC) {
     // a shared piece of partition j = t0 / T of every member: slot first + j,
@@ -1249,8 +1260,8 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void decode_mfma_kernel(Dec
       }
     }
     const float inv = sum > 0.f ? 1.f / sum : 0.f;
-    const int32_t hm = h / G;
-    const int32_t qh = g * G + (h - hm * G);
+    const int32_t hm = h / GC;
+    const int32_t qh = h0 + (h - hm * GC);
     const int32_t seq = u.b + hm;
     const int32_t slot = u.pack > 1 ? col_slot[h] : u.slot;
     const int32_t np = u.pack > 1 ? col_np[h] : u.nparts;
@@ -1687,9 +1698,10 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
 // Merge.  For query head h of a sequence with n > 1 partial results in slots
 // f0 .. f0 + n - 1 (partition order), over the slots with l_i > 0:
 //   M = max_i m_i,  w_i = l_i 2^(m_i - M),  out = sum_i w_i o_i / sum_i w_i.
-// One workgroup per (sequence, KV head) takes the G query heads of that KV
-// head, EPT output elements per thread (G D / EPT threads, rounded up to
-// whole waves), so the grid is n_seqs * Hkv workgroups; those
+// One workgroup per (sequence, KV head, column set) takes the query heads of
+// that set (G of them; G / gparts with more than 16), EPT output elements per
+// thread (G D / EPT threads, rounded up to whole waves), so the grid is
+// n_seqs * Hkv * gparts workgroups; those
 // of a sequence with one partition return at once (it wrote its output
 // directly).  Wave w finds M, the weights (to LDS, the first kMergeSlots
 // slots) and their total for heads w, w + W, ...; before any of that waits,
@@ -1704,9 +1716,8 @@ constexpr int kMergePre = 4;      // partial outputs loaded before the weights a
 constexpr int kMergeElems = 4;    // most output elements per thread (G D up to 4096)
 constexpr int kMergeHeads = 4;    // heads per wave whose first slots' (m, l) are loaded up front
 
-// threads of a merge workgroup for `ept` elements per thread (G * D <= 4096)
-inline int merge_threads(int32_t hq, int32_t hkv, int32_t d, int ept) {
-  const int32_t per = (hq / hkv) * d;
+// threads of a merge workgroup for `ept` elements per thread (per = G * D <= 4096)
+inline int merge_threads(int32_t per, int ept) {
   const int32_t t = (per + ept - 1) / ept;
   return std::min(1024, std::max(64, (t + 63) / 64 * 64));
 }
@@ -1715,8 +1726,11 @@ template <typename T, int EPT>
 __global__ __launch_bounds__(1024) void merge_kernel(DecodeArgs a) {
   __shared__ float wts[16][kMergeSlots];
   __shared__ float m_head[16], tot_head[16];
-  const int32_t b = blockIdx.x / a.hkv;
-  const int32_t g = blockIdx.x - b * a.hkv;
+  // workgroup: (sequence b, KV head g, column set `part` of g's query heads)
+  const int32_t hkv_v = a.hkv * a.gparts;
+  const int32_t b = blockIdx.x / hkv_v;
+  const int32_t gv = blockIdx.x - b * hkv_v;
+  const int32_t g = gv / a.gparts, part = gv - g * a.gparts;
   const int4 si = a.plan.seq_info[b];
   const int32_t f0 = si.x, n = si.y;
   if (!plan_matches(a)) return;       // another call's plan (flagged by the partition kernel)
@@ -1724,9 +1738,13 @@ __global__ __launch_bounds__(1024) void merge_kernel(DecodeArgs a) {
   if (a.plan.counts[0] == 0) return;  // plan overflowed
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int W = blockDim.x >> 6;
-  const int32_t D = a.d, G = a.hq / a.hkv, GD = G * D;
+  // this workgroup's G query heads, from head h0 (at most 16)
+  const int32_t GA = a.hq / a.hkv;
+  const int32_t G = a.gparts > 1 ? min(a.gcols, GA - part * a.gcols) : GA;
+  const int32_t h0 = g * GA + part * a.gcols;
+  const int32_t D = a.d, GD = G * D;
   const int64_t slot_stride = (int64_t)a.hq;  // (slot, head) rows per slot
-  const int64_t row0 = (int64_t)f0 * slot_stride + (int64_t)g * G;  // (slot f0, head g G)
+  const int64_t row0 = (int64_t)f0 * slot_stride + h0;  // (slot f0, head h0)
 
   // this thread's output elements: head hk[k], element dk[k] (ok[k]: in range)
   int32_t hk[EPT], dk[EPT];
@@ -1838,7 +1856,7 @@ __global__ __launch_bounds__(1024) void merge_kernel(DecodeArgs a) {
   for (int k = 0; k < EPT; ++k) {
     if (!ok[k]) continue;
     const float tot = tot_head[hk[k]];
-    store_f32((T*)a.out + ((int64_t)b * a.hq + g * G + hk[k]) * D + dk[k], tot > 0.f ? acc[k] / tot : 0.f);
+    store_f32((T*)a.out + ((int64_t)b * a.hq + h0 + hk[k]) * D + dk[k], tot > 0.f ? acc[k] / tot : 0.f);
   }
 }
 
@@ -1888,6 +1906,7 @@ struct Choice {
   bool may_pack;  // sized for packs of sharing sequences (one extra slot per sequence)
   bool wide;          // packs may be wide (dense product over up to kWideRows query rows)
   int32_t wide_split; // pieces per whole shared partition of a wide pack
+  int32_t gparts, gcols;  // column sets of a KV head's query heads, heads per set
 };
 
 enum { kMathAuto, kMathValu, kMathMfma, kMathDpp, kMathGeneric };
@@ -1902,8 +1921,9 @@ int math_mode() {
 
 bool mfma_shape_ok(int32_t hq, int32_t hkv, int32_t d, int32_t p, pkv_dtype dt) {
   const int32_t G = hq / hkv;
+  // (any G: beyond 16 the query heads run in several column sets)
   return dt == PKV_BF16 && (d == 64 || d == 128) && (p == 1 || p == 2 || p == 4 || p == 8 || p == 16 || p == 32 || p == 64) &&
-         G >= 1 && G <= 16;
+         G >= 1;
 }
 
 // DPP kernel: head_dim 64 / 128, head groups up to 4, block rows of whole
@@ -1923,7 +1943,7 @@ int choose(int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t p, int32_
   const bool dshape = dpp_shape_ok(hq, hkv, d, p, dt);
   int kind;
   if (mode == kMathMfma) {
-    if (!mshape) return fail(PKV_ERR_UNSUPPORTED, "matrix-core decode needs bf16, head_dim 64/128, block size a power of two up to 64, G <= 16");
+    if (!mshape) return fail(PKV_ERR_UNSUPPORTED, "matrix-core decode needs bf16, head_dim 64/128, block size a power of two up to 64");
     kind = kKindMfma;
   } else if (mode == kMathDpp) {
     if (!dshape) return fail(PKV_ERR_UNSUPPORTED, "DPP decode needs head_dim 64/128, G <= 4, 16-byte block rows");
@@ -1945,8 +1965,15 @@ int choose(int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t p, int32_
   if (kind == kKindGeneric && !generic_shape_ok(hq, hkv, d))
     return fail(PKV_ERR_UNSUPPORTED, "decode supports head_dim <= 256 and Hq/Hkv <= 16");
   const int64_t L = std::max<int32_t>(max_len, 1);
-  // packs need the matrix-core kernel and a batch not known to share nothing
-  const bool may_pack = kind == kKindMfma && !(unshared >= 0 && total >= 0 && unshared >= total);
+  // more than 16 query heads per KV head (matrix-core kernel only): column
+  // sets of at most 16, each reading the KV head's keys and values
+  const int32_t G = hq / hkv;
+  out->gparts = kind == kKindMfma && G > 16 ? (G + 15) / 16 : 1;
+  out->gcols = (G + out->gparts - 1) / out->gparts;
+  // packs need the matrix-core kernel, one column set and a batch not known
+  // to share nothing
+  const bool may_pack = kind == kKindMfma && out->gparts == 1 &&
+                        !(unshared >= 0 && total >= 0 && unshared >= total);
   if (total < 0) total = (int64_t)n_seqs * L;
   // W waves share a partition of T tokens; each wave's share is whole chunks
   int32_t W = 1, tmin = 64, tmax = 512;
@@ -2048,8 +2075,9 @@ Layout layout_of(int32_t n_seqs, int32_t hq, int32_t d, const Choice& c) {
 template <int D, int P>
 void launch_mfma(const DecodeArgs& a, int32_t waves_per_group, int64_t groups, hipStream_t st) {
   // a batch that packs sequences sharing blocks reads the packs' tokens with
-  // cached loads
-  const bool keep = a.pack_max > 1;
+  // cached loads, and so do the column sets of one KV head (adjacent
+  // workgroups over the same keys and values)
+  const bool keep = a.pack_max > 1 || a.gparts > 1;
   if (waves_per_group == 8) {
     if (keep) hipLaunchKernelGGL((decode_mfma_kernel<D, P, 8, true>), dim3((unsigned)groups), dim3(512), 0, st, a);
     else hipLaunchKernelGGL((decode_mfma_kernel<D, P, 8, false>), dim3((unsigned)groups), dim3(512), 0, st, a);
@@ -2112,13 +2140,13 @@ void launch_merge(const DecodeArgs& a, unsigned grid, hipStream_t st) {
   // Elements per thread: measured best is one for small batches (more waves
   // hide the latency of a short launch) and two for large ones (fewer waves
   // to dispatch); raised until G * D fits 1024 threads.
-  const int32_t gd = (a.hq / a.hkv) * a.d;
-  const int64_t elems = (int64_t)a.n_seqs * a.hkv * gd;
+  const int32_t gd = a.gcols * a.d;  // a column set's output elements
+  const int64_t elems = (int64_t)a.n_seqs * a.hkv * a.gparts * gd;
   const int dflt = elems <= (int64_t)1 << 19 ? 1 : 2;
   const int want = env_int("PKV_MERGE_ELEMS", dflt);
   int ept = want >= 4 ? 4 : (want >= 2 ? 2 : 1);  // an instantiated width
   while (ept < kMergeElems && gd > 1024 * ept) ept *= 2;  // G D <= 4096 = 1024 * kMergeElems
-  const dim3 block(merge_threads(a.hq, a.hkv, a.d, ept));
+  const dim3 block(merge_threads(gd, ept));
   if (ept == 1) hipLaunchKernelGGL((merge_kernel<T, 1>), grid, block, 0, st, a);
   else if (ept == 2) hipLaunchKernelGGL((merge_kernel<T, 2>), grid, block, 0, st, a);
   else hipLaunchKernelGGL((merge_kernel<T, 4>), grid, block, 0, st, a);
@@ -2236,13 +2264,16 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     const uintptr_t mis = (uintptr_t)out | (uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache;
     if (mis % 16) {
       const int math = pkv::math_mode();
-      if (math == pkv::kMathMfma || math == pkv::kMathDpp || mode == kRunPlanned)
+      // (the generic kernel takes at most 16 query heads per KV head)
+      if (math == pkv::kMathMfma || math == pkv::kMathDpp || mode == kRunPlanned || c.gparts > 1)
         return fail(PKV_ERR_UNSUPPORTED, "this decode kernel needs 16-byte aligned buffers");
       // same partition length and workspace; the generic kernel takes any
       c.kind = pkv::kKindGeneric;
     }
   }
-  if ((int64_t)c.max_units * num_kv_heads > (int64_t)INT32_MAX)
+  // one-dimensional grid: workgroups (units x KV heads x column sets) of up
+  // to 512 threads must stay below 2^32 threads
+  if ((int64_t)c.max_units * num_kv_heads * c.gparts * 512 >= (int64_t)1 << 32)
     return fail(PKV_ERR_UNSUPPORTED, "too many partitions");
   const pkv::Layout lay = pkv::layout_of(n_seqs, num_q_heads, head_dim, c);
   if (use_scratch) {
@@ -2291,6 +2322,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     a.pack_max = c.wide ? std::min(pkv::kWideMaxPack, pkv::kWideRows / G) : std::max(1, 16 / G);
   }
   a.wide_split = a.pack_max > 1 && c.wide ? c.wide_split : 1;
+  a.gparts = c.gparts;
+  a.gcols = c.gcols;
   a.len_cap = std::min<int64_t>((int64_t)max_blocks_per_seq * block_size, max_context_len);
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.plan.counts = (int32_t*)(ws + lay.counts);
@@ -2316,7 +2349,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode plan launch: %s", hipGetErrorString(e));
     return PKV_OK;
   }
-  const int64_t waves = c.max_units * num_kv_heads;
+  const int64_t waves = c.max_units * num_kv_heads * c.gparts;
   if (c.kind == pkv::kKindMfma) {
     const int32_t W = c.waves_per_group;
     if (head_dim == 128) pkv::launch_mfma_p<128>(a, block_size, W, waves, st);
@@ -2331,7 +2364,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   }
   // some sequence has several partials: a partition split, or a split shared partition
   if (c.need_partials && (c.part_tokens < std::max<int32_t>(max_context_len, 1) || a.pack_max > 1)) {
-    const unsigned grid = (unsigned)((int64_t)n_seqs * num_kv_heads);
+    const unsigned grid = (unsigned)((int64_t)n_seqs * num_kv_heads * c.gparts);
     if (dtype == PKV_BF16) pkv::launch_merge<uint16_t>(a, grid, st);
     else pkv::launch_merge<float>(a, grid, st);
   }

@@ -62,8 +62,9 @@ def test_decode_argument_validation_without_device():
     assert lib.pkv_decode_workspace_bytes(4, 6, 4, 128, 16, 100, -1, -1, L.BF16, ctypes.byref(out)) == L.ERR_INVALID_ARG
     # unsupported head_dim on every path
     assert lib.pkv_decode_workspace_bytes(4, 8, 8, 512, 16, 100, -1, -1, L.BF16, ctypes.byref(out)) == L.ERR_UNSUPPORTED
-    # group larger than 16
-    assert lib.pkv_decode_workspace_bytes(4, 64, 2, 128, 16, 100, -1, -1, L.BF16, ctypes.byref(out)) == L.ERR_UNSUPPORTED
+    # groups larger than 16: bf16 on matrix cores in column sets; no vector-ALU kernel takes them
+    assert lib.pkv_decode_workspace_bytes(4, 64, 2, 128, 16, 100, -1, -1, L.BF16, ctypes.byref(out)) == 0
+    assert lib.pkv_decode_workspace_bytes(4, 64, 2, 128, 16, 100, -1, -1, L.F32, ctypes.byref(out)) == L.ERR_UNSUPPORTED
     assert lib.pkv_decode_workspace_bytes(4, 32, 8, 128, 16, 100, -1, -1, L.BF16, ctypes.byref(out)) == 0
     assert out.value > 0
     # decode with NULL buffers, non-positive scale

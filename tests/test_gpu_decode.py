@@ -244,6 +244,24 @@ def test_edge_lengths(monkeypatch, dtype, hq, hkv, d, p, part):
     say(f"  {cfg.name} part={part}: max err {err:.3e}")
 
 
+@pytest.mark.parametrize("hq,hkv,d,p", [
+    (32, 1, 128, 16), (48, 1, 64, 8), (71, 1, 128, 16), (40, 2, 128, 32), (64, 1, 128, 1),
+])
+@pytest.mark.parametrize("part", ["64", "auto"])
+def test_head_groups_beyond_sixteen(monkeypatch, hq, hkv, d, p, part):
+    """More than 16 query heads per KV head (multi-query shapes): the matrix-core
+    kernel runs ceil(G / 16) column sets per KV head (G = 71: five sets of 15,
+    the last holding 11; G = 20: two of 10), each split into partitions and
+    merged on its own (part = 64) or whole (auto: contexts up to 1000 tokens)."""
+    if part != "auto":
+        monkeypatch.setenv("PKV_PARTITION_TOKENS", part)
+    cfg = DecodeConfig(f"mq_{hq}_{hkv}_{d}_{p}", len(EDGE_LENGTHS), hq, hkv, d, p, "bf16",
+                       "fixed", fixed_lengths=tuple(EDGE_LENGTHS))
+    case = build_case(cfg, seed=11)
+    err = check_attention(case)
+    say(f"  {cfg.name} part={part}: max err {err:.3e}")
+
+
 @pytest.mark.parametrize("dtype,hq,hkv,d,p", [
     ("bf16", 4, 4, 128, 16), ("bf16", 6, 3, 64, 8), ("bf16", 9, 3, 128, 32),
     ("bf16", 8, 2, 128, 16), ("f32", 8, 2, 128, 4), ("f32", 4, 4, 64, 16),

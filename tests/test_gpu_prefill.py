@@ -88,6 +88,8 @@ def _run(hq, hkv, d, p, ctx_lens, new_lens, seed, free_order=None, fill=None, la
     # four and two heads per workgroup)
     (3, 1, 128, 16), (10, 2, 64, 8), (12, 2, 128, 16), (28, 4, 128, 16), (24, 2, 128, 32),
     (40, 4, 64, 16),
+    # more than 16 query heads per KV head (the session's decode sizing takes them too)
+    (32, 1, 128, 16), (48, 2, 64, 8),
 ])
 def test_prefill_chunks_match_oracle(hq, hkv, d, p):
     ctx = [0, 0, 5, 100, 333, 16, 1000]
