@@ -262,6 +262,29 @@ def test_head_groups_beyond_sixteen(monkeypatch, hq, hkv, d, p, part):
     say(f"  {cfg.name} part={part}: max err {err:.3e}")
 
 
+@pytest.mark.parametrize("layout", ["head_major", "token_major"])
+def test_head_groups_beyond_sixteen_planned_and_token_major(monkeypatch, layout):
+    """Column sets (G = 40: three sets of 14, 14 and 12 heads) with split partitions:
+    both key layouts against float64, and the plan + planned call bit for bit
+    equal to the full call."""
+    import torch
+    monkeypatch.setenv("PKV_PARTITION_TOKENS", "64")
+    cfg = DecodeConfig(f"mq_planned_{layout}", len(EDGE_LENGTHS), 40, 1, 128, 16, "bf16", "fixed",
+                       fixed_lengths=tuple(EDGE_LENGTHS))
+    case = build_case(cfg, seed=12, layout=layout)
+    err = check_attention(case)
+    kv, m = case.kv, case.meta
+    q = case.w.q
+    full = torch.full_like(q, float("nan"))
+    planned = torch.full_like(q, float("nan"))
+    kv.attend(m, q, full)
+    kv.plan(m)
+    kv.attend(m, q, planned, planned=True)
+    torch.cuda.synchronize()
+    assert torch.equal(full, planned)
+    say(f"  {cfg.name}: max err {err:.3e}")
+
+
 @pytest.mark.parametrize("dtype,hq,hkv,d,p", [
     ("bf16", 4, 4, 128, 16), ("bf16", 6, 3, 64, 8), ("bf16", 9, 3, 128, 32),
     ("bf16", 8, 2, 128, 16), ("f32", 8, 2, 128, 4), ("f32", 4, 4, 64, 16),
