@@ -2004,8 +2004,16 @@ int choose(int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t p, int32_
     const int cus = device_cu_count();
     const int32_t div_default = (int64_t)n_seqs * hkv >= 8LL * cus ? 2 : 4;
     const int64_t div = std::max(1, env_int("PKV_SPLIT_DIV", div_default));
-    const int64_t want = total * hkv / ((int64_t)cus * div);
-    T = (int32_t)std::min<int64_t>(tmax, std::max<int64_t>(tmin, pow2_floor(std::max<int64_t>(want, 1))));
+    // (units are partitions x KV heads x column sets.)  Matrix-core units
+    // shorter than 256 tokens cost more in per-unit overhead than they gain in
+    // spread.  Measured (planned decode, head_dim 128, lengths up to 4096):
+    // 64 sequences on one KV head 48.4 us at 128 against 36.1 at 256; 16 on
+    // one 27.1 against 23.0; 4 on eight 20.1 against 17.6; 8 on two 17.2
+    // against 16.8; with 64 query heads on one KV head, counting the four
+    // column sets, 124.5 against 72.2.
+    const int64_t want = total * hkv * out->gparts / ((int64_t)cus * div);
+    const int32_t tfloor = kind == kKindMfma ? 256 : tmin;
+    T = (int32_t)std::min<int64_t>(tmax, std::max<int64_t>(tfloor, pow2_floor(std::max<int64_t>(want, 1))));
     // Contexts of at most kWholeLen tokens: one partition per sequence and
     // no merge launch.  Measured (plan + partition + merge, 16-token blocks):
     // longest context 512, batches of 8 and 64: 16.4-16.9 us against
