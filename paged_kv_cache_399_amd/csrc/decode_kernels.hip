@@ -951,10 +951,13 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void decode_mfma_kernel(Dec
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
   // workgroup: (unit, KV head g, column set `part` of g's query heads)
-  const int32_t hkv_v = a.hkv * a.gparts;
+  // (column sets run only in the cached-load variant, MIXED: the other one
+  // compiles for one set)
+  const int32_t gparts = MIXED ? a.gparts : 1;
+  const int32_t hkv_v = a.hkv * gparts;
   const int32_t unit = blockIdx.x / hkv_v;
   const int32_t gv = blockIdx.x - unit * hkv_v;
-  const int32_t g = gv / a.gparts, part = gv - g * a.gparts;
+  const int32_t g = gparts == 1 ? gv : gv / gparts, part = gv - g * gparts;
   if (unit >= a.max_units) return;  // uniform over the workgroup
   const Unit u = decode_unit(a, unit);
   if (!u.valid) return;             // uniform over the workgroup
@@ -969,11 +972,18 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void decode_mfma_kernel(Dec
   // MFMA column n: query head h0 + n % GC of pack member n / GC (the unit's
   // own sequence when the pack is one sequence; packs have one column set,
   // GC = G); columns >= NC are padding
-  const int32_t GC = a.gcols;
+  const int32_t GC = MIXED ? a.gcols : G;
   const int32_t h0 = g * G + part * GC;
-  const int32_t NC = a.gparts > 1 ? min(GC, G - part * GC) : u.pack * G;
-  const int32_t mem = n / GC;
-  const int32_t head = h0 + (n - mem * GC);
+  int32_t NC, mem, head;
+  if (gparts == 1) {  // uniform: one column set (pack members, G heads each)
+    NC = u.pack * G;
+    mem = n / G;
+    head = h0 + (n - mem * G);
+  } else {  // a column set of one sequence: heads h0 .. h0 + NC - 1
+    NC = min(GC, G - part * GC);
+    mem = 0;
+    head = h0 + n;
+  }
   const bool head_ok = n < NC;
   if (u.pack > 1 && threadIdx.x < NC) {
     // a shared piece of partition j = t0 / T of every member: slot first + j,
@@ -1260,8 +1270,8 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void decode_mfma_kernel(Dec
       }
     }
     const float inv = sum > 0.f ? 1.f / sum : 0.f;
-    const int32_t hm = h / GC;
-    const int32_t qh = h0 + (h - hm * GC);
+    const int32_t hm = gparts == 1 ? h / G : 0;
+    const int32_t qh = h0 + (h - hm * G);
     const int32_t seq = u.b + hm;
     const int32_t slot = u.pack > 1 ? col_slot[h] : u.slot;
     const int32_t np = u.pack > 1 ? col_np[h] : u.nparts;
@@ -1730,7 +1740,7 @@ __global__ __launch_bounds__(1024) void merge_kernel(DecodeArgs a) {
   const int32_t hkv_v = a.hkv * a.gparts;
   const int32_t b = blockIdx.x / hkv_v;
   const int32_t gv = blockIdx.x - b * hkv_v;
-  const int32_t g = gv / a.gparts, part = gv - g * a.gparts;
+  const int32_t g = a.gparts == 1 ? gv : gv / a.gparts, part = gv - g * a.gparts;
   const int4 si = a.plan.seq_info[b];
   const int32_t f0 = si.x, n = si.y;
   if (!plan_matches(a)) return;       // another call's plan (flagged by the partition kernel)
